@@ -1,0 +1,117 @@
+"""spec_verify over a batch: target pass, then the rule per batch row.
+
+Interface shape follows the verification call the pages describe: the drafted
+token ids, the draft's distributions [gamma, V] and the target's scores at
+gamma + 1 positions in, the number accepted and the accepted tokens plus one
+correction or bonus token out ([SSD] "The Accept/Reject Mechanism",
+SpeculationResult and speculative_accept_reject; [PIG] "How it works").
+
+Batch rows are independent ([SSD] "Batch-Level Speculation": rows accept
+different counts); row b draws its uniforms from counter (i, b, 0, 0).
+
+Outputs per row b:
+  n_accepted[b]  in 0..gamma, or -1 when a draft token id lies outside [0, V)
+  emitted[b]     drafts[0 .. n) followed by the correction / bonus token at
+                 index n, then -1 padding; all -1 for a rejected row
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .model import as_f64, forward
+from .philox import row_uniforms
+from .rule import MARGIN, verify_row, verify_row_greedy, warp_logits, warp_probs
+
+
+@dataclass
+class VerifyResult:
+    n_accepted: np.ndarray
+    emitted: np.ndarray
+    margins: list = field(default_factory=list)   # per row: [(kind, pos, value)]
+    logits: np.ndarray = None
+
+    def row_min_margin(self, b):
+        vals = [m[2] for m in self.margins[b]]
+        return min(vals) if vals else np.inf
+
+    def flagged_rows(self, threshold=MARGIN):
+        return [b for b in range(len(self.margins))
+                if self.row_min_margin(b) < threshold]
+
+    def n_decisions(self):
+        return sum(len(m) for m in self.margins)
+
+    def n_flagged_decisions(self, threshold=MARGIN):
+        return sum(1 for row in self.margins for m in row if m[2] < threshold)
+
+
+def _check_scalars(temperature, top_p):
+    if not (temperature >= 0.0) or not np.isfinite(temperature):
+        raise ValueError("temperature must be finite and >= 0")
+    if not (0.0 < top_p <= 1.0):
+        raise ValueError("top_p must lie in (0, 1]")
+
+
+def spec_verify_from_logits(logits, draft_tokens, q, temperature, top_p, seed):
+    """Acceptance rule for a batch given target logits [B, gamma+1, V].
+
+    q is [B, gamma, V] (the draft's T = 1 probabilities); it is not read and
+    may be None when temperature == 0.
+    """
+    _check_scalars(temperature, top_p)
+    ell = as_f64(logits)
+    draft = np.asarray(draft_tokens, dtype=np.int64)
+    B, G1, V = ell.shape
+    gamma = G1 - 1
+    if draft.shape != (B, gamma):
+        raise ValueError("draft_tokens must be [B, gamma]")
+    if not np.all(np.isfinite(ell)):
+        raise ValueError("non-finite logits")
+    greedy = temperature == 0.0
+    if not greedy:
+        qq = as_f64(q)
+        if qq.shape != (B, gamma, V):
+            raise ValueError("q must be [B, gamma, V]")
+        if not np.all(np.isfinite(qq)) or np.any(qq < 0):
+            raise ValueError("q must be finite and non-negative")
+
+    n_acc = np.full(B, -1, dtype=np.int32)
+    emitted = np.full((B, G1), -1, dtype=np.int32)
+    margins = []
+    for b in range(B):
+        xs = draft[b]
+        if np.any(xs < 0) or np.any(xs >= V):
+            margins.append([])
+            continue
+        if greedy:
+            j, tok, mg = verify_row_greedy(ell[b], xs)
+        else:
+            p_rows, p_mg = zip(*[warp_logits(ell[b, i], temperature, top_p)
+                                 for i in range(G1)])
+            q_rows, q_mg = zip(*[warp_probs(qq[b, i], temperature, top_p)
+                                 for i in range(gamma)]) if gamma else ((), ())
+            uni = [row_uniforms(seed, b, i) for i in range(G1)]
+            j, tok, mg = verify_row(p_rows, q_rows, xs, uni)
+            # top-p cuts of every row the decisions consulted
+            for i in range(j + 1):
+                mg += [("top_p_p", i, m) for m in p_mg[i]]
+            for i in range(min(j + 1, gamma)):
+                mg += [("top_p_q", i, m) for m in q_mg[i]]
+        n_acc[b] = j
+        emitted[b, :j] = xs[:j]
+        emitted[b, j] = tok
+        margins.append(mg)
+    return VerifyResult(n_acc, emitted, margins, ell)
+
+
+def spec_verify(hidden, weights, draft_tokens, q, temperature, top_p, seed):
+    """Full verification step: target pass over [B, gamma+1, d], then the rule.
+
+    weights: dict with "blocks" (list of {w_up, w_down, gain}), "lm_head" and
+    optionally "eps" (default 1e-6).
+    """
+    logits = forward(hidden, weights["blocks"], weights["lm_head"],
+                     weights.get("eps", 1e-6))
+    return spec_verify_from_logits(logits, draft_tokens, q, temperature,
+                                   top_p, seed)
