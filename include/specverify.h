@@ -1,0 +1,175 @@
+/*
+ * specverify.h -- C ABI of the speculative-decoding target-verification step
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One call scores gamma drafted positions plus the bonus position of B
+ * sequences in a single pass over the target's weights, then applies the
+ * acceptance rule over the vocabulary:
+ *   - accept draft x_i when r_i * q'_i(x_i) < p'_i(x_i), r_i uniform in [0,1)
+ *     ("Speculative decoding" explainer, lattice-ai-eng.pages.dev: acceptance
+ *     rule; pigeon guide "Speculative decoding", How it works, step 3);
+ *   - at the first rejection j, sample a replacement from
+ *     norm(max(0, p'_j - q'_j)) and drop the later drafts (pigeon guide, step
+ *     4), or from p'_j when that residual is exactly zero ("Build a
+ *     Speculative Decoding Engine to Cut LLM Latency by 3x", The Accept/Reject
+ *     Mechanism, numerical fallback);
+ *   - if nothing is rejected, sample one bonus token from p'_gamma (pigeon
+ *     guide, step 5);
+ *   - at temperature 0, accept while the draft equals the target's argmax and
+ *     emit the argmax (lattice-ai-eng explainer, greedy remark).
+ * p' and q' are the target and draft distributions after the same
+ * temperature and top-p transform (pigeon guide, When it breaks; scalablesystem
+ * article, Quality, Evaluation, and Guardrails, item 1).  q' is q^(1/T)
+ * renormalised; the nucleus is the shortest prefix of the tokens sorted by
+ * probability (descending, ties by lower id) whose mass reaches top_p.
+ *
+ * Sampling uses the inverse CDF in token-id order (smallest v whose inclusive
+ * prefix sum exceeds u * total).  Uniforms come from Philox4x64-10 (Salmon et
+ * al., SC'11) with key (seed, 0) and counter (i, b, 0, 0): r_{b,i} is the top
+ * 24 bits of word 0 times 2^-24 and u_{b,i} the top 24 bits of word 1, so a
+ * run is reproducible from its seed (scalablesystem article, guardrail 3).
+ *
+ * The synthetic target is a stack of MLP blocks
+ *     n = h / sqrt(mean(h^2) + eps) * g;  h += SiLU(n @ W_up) @ W_down
+ * followed by logits = h @ W_lm (no final norm).  Weights are row-major
+ * [in][out].
+ *
+ * Conventions for every entry point:
+ *   - Pointers documented "device" are HIP device pointers; "host" pointers
+ *     are ordinary process memory.  The caller owns every buffer it passes.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the default stream).  The caller synchronises the stream before it
+ *     reads outputs.
+ *   - Shapes, scalars, pointers and workspace size are checked before any
+ *     launch; on error nothing is launched and a negative spec_status is
+ *     returned.  A row whose draft token id lies outside [0, vocab) gets
+ *     n_accepted = -1 and an all -1 emitted row; other rows are unaffected.
+ *   - Non-finite inputs are a precondition violation: no fault, unspecified
+ *     outputs.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,      /* bad shape, scalar or null pointer              */
+  SPEC_EDTYPE = -2,      /* unsupported weight dtype                       */
+  SPEC_EWORKSPACE = -3,  /* workspace missing or smaller than required     */
+  SPEC_EHIP = -4,        /* a HIP runtime call failed                      */
+  SPEC_ENOMEM = -5       /* device allocation failed (create only)         */
+} spec_status;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Flags for spec_weights_desc.flags. */
+#define SPEC_FLAG_KEEP_ROWMAJOR 1u  /* bf16: also keep a row-major copy so the
+                                       vector-FMA GEMM can serve any row count */
+
+/* Description of the target's weights, read once by spec_weights_create.
+ * The pointer arrays are host arrays of n_blocks device pointers.  The
+ * library copies (and repacks) every weight into memory it owns, so the
+ * caller may free its buffers once spec_weights_create has returned and the
+ * stream has been synchronised. */
+typedef struct {
+  int32_t d;               /* hidden size                                  */
+  int32_t ffn;             /* MLP inner size                               */
+  int32_t n_blocks;        /* number of MLP blocks (>= 0)                  */
+  int32_t vocab;           /* V                                            */
+  int32_t wdtype;          /* spec_dtype of every weight and gain          */
+  float rms_eps;           /* RMSNorm epsilon (1e-6 in the workloads)      */
+  const void* const* w_up;      /* host array: n_blocks device [d][ffn]    */
+  const void* const* w_down;    /* host array: n_blocks device [ffn][d]    */
+  const void* const* norm_gain; /* NULL (all ones) or host array of
+                                   n_blocks device [d]                     */
+  const void* lm_head;          /* device [d][vocab]                       */
+  uint32_t flags;               /* SPEC_FLAG_*                             */
+  int32_t mfma_min_rows;        /* bf16: use the MFMA GEMM when
+                                   B*(gamma+1) >= this; <= 0 means the
+                                   library default                         */
+} spec_weights_desc;
+
+typedef struct spec_weights* spec_weights_t;
+
+/* Validate the description, allocate device memory and copy the weights
+ * into the library's layouts (fp32 row-major for SPEC_F32; MFMA tiles for
+ * SPEC_BF16, plus row-major when SPEC_FLAG_KEEP_ROWMAJOR).  Runs on `stream`
+ * and synchronises it before returning.  *out is set only on SPEC_OK. */
+spec_status spec_weights_create(const spec_weights_desc* desc, void* stream,
+                                spec_weights_t* out);
+
+/* Free what spec_weights_create allocated.  NULL is accepted. */
+spec_status spec_weights_destroy(spec_weights_t w);
+
+/* Bytes of device workspace spec_verify / spec_verify_debug need for this
+ * batch shape, or 0 when the arguments are invalid (B < 1, gamma < 0). */
+size_t spec_workspace_size(spec_weights_t w, int32_t B, int32_t gamma);
+
+/* The verification step.
+ *   hidden       device fp32 [B][gamma+1][d]; row i < gamma scores draft i,
+ *                row gamma scores the bonus slot
+ *   draft_tokens device int32 [B][gamma]
+ *   q            device fp32 [B][gamma][vocab], the draft's temperature-1
+ *                probabilities (need not be normalised; not read when
+ *                temperature == 0, may then be NULL)
+ *   temperature  >= 0 and finite; 0 selects the greedy rule
+ *   top_p        in (0, 1]; 1 disables the nucleus; ignored when
+ *                temperature == 0
+ *   seed         Philox key word 0
+ *   n_accepted   device int32 [B] out: 0..gamma, or -1 for a bad row
+ *   emitted      device int32 [B][gamma+1] out: the n accepted drafts, then
+ *                the correction or bonus token, then -1 padding
+ *   workspace    device, at least spec_workspace_size(w, B, gamma) bytes,
+ *                256-byte aligned; contents on entry are ignored */
+spec_status spec_verify(spec_weights_t w, int32_t B, int32_t gamma,
+                        const float* hidden, const int32_t* draft_tokens,
+                        const float* q, float temperature, float top_p,
+                        uint64_t seed, int32_t* n_accepted, int32_t* emitted,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_verify plus optional dumps for parity checks (not a timed path).
+ *   logits_out  device fp32 [B][gamma+1][vocab] or NULL: target logits
+ *   p_out       device fp32 [B][gamma+1][vocab] or NULL: p' (T > 0 only)
+ *   q_out       device fp32 [B][gamma][vocab] or NULL: q' (T > 0 only) */
+spec_status spec_verify_debug(spec_weights_t w, int32_t B, int32_t gamma,
+                              const float* hidden, const int32_t* draft_tokens,
+                              const float* q, float temperature, float top_p,
+                              uint64_t seed, int32_t* n_accepted,
+                              int32_t* emitted, void* workspace,
+                              size_t workspace_bytes, void* stream,
+                              float* logits_out, float* p_out, float* q_out);
+
+/* Workspace bytes for spec_verify_from_logits, or 0 on invalid arguments. */
+size_t spec_workspace_size_from_logits(int32_t B, int32_t gamma, int32_t vocab);
+
+/* The acceptance rule alone, given target logits instead of hidden states
+ * and weights: logits is device fp32 [B][gamma+1][vocab].  Every other
+ * argument means what it means for spec_verify. */
+spec_status spec_verify_from_logits(int32_t B, int32_t gamma, int32_t vocab,
+                                    const float* logits,
+                                    const int32_t* draft_tokens,
+                                    const float* q, float temperature,
+                                    float top_p, uint64_t seed,
+                                    int32_t* n_accepted, int32_t* emitted,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* Static text for a status code. */
+const char* spec_status_string(spec_status s);
+
+/* Row count B*(gamma+1) from which bf16 weights use the MFMA GEMM when the
+ * description leaves mfma_min_rows at 0. */
+int32_t spec_default_mfma_min_rows(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

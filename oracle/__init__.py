@@ -41,13 +41,13 @@ Parity status of each part (what pins it) is listed in the module docstrings.
 from .philox import philox4x64_10, row_uniforms, PURPOSE_VERIFY, PURPOSE_DRAFT
 from .model import bf16_to_f64, as_f64, rmsnorm, silu, forward
 from .rule import (warp_logits, warp_probs, nucleus_mask, accept_test,
-                   inverse_cdf, verify_row, verify_row_greedy, MARGIN)
+                   inverse_cdf, verify_row, verify_row_greedy, MARGIN, TopP)
 from .verify import spec_verify, spec_verify_from_logits, VerifyResult
 
 __all__ = [
     "philox4x64_10", "row_uniforms", "PURPOSE_VERIFY", "PURPOSE_DRAFT",
     "bf16_to_f64", "as_f64", "rmsnorm", "silu", "forward",
     "warp_logits", "warp_probs", "nucleus_mask", "accept_test", "inverse_cdf",
-    "verify_row", "verify_row_greedy", "MARGIN",
+    "verify_row", "verify_row_greedy", "MARGIN", "TopP",
     "spec_verify", "spec_verify_from_logits", "VerifyResult",
 ]

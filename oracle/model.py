@@ -35,7 +35,7 @@ def as_f64(x):
     x = np.asarray(x)
     if x.dtype == np.uint16:
         return bf16_to_f64(x)
-    return x.astype(np.float64)
+    return np.asarray(x, dtype=np.float64)       # no copy when already float64
 
 
 def rmsnorm(h, g, eps):

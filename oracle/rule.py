@@ -42,11 +42,18 @@ float32 implementation may be compared decision by decision:
   ratio test       |r - p'(x)/q'(x)|            (p'(x) when q'(x) = 0)
   inverse CDF      distance of u*R to the nearest of C(v-1), C(v), over R
                    (and R itself when R < 1e-6)
-  top-p cut        cumulative mass minus top_p at the cut, top_p minus the
-                   mass before it, and the relative gap between the last kept
-                   and the first dropped probability
+  top-p cut        tokens whose nucleus membership is uncertain: the next
+                   token when the kept mass exceeds top_p by less than MARGIN,
+                   the last kept token when the mass before it falls short of
+                   top_p by less than MARGIN, and (target rows only) every
+                   token in a near-tied band at the cut, i.e. within
+                   MARGIN * max|logit| of the last kept or first dropped logit.
+                   A ratio test on an uncertain token has margin 0; other
+                   ratio tests lose ratio * (uncertain mass of p' and q') of
+                   margin; the inverse CDF loses twice that mass over R
   greedy argmax    gap between the two largest logits over max |logit|
-A decision whose margin is below MARGIN is a knife-edge event.
+A decision whose margin is below MARGIN is a knife-edge event.  The draft
+distribution needs no order band: both sides sort the same float32 q.
 
 Pinned by: the [LAT] worked example (tests/golden/worked_example.json); the
 two-case identity and the emission law P(emit t) = p'(t) by quadrature over
@@ -61,16 +68,26 @@ import numpy as np
 MARGIN = 1e-5
 
 
-def nucleus_mask(probs, top_p):
-    """Boolean mask of the top-p nucleus of a probability vector, and margins.
+class TopP:
+    """Knife-edge information of one nucleus cut (see the module docstring)."""
 
-    Returns (mask, margins) where margins is a list of floats (empty when
-    top_p >= 1, which keeps every token).
+    def __init__(self, uncertain=(), mass=0.0):
+        self.uncertain = set(int(v) for v in uncertain)   # may change sides
+        self.mass = float(mass)    # their mass in the renormalised distribution
+
+
+def nucleus_mask(probs, top_p, logp_tol=0.0):
+    """Boolean mask of the top-p nucleus of a probability vector, and its
+    knife-edge information.
+
+    logp_tol: log-probability tolerance within which two tokens may swap
+    order on the other side of the comparison (0: the order is exact).
+    Returns (mask, TopP).  top_p >= 1 keeps every token.
     """
     probs = np.asarray(probs, dtype=np.float64)
     V = probs.shape[0]
     if top_p >= 1.0:
-        return np.ones(V, dtype=bool), []
+        return np.ones(V, dtype=bool), TopP()
     order = np.lexsort((np.arange(V), -probs))   # prob descending, id ascending
     s = probs[order]
     c = np.cumsum(s)
@@ -78,31 +95,39 @@ def nucleus_mask(probs, top_p):
     k = int(hit[0]) if hit.size else V - 1
     mask = np.zeros(V, dtype=bool)
     mask[order[:k + 1]] = True
-    margins = [abs(c[k] - top_p)]
-    if k > 0:
-        margins.append(abs(top_p - c[k - 1]))
-    if k + 1 < V and s[k] > 0:
-        margins.append((s[k] - s[k + 1]) / s[k])
-    return mask, margins
+    unc = set()
+    if k + 1 < V and c[k] - top_p < MARGIN:
+        unc.add(int(order[k + 1]))                 # could join
+    if k > 0 and top_p - c[k - 1] < MARGIN:
+        unc.add(int(order[k]))                     # could drop out
+    if logp_tol > 0 and k + 1 < V and s[k + 1] > 0:
+        lo, hi = np.log(s[k + 1]), np.log(s[k])
+        if hi - lo < logp_tol:
+            with np.errstate(divide="ignore"):
+                lp = np.log(probs)
+            unc.update(int(v) for v in np.nonzero((lp >= lo - logp_tol) & (lp <= hi + logp_tol))[0])
+    mass = probs[sorted(unc)].sum() / c[k] if unc else 0.0
+    return mask, TopP(unc, mass)
 
 
-def _apply_top_p(w, top_p):
-    mask, margins = nucleus_mask(w, top_p)
+def _apply_top_p(w, top_p, logp_tol=0.0):
+    mask, info = nucleus_mask(w, top_p, logp_tol)
     if top_p < 1.0:
         w = np.where(mask, w, 0.0)
         w = w / w.sum()
-    return w, margins
+    return w, info
 
 
 def warp_logits(ell, T, top_p):
-    """p' = top_p(softmax(ell / T)) for T > 0; returns (p', top-p margins)."""
+    """p' = top_p(softmax(ell / T)) for T > 0; returns (p', TopP)."""
     ell = np.asarray(ell, dtype=np.float64)
     e = np.exp((ell - ell.max()) / T)
-    return _apply_top_p(e / e.sum(), top_p)
+    scale = np.abs(ell).max()
+    return _apply_top_p(e / e.sum(), top_p, MARGIN * (scale if scale > 0 else 1.0) / T)
 
 
 def warp_probs(q, T, top_p):
-    """q' = top_p(q^(1/T) / sum q^(1/T)) for T > 0; returns (q', margins)."""
+    """q' = top_p(q^(1/T) / sum q^(1/T)) for T > 0; returns (q', TopP)."""
     q = np.asarray(q, dtype=np.float64)
     # q^(1/T) scaled by qmax^(-1/T) so small T cannot underflow every entry
     pos = q > 0
@@ -115,7 +140,11 @@ def warp_probs(q, T, top_p):
 def accept_test(p_x, q_x, r):
     """(accepted, margin) for one drafted token."""
     accepted = r * q_x < p_x
-    margin = abs(r - p_x / q_x) if q_x > 0 else p_x
+    if q_x > 0:
+        margin = abs(r - p_x / q_x)
+    else:
+        # accept iff p'(x) > 0: a knife edge only if p'(x) is tiny but nonzero
+        margin = p_x if p_x > 0 else np.inf
     return bool(accepted), float(margin)
 
 
@@ -139,29 +168,42 @@ def residual(p, q):
     return res if np.cumsum(res)[-1] > 0 else p
 
 
-def verify_row(p_rows, q_rows, draft, uniforms):
+def verify_row(p_rows, q_rows, draft, uniforms, p_cuts=None, q_cuts=None):
     """Sampling branch (T > 0) for one batch row.
 
     p_rows   : gamma+1 warped target distributions p'_0 .. p'_gamma
     q_rows   : gamma warped draft distributions q'_0 .. q'_{gamma-1}
     draft    : gamma token ids, already checked to lie in [0, V)
     uniforms : gamma+1 pairs (r_i, u_i)
+    p_cuts, q_cuts : optional TopP per row (top-p knife edges)
     Returns (n_accepted, token, margins) with margins a list of
     (kind, position, value) for the decisions actually taken.
     """
     gamma = len(draft)
     margins = []
+    none = TopP()
+    pc = (lambda i: p_cuts[i]) if p_cuts is not None else (lambda i: none)
+    qc = (lambda i: q_cuts[i]) if q_cuts is not None else (lambda i: none)
     for i in range(gamma):
         x = int(draft[i])
         r, u = uniforms[i]
         ok, m = accept_test(p_rows[i][x], q_rows[i][x], r)
+        unc_mass = pc(i).mass + qc(i).mass
+        if x in pc(i).uncertain or x in qc(i).uncertain:
+            m = 0.0
+        elif unc_mass and q_rows[i][x] > 0:
+            m -= p_rows[i][x] / q_rows[i][x] * unc_mass
         margins.append(("accept", i, m))
         if ok:
             continue
-        tok, m = inverse_cdf(residual(p_rows[i], q_rows[i]), u)
+        w = residual(p_rows[i], q_rows[i])
+        tok, m = inverse_cdf(w, u)
+        if unc_mass:
+            m -= 2.0 * unc_mass / np.cumsum(w)[-1]
         margins.append(("resample", i, m))
         return i, tok, margins
     tok, m = inverse_cdf(p_rows[gamma], uniforms[gamma][1])
+    m -= 2.0 * pc(gamma).mass
     margins.append(("bonus", gamma, m))
     return gamma, tok, margins
 

@@ -30,6 +30,15 @@ class VerifyResult:
     emitted: np.ndarray
     margins: list = field(default_factory=list)   # per row: [(kind, pos, value)]
     logits: np.ndarray = None
+    cuts: list = field(default_factory=list)      # per row: (p TopPs, q TopPs) at T > 0
+
+    def nucleus_uncertain(self, b):
+        """(p rows, q rows) of row b whose top-p membership is uncertain."""
+        if not self.cuts or self.cuts[b] is None:
+            return set(), set()
+        pc, qc = self.cuts[b]
+        return ({i for i, c in enumerate(pc) if c.uncertain},
+                {i for i, c in enumerate(qc) if c.uncertain})
 
     def row_min_margin(self, b):
         vals = [m[2] for m in self.margins[b]]
@@ -53,11 +62,14 @@ def _check_scalars(temperature, top_p):
         raise ValueError("top_p must lie in (0, 1]")
 
 
-def spec_verify_from_logits(logits, draft_tokens, q, temperature, top_p, seed):
+def spec_verify_from_logits(logits, draft_tokens, q, temperature, top_p, seed,
+                            batch_ids=None):
     """Acceptance rule for a batch given target logits [B, gamma+1, V].
 
     q is [B, gamma, V] (the draft's T = 1 probabilities); it is not read and
-    may be None when temperature == 0.
+    may be None when temperature == 0.  batch_ids gives the batch index b of
+    each row for its uniforms (default 0..B-1), so a few sequences of a larger
+    batch can be checked on their own.
     """
     _check_scalars(temperature, top_p)
     ell = as_f64(logits)
@@ -76,33 +88,34 @@ def spec_verify_from_logits(logits, draft_tokens, q, temperature, top_p, seed):
         if not np.all(np.isfinite(qq)) or np.any(qq < 0):
             raise ValueError("q must be finite and non-negative")
 
+    bids = np.arange(B) if batch_ids is None else np.asarray(batch_ids, dtype=np.int64)
+    if bids.shape != (B,):
+        raise ValueError("batch_ids must have one entry per row")
     n_acc = np.full(B, -1, dtype=np.int32)
     emitted = np.full((B, G1), -1, dtype=np.int32)
-    margins = []
+    margins, cuts = [], []
     for b in range(B):
         xs = draft[b]
         if np.any(xs < 0) or np.any(xs >= V):
             margins.append([])
+            cuts.append(None)
             continue
         if greedy:
             j, tok, mg = verify_row_greedy(ell[b], xs)
+            cuts.append(None)
         else:
             p_rows, p_mg = zip(*[warp_logits(ell[b, i], temperature, top_p)
                                  for i in range(G1)])
             q_rows, q_mg = zip(*[warp_probs(qq[b, i], temperature, top_p)
                                  for i in range(gamma)]) if gamma else ((), ())
-            uni = [row_uniforms(seed, b, i) for i in range(G1)]
-            j, tok, mg = verify_row(p_rows, q_rows, xs, uni)
-            # top-p cuts of every row the decisions consulted
-            for i in range(j + 1):
-                mg += [("top_p_p", i, m) for m in p_mg[i]]
-            for i in range(min(j + 1, gamma)):
-                mg += [("top_p_q", i, m) for m in q_mg[i]]
+            uni = [row_uniforms(seed, int(bids[b]), i) for i in range(G1)]
+            j, tok, mg = verify_row(p_rows, q_rows, xs, uni, p_cuts=p_mg, q_cuts=q_mg)
+            cuts.append((list(p_mg), list(q_mg)))
         n_acc[b] = j
         emitted[b, :j] = xs[:j]
         emitted[b, j] = tok
         margins.append(mg)
-    return VerifyResult(n_acc, emitted, margins, ell)
+    return VerifyResult(n_acc, emitted, margins, ell, cuts)
 
 
 def spec_verify(hidden, weights, draft_tokens, q, temperature, top_p, seed):

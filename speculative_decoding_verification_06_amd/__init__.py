@@ -1,0 +1,239 @@
+"""Python binding of libspecverify (the C ABI in include/specverify.h).
+
+Argument marshalling only: every step of the verification runs in the HIP
+library.  PyTorch supplies device memory and the current stream.  If the
+shared library has not been built the import of a binding function raises;
+there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_ENOMEM = 0, -1, -2, -3, -4, -5
+SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_FLAG_KEEP_ROWMAJOR = 1
+
+# Every symbol include/specverify.h declares.
+EXPORTS = ["spec_weights_create", "spec_weights_destroy", "spec_workspace_size", "spec_verify",
+           "spec_verify_debug", "spec_workspace_size_from_logits", "spec_verify_from_logits",
+           "spec_status_string", "spec_default_mfma_min_rows"]
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("ffn", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("wdtype", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("w_up", ctypes.POINTER(ctypes.c_void_p)), ("w_down", ctypes.POINTER(ctypes.c_void_p)),
+                ("norm_gain", ctypes.POINTER(ctypes.c_void_p)), ("lm_head", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32), ("mfma_min_rows", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load():
+    """Load libspecverify.so (built by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_uint64, ctypes.c_size_t
+    lib.spec_weights_create.argtypes = [ctypes.POINTER(_Desc), vp, ctypes.POINTER(vp)]
+    lib.spec_weights_create.restype = i32
+    lib.spec_weights_destroy.argtypes = [vp]
+    lib.spec_weights_destroy.restype = i32
+    lib.spec_workspace_size.argtypes = [vp, i32, i32]
+    lib.spec_workspace_size.restype = sz
+    common = [vp, i32, i32, vp, vp, vp, f32, f32, u64, vp, vp, vp, sz, vp]
+    lib.spec_verify.argtypes = common
+    lib.spec_verify.restype = i32
+    lib.spec_verify_debug.argtypes = common + [vp, vp, vp]
+    lib.spec_verify_debug.restype = i32
+    lib.spec_workspace_size_from_logits.argtypes = [i32, i32, i32]
+    lib.spec_workspace_size_from_logits.restype = sz
+    lib.spec_verify_from_logits.argtypes = [i32, i32, i32, vp, vp, vp, f32, f32, u64, vp, vp, vp, sz, vp]
+    lib.spec_verify_from_logits.restype = i32
+    lib.spec_status_string.argtypes = [i32]
+    lib.spec_status_string.restype = ctypes.c_char_p
+    lib.spec_default_mfma_min_rows.argtypes = []
+    lib.spec_default_mfma_min_rows.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().spec_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, what):
+    if status != SPEC_OK:
+        raise SpecError(status, what)
+
+
+def _dev(t, dtype, name):
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor")
+    return t
+
+
+class Weights:
+    """Target weights registered with the library (it keeps its own copy).
+
+    blocks: list of dicts with "w_up" [d][ffn], "w_down" [ffn][d] and an
+    optional "gain" [d]; lm_head [d][V].  All tensors on the device, all
+    torch.float32 or all torch.bfloat16.
+    """
+
+    def __init__(self, blocks, lm_head, eps=1e-6, keep_rowmajor=False, mfma_min_rows=0,
+                 stream=None):
+        lib = load()
+        dtype = lm_head.dtype
+        if dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("weights must be float32 or bfloat16")
+        d, V = lm_head.shape
+        ffn = blocks[0]["w_up"].shape[1] if blocks else 1
+        for blk in blocks:
+            _dev(blk["w_up"], dtype, "w_up")
+            _dev(blk["w_down"], dtype, "w_down")
+            if tuple(blk["w_up"].shape) != (d, ffn) or tuple(blk["w_down"].shape) != (ffn, d):
+                raise ValueError("block shapes must be [d][ffn] and [ffn][d]")
+        _dev(lm_head, dtype, "lm_head")
+        n = len(blocks)
+        gains = [blk.get("gain") for blk in blocks]
+        if any(g is not None for g in gains) and any(g is None for g in gains):
+            raise ValueError("give a gain for every block or for none")
+        arr = ctypes.c_void_p * max(n, 1)
+        self._up = arr(*[b["w_up"].data_ptr() for b in blocks])
+        self._down = arr(*[b["w_down"].data_ptr() for b in blocks])
+        self._gain = arr(*[_dev(g, dtype, "gain").data_ptr() for g in gains]) if n and gains[0] is not None else None
+        desc = _Desc(int(d), int(ffn), n, int(V), SPEC_BF16 if dtype == torch.bfloat16 else SPEC_F32,
+                     float(eps), ctypes.cast(self._up, ctypes.POINTER(ctypes.c_void_p)),
+                     ctypes.cast(self._down, ctypes.POINTER(ctypes.c_void_p)),
+                     ctypes.cast(self._gain, ctypes.POINTER(ctypes.c_void_p)) if self._gain is not None else None,
+                     ctypes.c_void_p(lm_head.data_ptr()),
+                     SPEC_FLAG_KEEP_ROWMAJOR if keep_rowmajor else 0, int(mfma_min_rows))
+        handle = ctypes.c_void_p()
+        _check(lib.spec_weights_create(ctypes.byref(desc), _stream(stream), ctypes.byref(handle)),
+               "spec_weights_create")
+        self.handle = handle
+        self.d, self.ffn, self.n_blocks, self.V, self.dtype = int(d), int(ffn), n, int(V), dtype
+
+    def close(self):
+        if getattr(self, "handle", None):
+            load().spec_weights_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, B, gamma):
+        return int(load().spec_workspace_size(self.handle, int(B), int(gamma)))
+
+    def workspace(self, B, gamma):
+        n = self.workspace_size(B, gamma)
+        if n == 0:
+            raise SpecError(SPEC_EINVAL, "spec_workspace_size")
+        return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def _outputs(B, gamma, n_accepted, emitted):
+    if n_accepted is None:
+        n_accepted = torch.empty(B, dtype=torch.int32, device="cuda")
+    if emitted is None:
+        emitted = torch.empty((B, gamma + 1), dtype=torch.int32, device="cuda")
+    return n_accepted, emitted
+
+
+def verify(w, hidden, draft_tokens, q, temperature, top_p, seed, workspace=None,
+           n_accepted=None, emitted=None, stream=None):
+    """spec_verify; returns (n_accepted [B], emitted [B][gamma+1]) int32."""
+    B, G1, d = hidden.shape
+    gamma = G1 - 1
+    _dev(hidden, torch.float32, "hidden")
+    _dev(draft_tokens, torch.int32, "draft_tokens")
+    if q is not None:
+        _dev(q, torch.float32, "q")
+    n_accepted, emitted = _outputs(B, gamma, n_accepted, emitted)
+    if workspace is None:
+        workspace = w.workspace(B, gamma)
+    _check(load().spec_verify(w.handle, B, gamma, _ptr(hidden), _ptr(draft_tokens), _ptr(q),
+                              float(temperature), float(top_p), int(seed), _ptr(n_accepted),
+                              _ptr(emitted), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "spec_verify")
+    return n_accepted, emitted
+
+
+def verify_debug(w, hidden, draft_tokens, q, temperature, top_p, seed, want_probs=True,
+                 workspace=None, stream=None):
+    """spec_verify_debug; returns (n_accepted, emitted, logits, p', q')."""
+    B, G1, d = hidden.shape
+    gamma = G1 - 1
+    _dev(hidden, torch.float32, "hidden")
+    _dev(draft_tokens, torch.int32, "draft_tokens")
+    n_accepted, emitted = _outputs(B, gamma, None, None)
+    logits = torch.empty((B, G1, w.V), dtype=torch.float32, device="cuda")
+    tempered = want_probs and temperature > 0
+    p_out = torch.empty((B, G1, w.V), dtype=torch.float32, device="cuda") if tempered else None
+    q_out = torch.empty((B, gamma, w.V), dtype=torch.float32, device="cuda") if tempered else None
+    if workspace is None:
+        workspace = w.workspace(B, gamma)
+    _check(load().spec_verify_debug(w.handle, B, gamma, _ptr(hidden), _ptr(draft_tokens), _ptr(q),
+                                    float(temperature), float(top_p), int(seed), _ptr(n_accepted),
+                                    _ptr(emitted), _ptr(workspace), workspace.numel(),
+                                    _stream(stream), _ptr(logits), _ptr(p_out), _ptr(q_out)),
+           "spec_verify_debug")
+    return n_accepted, emitted, logits, p_out, q_out
+
+
+def workspace_size_from_logits(B, gamma, V):
+    return int(load().spec_workspace_size_from_logits(int(B), int(gamma), int(V)))
+
+
+def verify_from_logits(logits, draft_tokens, q, temperature, top_p, seed, workspace=None,
+                       n_accepted=None, emitted=None, stream=None):
+    """spec_verify_from_logits; logits [B][gamma+1][V] fp32 on the device."""
+    B, G1, V = logits.shape
+    gamma = G1 - 1
+    _dev(logits, torch.float32, "logits")
+    _dev(draft_tokens, torch.int32, "draft_tokens")
+    if q is not None:
+        _dev(q, torch.float32, "q")
+    n_accepted, emitted = _outputs(B, gamma, n_accepted, emitted)
+    if workspace is None:
+        n = workspace_size_from_logits(B, gamma, V)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    _check(load().spec_verify_from_logits(B, gamma, V, _ptr(logits), _ptr(draft_tokens), _ptr(q),
+                                          float(temperature), float(top_p), int(seed),
+                                          _ptr(n_accepted), _ptr(emitted), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)),
+           "spec_verify_from_logits")
+    return n_accepted, emitted
+
+
+def default_mfma_min_rows():
+    return int(load().spec_default_mfma_min_rows())

@@ -1,0 +1,388 @@
+// C ABI of the verification step: argument checks, workspace layout, weight
+// registration and the launch sequence (target pass, then the rule).
+
+#include <cmath>
+#include <new>
+#include <vector>
+
+#include "common.h"
+#include "internal.h"
+#include "specverify.h"
+
+using namespace sv;
+
+struct spec_weights {
+  int d = 0, ffn = 0, n_blocks = 0, V = 0, wdtype = 0;
+  float eps = 0.f;
+  uint32_t flags = 0;
+  int mfma_min_rows = 1;
+  int device = 0;
+  std::vector<Mat> up, down;
+  Mat lm;
+  std::vector<float*> gain;
+};
+
+namespace {
+
+constexpr int kDefaultMfmaMinRows = 1;
+constexpr int kMaxGamma = 4096;
+constexpr int kMaxRowsMfma = 224;
+constexpr int kMaxRowsFma = 192;
+
+inline int roundup(int x, int m) { return (x + m - 1) / m * m; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  int M = 0, ldd = 0, ldf = 0, Vs = 0, G = 0, nch = 0, ncnt = 0;
+  size_t h = 0, xg = 0, ss = 0, act = 0, part = 0, cnt = 0, logits = 0, pst = 0, pidx = 0,
+         qst = 0, rowinfo = 0, dec = 0, csum = 0, total = 0;
+};
+
+int gemm_path(const spec_weights* w, int M) {
+  if (w->wdtype == SPEC_F32) return PATH_FMA_F32;
+  const bool have_rm = w->lm.rowmajor != nullptr;
+  return (M >= w->mfma_min_rows || !have_rm) ? PATH_MFMA : PATH_FMA_BF16;
+}
+
+int max_rows(int path) { return path == PATH_MFMA ? kMaxRowsMfma : kMaxRowsFma; }
+
+// Sampling-side buffers, shared by both entry points.
+void layout_sampling(Layout& L, int B, int gamma, int V, size_t& off) {
+  L.G = (V + kGroupCols - 1) / kGroupCols;
+  L.nch = (V + kResampleChunk - 1) / kResampleChunk;
+  const size_t qrows = (size_t)B * gamma;
+  L.pst = off; off = align256(off + sizeof(float) * 2 * (size_t)L.M * L.G);
+  L.pidx = off; off = align256(off + sizeof(int) * (size_t)L.M * L.G);
+  L.qst = off; off = align256(off + sizeof(float) * 2 * qrows * L.G);
+  L.rowinfo = off; off = align256(off + sizeof(float) * 8 * ((size_t)L.M + qrows));
+  L.dec = off; off = align256(off + sizeof(int) * 4 * (size_t)B);
+  L.csum = off; off = align256(off + sizeof(double) * 2 * (size_t)B * L.nch);
+}
+
+Layout make_layout(const spec_weights* w, int B, int gamma) {
+  Layout L;
+  L.M = B * (gamma + 1);
+  L.ldd = roundup(w->d, kGroupCols);
+  L.ldf = roundup(w->ffn, kGroupCols);
+  L.Vs = roundup(w->V, kGroupCols);
+  const int path = gemm_path(w, L.M);
+  // run_gemm launches full chunks of max_rows(path) rows plus one remainder
+  const int chunk = std::min(L.M, max_rows(path));
+  const int rem = L.M % max_rows(path);
+  size_t part = 0;
+  int ncnt = 0;
+  auto consider = [&](const Mat& m) {
+    part = std::max(part, gemm_part_floats(path, chunk, m));
+    if (rem) part = std::max(part, gemm_part_floats(path, rem, m));
+    ncnt = std::max(ncnt, m.Np / kGroupCols);
+  };
+  for (int l = 0; l < w->n_blocks; ++l) { consider(w->up[l]); consider(w->down[l]); }
+  consider(w->lm);
+  L.ncnt = ncnt;
+  size_t off = 0;
+  const size_t M = L.M;
+  L.h = off; off = align256(off + sizeof(float) * M * L.ldd);
+  L.xg = off; off = align256(off + sizeof(float) * M * L.ldd);
+  L.ss = off; off = align256(off + sizeof(float) * M * (L.ldd / kGroupCols));
+  L.act = off; off = align256(off + sizeof(float) * M * L.ldf);
+  L.part = off; off = align256(off + sizeof(float) * part);
+  L.cnt = off; off = align256(off + sizeof(int) * (size_t)ncnt);
+  L.logits = off; off = align256(off + sizeof(float) * M * L.Vs);
+  layout_sampling(L, B, gamma, w->V, off);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+bool bad_scalars(float T, float top_p) {
+  if (!std::isfinite(T) || T < 0.f) return true;
+  if (T > 0.f && !(top_p > 0.f && top_p <= 1.f)) return true;
+  return false;
+}
+
+int tmode_of(float T) { return T == 0.f ? 0 : (T == 1.f ? 1 : 2); }
+
+void free_weights(spec_weights* w) {
+  if (!w) return;
+  auto fm = [](Mat& m) {
+    if (m.rowmajor) (void)hipFree(m.rowmajor);
+    if (m.mfma) (void)hipFree(m.mfma);
+    m.rowmajor = m.mfma = nullptr;
+  };
+  for (auto& m : w->up) fm(m);
+  for (auto& m : w->down) fm(m);
+  fm(w->lm);
+  for (float* g : w->gain)
+    if (g) (void)hipFree(g);
+  delete w;
+}
+
+spec_status register_matrix(spec_weights* w, const void* src, int K, int N, bool keep_rm,
+                            Mat& m, hipStream_t st) {
+  m.K = K; m.N = N; m.Kp = roundup(K, kKStep); m.Np = roundup(N, kGroupCols);
+  const size_t elems = (size_t)m.Kp * m.Np;
+  if (w->wdtype == SPEC_F32) {
+    if (hipMalloc(&m.rowmajor, elems * sizeof(float)) != hipSuccess) { m.rowmajor = nullptr; return SPEC_ENOMEM; }
+    if (launch_copy_rowmajor(src, 0, K, N, m.rowmajor, 0, m.Kp, m.Np, st) != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
+  }
+  if (hipMalloc(&m.mfma, elems * sizeof(uint16_t)) != hipSuccess) { m.mfma = nullptr; return SPEC_ENOMEM; }
+  if (launch_pack_mfma(src, 1, K, N, m.mfma, m.Kp, m.Np, st) != hipSuccess) return SPEC_EHIP;
+  if (keep_rm) {
+    if (hipMalloc(&m.rowmajor, elems * sizeof(uint16_t)) != hipSuccess) { m.rowmajor = nullptr; return SPEC_ENOMEM; }
+    if (launch_copy_rowmajor(src, 1, K, N, m.rowmajor, 1, m.Kp, m.Np, st) != hipSuccess) return SPEC_EHIP;
+  }
+  return SPEC_OK;
+}
+
+const void* mat_ptr(const Mat& m, int path) { return path == PATH_MFMA ? m.mfma : m.rowmajor; }
+
+// One GEMM over all M rows, in row chunks the kernels can hold.
+hipError_t run_gemm(int path, int epi, const Mat& W, const float* X, int ldx, int M, EpiArgs e,
+                    float* part, int* cnt, hipStream_t st) {
+  const int chunk = max_rows(path);
+  for (int m0 = 0; m0 < M; m0 += chunk) {
+    GemmArgs a;
+    a.X = X + (size_t)m0 * ldx;
+    a.ldx = ldx;
+    a.M = std::min(chunk, M - m0);
+    a.K = W.K;
+    a.W = mat_ptr(W, path);
+    a.Np = W.Np;
+    a.KS = W.Kp / kKStep;
+    a.G = W.Np / kGroupCols;
+    choose_split(path, a.M, a.KS, a.G, a.S, a.kps);
+    a.part = part;
+    a.cnt = cnt;
+    a.e = e;
+    a.e.out = e.out + (size_t)m0 * e.ldo;
+    if (epi == EPI_UP) a.e.ss_in = e.ss_in + (size_t)m0 * e.ss_ld;
+    if (epi == EPI_DOWN) {
+      a.e.xg = e.xg + (size_t)m0 * e.ldo;
+      a.e.ss_out = e.ss_out + (size_t)m0 * e.ss_ld;
+    }
+    a.e.row0 = m0;
+    const hipError_t err = launch_gemm(path, epi, a, st);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+spec_status check_device(const spec_weights* w) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SPEC_EHIP;
+  return dev == w->device ? SPEC_OK : SPEC_EINVAL;
+}
+
+spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float* hidden,
+                        const int32_t* draft, const float* q, float T, float top_p,
+                        uint64_t seed, int32_t* n_acc, int32_t* emitted, void* ws,
+                        size_t ws_bytes, void* stream, float* logits_out, float* p_out,
+                        float* q_out) {
+  if (!w || B < 1 || gamma < 0 || gamma > kMaxGamma || !hidden || !n_acc || !emitted)
+    return SPEC_EINVAL;
+  if (gamma > 0 && !draft) return SPEC_EINVAL;
+  if (bad_scalars(T, top_p)) return SPEC_EINVAL;
+  if (T > 0.f && gamma > 0 && !q) return SPEC_EINVAL;
+  if ((size_t)B * (gamma + 1) > (size_t)INT32_MAX / 2) return SPEC_EINVAL;
+  const Layout L = make_layout(w, B, gamma);
+  if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) & 255)) return SPEC_EWORKSPACE;
+  if (spec_status s = check_device(w); s != SPEC_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+
+  const int M = L.M, path = gemm_path(w, M);
+  float* h = at<float>(ws, L.h);
+  float* xg = at<float>(ws, L.xg);
+  float* ss = at<float>(ws, L.ss);
+  float* act = at<float>(ws, L.act);
+  float* part = at<float>(ws, L.part);
+  int* cnt = at<int>(ws, L.cnt);
+  float* logits = at<float>(ws, L.logits);
+  const int ss_ld = L.ldd / kGroupCols;
+  const int tmode = tmode_of(T);
+
+  hipError_t err = launch_prep(h, xg, ss, ss_ld, hidden, w->n_blocks ? w->gain[0] : nullptr, M,
+                               w->d, L.ldd, cnt, L.ncnt, st);
+  for (int l = 0; l < w->n_blocks && err == hipSuccess; ++l) {
+    EpiArgs up;
+    up.out = act; up.ldo = L.ldf; up.N = w->ffn;
+    up.ss_in = ss; up.ss_ld = ss_ld; up.ss_n = ss_ld;
+    up.inv_d = 1.0f / (float)w->d; up.eps = w->eps;
+    err = run_gemm(path, EPI_UP, w->up[l], xg, L.ldd, M, up, part, cnt, st);
+    if (err != hipSuccess) break;
+    EpiArgs dn;
+    dn.out = h; dn.ldo = L.ldd; dn.N = w->d;
+    dn.xg = xg; dn.gain_next = l + 1 < w->n_blocks ? w->gain[l + 1] : nullptr;
+    dn.ss_out = ss; dn.ss_ld = ss_ld;
+    err = run_gemm(path, EPI_DOWN, w->down[l], act, L.ldf, M, dn, part, cnt, st);
+  }
+  if (err == hipSuccess) {
+    EpiArgs lm;
+    lm.out = logits; lm.ldo = L.Vs; lm.N = w->V;
+    lm.pst = at<float>(ws, L.pst); lm.pidx = at<int>(ws, L.pidx); lm.qst = at<float>(ws, L.qst);
+    lm.q = q; lm.G = L.G; lm.G1 = gamma + 1; lm.gamma = gamma; lm.V = w->V;
+    lm.tmode = tmode; lm.invT = tmode ? 1.0f / T : 1.0f;
+    err = run_gemm(path, EPI_LM, w->lm, h, L.ldd, M, lm, part, cnt, st);
+  }
+  SampleArgs sa;
+  if (err == hipSuccess) {
+    sa.B = B; sa.gamma = gamma; sa.V = w->V; sa.G = L.G; sa.M = M;
+    sa.logits = logits; sa.ldl = L.Vs; sa.q = q; sa.draft = draft;
+    sa.T = T; sa.invT = tmode ? 1.0f / T : 1.0f; sa.top_p = top_p; sa.tmode = tmode; sa.seed = seed;
+    sa.n_acc = n_acc; sa.emitted = emitted;
+    sa.pst = at<float>(ws, L.pst); sa.pidx = at<int>(ws, L.pidx); sa.qst = at<float>(ws, L.qst);
+    sa.rowinfo = at<float>(ws, L.rowinfo); sa.dec = at<int>(ws, L.dec);
+    sa.csum = at<double>(ws, L.csum); sa.nch = L.nch;
+    err = launch_sampling(sa, st);
+  }
+  if (err == hipSuccess && (p_out || q_out)) {
+    sa.p_out = p_out; sa.q_out = q_out;
+    err = launch_dump_probs(sa, st);
+  }
+  if (err == hipSuccess && logits_out)
+    err = hipMemcpy2DAsync(logits_out, sizeof(float) * w->V, logits, sizeof(float) * L.Vs,
+                           sizeof(float) * w->V, M, hipMemcpyDeviceToDevice, st);
+  return err == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_status_string(spec_status s) {
+  switch (s) {
+    case SPEC_OK: return "ok";
+    case SPEC_EINVAL: return "invalid argument";
+    case SPEC_EDTYPE: return "unsupported weight dtype";
+    case SPEC_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case SPEC_EHIP: return "HIP runtime error";
+    case SPEC_ENOMEM: return "device allocation failed";
+  }
+  return "unknown status";
+}
+
+int32_t spec_default_mfma_min_rows(void) { return kDefaultMfmaMinRows; }
+
+spec_status spec_weights_create(const spec_weights_desc* desc, void* stream, spec_weights_t* out) {
+  if (!desc || !out) return SPEC_EINVAL;
+  if (desc->wdtype != SPEC_F32 && desc->wdtype != SPEC_BF16) return SPEC_EDTYPE;
+  if (desc->d < 1 || desc->ffn < 1 || desc->vocab < 1 || desc->n_blocks < 0) return SPEC_EINVAL;
+  if (!std::isfinite(desc->rms_eps) || desc->rms_eps < 0.f || !desc->lm_head) return SPEC_EINVAL;
+  if (desc->n_blocks > 0 && (!desc->w_up || !desc->w_down)) return SPEC_EINVAL;
+  for (int l = 0; l < desc->n_blocks; ++l) {
+    if (!desc->w_up[l] || !desc->w_down[l]) return SPEC_EINVAL;
+    if (desc->norm_gain && !desc->norm_gain[l]) return SPEC_EINVAL;
+  }
+  spec_weights* w = new (std::nothrow) spec_weights;
+  if (!w) return SPEC_ENOMEM;
+  w->d = desc->d; w->ffn = desc->ffn; w->n_blocks = desc->n_blocks; w->V = desc->vocab;
+  w->wdtype = desc->wdtype; w->eps = desc->rms_eps; w->flags = desc->flags;
+  w->mfma_min_rows = desc->mfma_min_rows > 0 ? desc->mfma_min_rows : kDefaultMfmaMinRows;
+  if (hipGetDevice(&w->device) != hipSuccess) { delete w; return SPEC_EHIP; }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool keep_rm = w->wdtype == SPEC_BF16 &&
+                       ((desc->flags & SPEC_FLAG_KEEP_ROWMAJOR) || w->mfma_min_rows > 1);
+  w->up.resize(w->n_blocks);
+  w->down.resize(w->n_blocks);
+  w->gain.assign(w->n_blocks, nullptr);
+  spec_status s = SPEC_OK;
+  for (int l = 0; l < w->n_blocks && s == SPEC_OK; ++l) {
+    s = register_matrix(w, desc->w_up[l], w->d, w->ffn, keep_rm, w->up[l], st);
+    if (s == SPEC_OK) s = register_matrix(w, desc->w_down[l], w->ffn, w->d, keep_rm, w->down[l], st);
+    if (s == SPEC_OK) {
+      if (hipMalloc(&w->gain[l], sizeof(float) * w->d) != hipSuccess) { w->gain[l] = nullptr; s = SPEC_ENOMEM; }
+      else if (launch_vec_to_f32(desc->norm_gain ? desc->norm_gain[l] : nullptr, w->wdtype, w->d,
+                                 w->gain[l], st) != hipSuccess) s = SPEC_EHIP;
+    }
+  }
+  if (s == SPEC_OK) s = register_matrix(w, desc->lm_head, w->d, w->V, keep_rm, w->lm, st);
+  if (s == SPEC_OK && hipStreamSynchronize(st) != hipSuccess) s = SPEC_EHIP;
+  if (s != SPEC_OK) {
+    (void)hipStreamSynchronize(st);
+    free_weights(w);
+    return s;
+  }
+  *out = w;
+  return SPEC_OK;
+}
+
+spec_status spec_weights_destroy(spec_weights_t w) {
+  if (w) {
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(w->device);
+    (void)hipDeviceSynchronize();
+    free_weights(w);
+    (void)hipSetDevice(prev);
+  }
+  return SPEC_OK;
+}
+
+size_t spec_workspace_size(spec_weights_t w, int32_t B, int32_t gamma) {
+  if (!w || B < 1 || gamma < 0 || gamma > kMaxGamma) return 0;
+  return make_layout(w, B, gamma).total;
+}
+
+spec_status spec_verify(spec_weights_t w, int32_t B, int32_t gamma, const float* hidden,
+                        const int32_t* draft_tokens, const float* q, float temperature,
+                        float top_p, uint64_t seed, int32_t* n_accepted, int32_t* emitted,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return verify_impl(w, B, gamma, hidden, draft_tokens, q, temperature, top_p, seed, n_accepted,
+                     emitted, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+spec_status spec_verify_debug(spec_weights_t w, int32_t B, int32_t gamma, const float* hidden,
+                              const int32_t* draft_tokens, const float* q, float temperature,
+                              float top_p, uint64_t seed, int32_t* n_accepted, int32_t* emitted,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              float* logits_out, float* p_out, float* q_out) {
+  return verify_impl(w, B, gamma, hidden, draft_tokens, q, temperature, top_p, seed, n_accepted,
+                     emitted, workspace, workspace_bytes, stream, logits_out, p_out, q_out);
+}
+
+size_t spec_workspace_size_from_logits(int32_t B, int32_t gamma, int32_t vocab) {
+  if (B < 1 || gamma < 0 || gamma > kMaxGamma || vocab < 1) return 0;
+  Layout L;
+  L.M = B * (gamma + 1);
+  size_t off = 0;
+  layout_sampling(L, B, gamma, vocab, off);
+  return off;
+}
+
+spec_status spec_verify_from_logits(int32_t B, int32_t gamma, int32_t vocab, const float* logits,
+                                    const int32_t* draft_tokens, const float* q,
+                                    float temperature, float top_p, uint64_t seed,
+                                    int32_t* n_accepted, int32_t* emitted, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (B < 1 || gamma < 0 || gamma > kMaxGamma || vocab < 1 || !logits || !n_accepted || !emitted)
+    return SPEC_EINVAL;
+  if (gamma > 0 && !draft_tokens) return SPEC_EINVAL;
+  if (bad_scalars(temperature, top_p)) return SPEC_EINVAL;
+  if (temperature > 0.f && gamma > 0 && !q) return SPEC_EINVAL;
+  Layout L;
+  L.M = B * (gamma + 1);
+  size_t off = 0;
+  layout_sampling(L, B, gamma, vocab, off);
+  if (!workspace || workspace_bytes < off || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return SPEC_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int tmode = tmode_of(temperature);
+  SampleArgs sa;
+  sa.B = B; sa.gamma = gamma; sa.V = vocab; sa.G = L.G; sa.M = L.M;
+  sa.logits = logits; sa.ldl = vocab; sa.q = q; sa.draft = draft_tokens;
+  sa.T = temperature; sa.invT = tmode ? 1.0f / temperature : 1.0f; sa.top_p = top_p;
+  sa.tmode = tmode; sa.seed = seed;
+  sa.n_acc = n_accepted; sa.emitted = emitted;
+  sa.pst = at<float>(workspace, L.pst); sa.pidx = at<int>(workspace, L.pidx);
+  sa.qst = at<float>(workspace, L.qst); sa.rowinfo = at<float>(workspace, L.rowinfo);
+  sa.dec = at<int>(workspace, L.dec); sa.csum = at<double>(workspace, L.csum); sa.nch = L.nch;
+  hipError_t err = launch_tile_stats(sa, st);
+  if (err == hipSuccess) err = launch_sampling(sa, st);
+  return err == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+}  // extern "C"

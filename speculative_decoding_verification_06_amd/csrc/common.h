@@ -1,0 +1,174 @@
+// Device helpers shared by the gfx950 kernels of the verification step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr int kGroupCols = 64;     // output columns per GEMM work group / stats tile
+constexpr int kKStep = 32;         // K rows per MFMA step (16x16x32)
+
+// ---- bfloat16 ------------------------------------------------------------
+// A bf16 is the top half of an fp32, so widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round fp32 to bf16, nearest-even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  uint32_t b = __float_as_uint(x);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// Split 8 fp32 values into NSPLIT bf16 vectors whose sum reproduces them:
+// hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid).  Each
+// difference is exact in fp32, so three terms carry the full 24-bit
+// significand and two carry 16 bits.
+template <int NSPLIT>
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8 (&out)[NSPLIT]) {
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = x[j];
+#pragma unroll
+  for (int s = 0; s < NSPLIT; ++s) {
+    u32x4 packed;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t b0 = bf16_bits_rne(r[2 * p]);
+      uint32_t b1 = bf16_bits_rne(r[2 * p + 1]);
+      packed[p] = b0 | (b1 << 16);
+      if (s + 1 < NSPLIT) {
+        r[2 * p] -= __uint_as_float(b0 << 16);
+        r[2 * p + 1] -= __uint_as_float(b1 << 16);
+      }
+    }
+    out[s] = __builtin_bit_cast(bf16x8, packed);
+  }
+}
+
+// ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) -------------------
+// Each round: (hi0,lo0) = M0*c0, (hi1,lo1) = M1*c2,
+// c = (hi1^c1^k0, lo1, hi0^c3^k1, lo0); the key is bumped by the Weyl
+// constants between rounds.
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+  }
+}
+
+// Uniforms of batch row b, position i: word 0 -> r (ratio test), word 1 -> u
+// (inverse CDF); top 24 bits scaled by 2^-24, exact in fp32.
+__device__ __forceinline__ void row_uniforms(uint64_t seed, int b, int i, float& r, float& u) {
+  uint64_t c[4] = {(uint64_t)i, (uint64_t)b, 0ull, 0ull};
+  philox4x64_10(c, seed, 0ull);
+  r = (float)(uint32_t)(c[0] >> 40) * 0x1.0p-24f;
+  u = (float)(uint32_t)(c[1] >> 40) * 0x1.0p-24f;
+}
+
+// ---- wave reductions (butterfly, identical result in every lane) ---------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// Max with the lowest index among equal maxima.
+__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(idx, o, kWave);
+    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+  }
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Online-softmax merge of (max, sum of exp((x - max) * invT)) pairs.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2, float invT) {
+  if (s2 == 0.0f) return;
+  if (s == 0.0f) { m = m2; s = s2; return; }
+  if (m2 > m) { s = s * expf((m - m2) * invT) + s2; m = m2; }
+  else { s = s + s2 * expf((m2 - m) * invT); }
+}
+__device__ __forceinline__ void wave_lse(float& m, float& s, float invT) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, kWave);
+    const float s2 = __shfl_xor(s, o, kWave);
+    // merge in a lane-independent order so every lane gets the same bits
+    float am = m, as = s, bm = m2, bs = s2;
+    const bool swap = (threadIdx.x & o) != 0;
+    if (swap) { am = m2; as = s2; bm = m; bs = s; }
+    lse_merge(am, as, bm, bs, invT);
+    m = am; s = as;
+  }
+}
+
+// Order-preserving map of an fp32 logit to uint32 (larger value, larger key).
+__device__ __forceinline__ uint32_t logit_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Per-tile statistics of one logits row tile (64 columns, one value per
+// lane): greedy -> (max, lowest argmax); otherwise (max, sum exp((l - max)/T))
+// for p, and for the matching draft row (i < gamma) the statistics of q':
+// T == 1 -> sum q; else (max y, sum exp(y - max y)) with y = log(q) / T.
+__device__ __forceinline__ void lm_tile_stats(float l, bool valid, int n, int grow, int g,
+                                              int G, int G1, int gamma, int V, int tmode,
+                                              float invT, const float* q, float* pst,
+                                              int* pidx, float* qst) {
+  const int lane = threadIdx.x & 63;
+  const size_t t = (size_t)grow * G + g;
+  if (tmode == 0) {
+    float v = valid ? l : -INFINITY;
+    int idx = valid ? n : 0x7fffffff;
+    wave_argmax(v, idx);
+    if (lane == 0) { pst[2 * t] = v; pst[2 * t + 1] = 0.f; pidx[t] = idx; }
+    return;
+  }
+  const float mx = wave_max(valid ? l : -INFINITY);
+  const float se = wave_sum(valid ? expf((l - mx) * invT) : 0.f);
+  if (lane == 0) { pst[2 * t] = mx; pst[2 * t + 1] = se; }
+  const int b = grow / G1, i = grow - b * G1;
+  if (i < gamma) {
+    const size_t qrow = (size_t)b * gamma + i;
+    const float qv = valid ? q[qrow * V + n] : 0.f;
+    float ym = 0.f, sq;
+    if (tmode == 1) {
+      sq = wave_sum(qv);
+    } else {
+      const float y = qv > 0.f ? logf(qv) * invT : -INFINITY;
+      ym = wave_max(y);
+      sq = wave_sum(qv > 0.f ? expf(y - ym) : 0.f);
+    }
+    if (lane == 0) {
+      const size_t tq = qrow * G + g;
+      qst[2 * tq] = ym;
+      qst[2 * tq + 1] = sq;
+    }
+  }
+}
+
+}  // namespace sv

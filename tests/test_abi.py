@@ -1,0 +1,95 @@
+"""The C-ABI library loads and exports every entry point include/*.h declares.
+
+CPU only: no call here touches a GPU (only host-side status strings, size
+queries and argument checks that return before any HIP call)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verification_06_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(spec_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_binding_list():
+    assert declared_symbols() == set(sv.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sv.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert sv.status_string(0) == "ok"
+    assert "workspace" in sv.status_string(-3)
+    assert sv.status_string(-99) == "unknown status"
+
+
+def test_default_threshold_is_positive():
+    assert sv.default_mfma_min_rows() >= 1
+
+
+def test_workspace_size_from_logits_is_host_arithmetic():
+    lib = sv.load()
+    assert lib.spec_workspace_size_from_logits(0, 4, 100) == 0
+    assert lib.spec_workspace_size_from_logits(1, -1, 100) == 0
+    assert lib.spec_workspace_size_from_logits(1, 4, 0) == 0
+    a = lib.spec_workspace_size_from_logits(1, 4, 512)
+    b = lib.spec_workspace_size_from_logits(8, 8, 128256)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+
+
+def test_argument_checks_return_before_any_launch():
+    lib = sv.load()
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)   # never dereferenced: every call below fails validation first
+    # null logits
+    assert lib.spec_verify_from_logits(1, 2, 10, None, fake, fake, 1.0, 1.0, 0, fake, fake,
+                                       fake, 1 << 20, None) == sv.SPEC_EINVAL
+    # bad temperature / top_p
+    for T, tp in ((-1.0, 1.0), (float("nan"), 1.0), (1.0, 0.0), (1.0, 1.5)):
+        assert lib.spec_verify_from_logits(1, 2, 10, fake, fake, fake, T, tp, 0, fake, fake,
+                                           fake, 1 << 20, None) == sv.SPEC_EINVAL
+    # q missing at T > 0
+    assert lib.spec_verify_from_logits(1, 2, 10, fake, fake, None, 1.0, 1.0, 0, fake, fake,
+                                       fake, 1 << 20, None) == sv.SPEC_EINVAL
+    # workspace too small / misaligned
+    assert lib.spec_verify_from_logits(1, 2, 10, fake, fake, fake, 1.0, 1.0, 0, fake, fake,
+                                       fake, 16, None) == sv.SPEC_EWORKSPACE
+    assert lib.spec_verify_from_logits(1, 2, 10, fake, fake, fake, 1.0, 1.0, 0, fake, fake,
+                                       vp(0x1001), 1 << 20, None) == sv.SPEC_EWORKSPACE
+    # null weights handle
+    assert lib.spec_verify(None, 1, 2, fake, fake, fake, 1.0, 1.0, 0, fake, fake, fake,
+                           1 << 20, None) == sv.SPEC_EINVAL
+    assert lib.spec_workspace_size(None, 1, 2) == 0
+    assert lib.spec_weights_destroy(None) == sv.SPEC_OK
+
+
+def test_weights_create_rejects_bad_descriptions():
+    lib = sv.load()
+    d = sv._Desc(0, 16, 1, 10, sv.SPEC_F32, 1e-6, None, None, None, ctypes.c_void_p(0x1000), 0, 0)
+    h = ctypes.c_void_p()
+    assert lib.spec_weights_create(ctypes.byref(d), None, ctypes.byref(h)) == sv.SPEC_EINVAL
+    d.d, d.wdtype = 16, 7
+    assert lib.spec_weights_create(ctypes.byref(d), None, ctypes.byref(h)) == sv.SPEC_EDTYPE
+    d.wdtype = sv.SPEC_F32
+    assert lib.spec_weights_create(ctypes.byref(d), None, ctypes.byref(h)) == sv.SPEC_EINVAL  # null block arrays
+    d.rms_eps = float("inf")
+    assert lib.spec_weights_create(ctypes.byref(d), None, ctypes.byref(h)) == sv.SPEC_EINVAL
+    assert not h.value

@@ -1,0 +1,103 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (one spec_verify call per pass, default paths).
+
+B = 1 workloads: every row is checked against the oracle.  Batched
+workloads: the oracle checks sampled sequences one by one; every other row
+is checked for properties that hold at any size (accepted prefix equals the
+drafts, one correction or bonus token in range, -1 padding; greedy rows agree
+with the argmax of the GPU's own logits)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from harness import (assert_tokens_match, calibrate_sigma, compare_probs, draft_q,
+                     greedy_drafts, log_measurement, logits_rel_err, sample_drafts,
+                     softmax_rows)
+
+pytestmark = pytest.mark.gpu
+sv = pytest.importorskip("speculative_decoding_verification_06_amd")
+DEV = "cuda"
+
+SAMPLED = {"mid": None, "large": None, "topp": [0, 5], "greedy": [0, 13, 31]}
+
+
+def to_f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def build(name):
+    wl = synth.WORKLOADS[name]
+    key = (200 + list(synth.WORKLOADS).index(name),)
+    B, gamma, V = wl.B, wl.gamma, wl.V
+    model = synth.model_torch(key, wl.d, wl.ffn, wl.n_blocks, V, wl.wdtype, DEV)
+    hidden = synth.normal_torch((*key, synth.T_HIDDEN), (B, gamma + 1, wl.d), 1.0, DEV)
+    rows = SAMPLED[name] or list(range(B))
+    host = {"blocks": [{"w_up": to_f64(b["w_up"]), "w_down": to_f64(b["w_down"]), "gain": None}
+                       for b in model["blocks"]],
+            "lm_head": to_f64(model["lm_head"])}
+    h_host = hidden.cpu().numpy()
+    ell = oracle.forward(h_host[rows], host["blocks"], host["lm_head"], 1e-6)
+    del host
+    gen = synth.generator(*key, synth.T_MISC)
+    z = synth.noise_np(key, len(rows), gamma, V, 1.0)
+    if name == "topp":
+        sig = gen.uniform(0.2, 1.5, size=len(rows)).astype(np.float32)
+        noise = z * sig.reshape(-1, 1, 1)
+    elif wl.alpha_target and wl.temperature > 0:
+        noise = calibrate_sigma(ell, z, wl.alpha_target) * z
+    else:
+        noise = 0.5 * z
+    q_s = draft_q(ell, noise)
+    if wl.temperature == 0:
+        d_s = greedy_drafts(ell, key, agree=0.75)
+    else:
+        d_s = sample_drafts(q_s, wl.temperature, wl.top_p, key)
+    # rows the oracle does not check: any valid draft distribution and drafts
+    q = softmax_rows(gen.standard_normal((B, gamma, V)).astype(np.float32) * 2).astype(np.float32)
+    draft = gen.integers(0, V, size=(B, gamma)).astype(np.int32)
+    q[rows], draft[rows] = q_s, d_s
+    return wl, model, hidden, ell, rows, q, draft
+
+
+@pytest.mark.parametrize("name", list(SAMPLED))
+def test_full_size_parity(name):
+    print(f"[case] full {name}", flush=True)
+    wl, model, hidden, ell, rows, q, draft = build(name)
+    w = sv.Weights(model["blocks"], model["lm_head"])
+    del model
+    torch.cuda.empty_cache()
+    T, top_p, seed = wl.temperature, wl.top_p, 2026
+    n, e, logits, p, qq = sv.verify_debug(w, hidden, torch.from_numpy(draft).to(DEV),
+                                          torch.from_numpy(q).to(DEV), T, top_p, seed)
+    torch.cuda.synchronize()
+    n, e, logits = n.cpu().numpy(), e.cpu().numpy(), logits.cpu().numpy()
+    err = logits_rel_err(logits[rows], ell)
+    print(f"{name}: logits rel err max {err.max():.2e} median {np.median(err):.2e}")
+    log_measurement({"what": f"full {name} logits", "rel_err_max": float(err.max()),
+                     "rel_err_median": float(np.median(err))})
+    assert err.max() <= 1e-3
+    ref = oracle.spec_verify_from_logits(ell, draft[rows], q[rows] if T > 0 else None, T,
+                                         top_p, seed, batch_ids=rows)
+    mism, flagged, total = assert_tokens_match(n[rows], e[rows], ref, what=name)
+    print(f"{name}: {total} decisions, {flagged} knife-edge, {len(mism)} differing rows, "
+          f"n_accepted {n.tolist()[:16]}")
+    if T > 0:
+        compare_probs(p.cpu().numpy()[rows], qq.cpu().numpy()[rows], ref, ell, q[rows], T, top_p,
+                      range(len(rows)), name)
+    # properties of every row
+    G1 = wl.gamma + 1
+    for b in range(wl.B):
+        k = int(n[b])
+        assert 0 <= k <= wl.gamma
+        assert np.array_equal(e[b, :k], draft[b, :k])
+        assert 0 <= e[b, k] < wl.V
+        assert (e[b, k + 1:] == -1).all()
+        if T == 0:
+            am = logits[b].argmax(axis=-1)
+            assert np.array_equal(draft[b, :k], am[:k]) and e[b, k] == am[k]
+            if k < wl.gamma:
+                assert draft[b, k] != am[k]
+    w.close()

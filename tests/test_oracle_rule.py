@@ -78,9 +78,39 @@ def test_top_p_ties_by_lower_id_and_full_keep():
     mask, _ = nucleus_mask(p, 0.5)
     assert mask.tolist() == [True, True, False, False]
     mask, m = nucleus_mask(p, 1.0)
-    assert mask.all() and m == []
+    assert mask.all() and not m.uncertain
     mask, _ = nucleus_mask(np.array([0.1, 0.6, 0.3]), 0.6)   # exactly reaching
     assert mask.tolist() == [False, True, False]
+
+
+def test_top_p_uncertain_tokens():
+    """Target rows: a near-tied cut puts the tied tokens in the uncertain set;
+    a cut that barely reaches top_p makes the last kept token uncertain; a
+    clear cut has none."""
+    p = np.array([0.5, 0.2, 0.2 * (1 - 1e-7), 0.1 - 0.2 * (1 - 1e-7) + 0.2])
+    p = p / p.sum()
+    mask, info = nucleus_mask(p, 0.6, logp_tol=1e-5)   # cut between tokens 1 and 2
+    assert mask.tolist() == [True, True, False, False]
+    assert info.uncertain == {1, 2} and info.mass > 0
+    mask, info = nucleus_mask(p, 0.6, logp_tol=0.0)
+    assert not info.uncertain
+    mask, info = nucleus_mask(np.array([0.5, 0.3, 0.2]), 0.6, logp_tol=1e-5)
+    assert not info.uncertain
+    mask, info = nucleus_mask(np.array([0.5, 0.3, 0.2]), 0.8 - 1e-7)   # 0.5 + 0.3 barely reaches
+    assert mask.tolist() == [True, True, False] and info.uncertain == {2}
+    mask, info = nucleus_mask(np.array([0.5, 0.3, 0.2]), 0.5 + 1e-7)   # 0.5 barely misses
+    assert info.uncertain == {1}
+
+
+def test_uncertain_token_ratio_test_is_a_knife_edge():
+    ell = np.log(np.array([0.5, 0.2, 0.2 * (1 - 1e-9), 0.1]))
+    p, cut = warp_logits(ell, 1.0, 0.6)
+    assert cut.uncertain == {1, 2}
+    q = np.full(4, 0.25)
+    _, _, mg = verify_row([p, p], [q], [2], [(0.1, 0.5), (0.5, 0.5)], p_cuts=[cut, cut])
+    assert mg[0][0] == "accept" and mg[0][2] == 0.0
+    _, _, mg = verify_row([p, p], [q], [0], [(0.999, 0.5), (0.5, 0.5)], p_cuts=[cut, cut])
+    assert mg[0][2] < abs(0.999 - p[0] / 0.25)
 
 
 def test_warp_logits_is_library_softmax():
