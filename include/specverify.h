@@ -161,6 +161,18 @@ spec_status spec_verify_from_logits(int32_t B, int32_t gamma, int32_t vocab,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* Kernel timing for benchmarks.  While enabled, every GEMM launch that
+ * spec_verify / spec_verify_debug make with these weights is bracketed by a
+ * pair of HIP events recorded on the launch stream (the library creates the
+ * events; a call may grow the pool).  spec_profile_read synchronises those
+ * events and returns, since the previous read or enable: the summed GEMM
+ * time in milliseconds, the number of GEMM launches, and the algorithmic
+ * weight bytes they streamed (K * N * bytes per weight, padding excluded);
+ * any out pointer may be NULL.  Reading clears the record. */
+spec_status spec_profile_enable(spec_weights_t w, int32_t on);
+spec_status spec_profile_read(spec_weights_t w, double* gemm_ms, int64_t* launches,
+                              int64_t* weight_bytes);
+
 /* Static text for a status code. */
 const char* spec_status_string(spec_status s);
 

@@ -21,7 +21,8 @@ SPEC_FLAG_KEEP_ROWMAJOR = 1
 # Every symbol include/specverify.h declares.
 EXPORTS = ["spec_weights_create", "spec_weights_destroy", "spec_workspace_size", "spec_verify",
            "spec_verify_debug", "spec_workspace_size_from_logits", "spec_verify_from_logits",
-           "spec_status_string", "spec_default_mfma_min_rows"]
+           "spec_status_string", "spec_default_mfma_min_rows", "spec_profile_enable",
+           "spec_profile_read"]
 
 
 class SpecError(RuntimeError):
@@ -69,6 +70,11 @@ def load():
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_default_mfma_min_rows.argtypes = []
     lib.spec_default_mfma_min_rows.restype = i32
+    lib.spec_profile_enable.argtypes = [vp, i32]
+    lib.spec_profile_enable.restype = i32
+    lib.spec_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.spec_profile_read.restype = i32
     _lib = lib
     return lib
 
@@ -150,6 +156,17 @@ class Weights:
             self.close()
         except Exception:
             pass
+
+    def profile(self, on=True):
+        """Bracket every GEMM launch with HIP events on its stream."""
+        _check(load().spec_profile_enable(self.handle, 1 if on else 0), "spec_profile_enable")
+
+    def profile_read(self):
+        """(summed GEMM ms, GEMM launches, algorithmic weight bytes) since the last read."""
+        ms, n, b = ctypes.c_double(), ctypes.c_int64(), ctypes.c_int64()
+        _check(load().spec_profile_read(self.handle, ctypes.byref(ms), ctypes.byref(n),
+                                        ctypes.byref(b)), "spec_profile_read")
+        return ms.value, n.value, b.value
 
     def workspace_size(self, B, gamma):
         return int(load().spec_workspace_size(self.handle, int(B), int(gamma)))

@@ -20,6 +20,11 @@ struct spec_weights {
   std::vector<Mat> up, down;
   Mat lm;
   std::vector<float*> gain;
+  // optional GEMM timing (spec_profile_*)
+  bool prof = false;
+  std::vector<hipEvent_t> ev;       // pairs: [2i] before, [2i+1] after launch i
+  std::vector<int64_t> ev_bytes;    // algorithmic weight bytes of launch i
+  size_t ev_used = 0;               // launches recorded
 };
 
 namespace {
@@ -33,9 +38,9 @@ inline int roundup(int x, int m) { return (x + m - 1) / m * m; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  int M = 0, ldd = 0, ldf = 0, Vs = 0, G = 0, nch = 0, ncnt = 0;
-  size_t h = 0, xg = 0, ss = 0, act = 0, part = 0, cnt = 0, logits = 0, pst = 0, pidx = 0,
-         qst = 0, rowinfo = 0, dec = 0, csum = 0, total = 0;
+  int M = 0, ldd = 0, ldf = 0, Vs = 0, G = 0, nch = 0;
+  size_t h = 0, xg = 0, ss = 0, act = 0, logits = 0, pst = 0, pidx = 0, qst = 0, rowinfo = 0,
+         dec = 0, csum = 0, total = 0;
 };
 
 int gemm_path(const spec_weights* w, int M) {
@@ -48,7 +53,7 @@ int max_rows(int path) { return path == PATH_MFMA ? kMaxRowsMfma : kMaxRowsFma; 
 
 // Sampling-side buffers, shared by both entry points.
 void layout_sampling(Layout& L, int B, int gamma, int V, size_t& off) {
-  L.G = (V + kGroupCols - 1) / kGroupCols;
+  L.G = (V + kSub - 1) / kSub;
   L.nch = (V + kResampleChunk - 1) / kResampleChunk;
   const size_t qrows = (size_t)B * gamma;
   L.pst = off; off = align256(off + sizeof(float) * 2 * (size_t)L.M * L.G);
@@ -65,28 +70,12 @@ Layout make_layout(const spec_weights* w, int B, int gamma) {
   L.ldd = roundup(w->d, kGroupCols);
   L.ldf = roundup(w->ffn, kGroupCols);
   L.Vs = roundup(w->V, kGroupCols);
-  const int path = gemm_path(w, L.M);
-  // run_gemm launches full chunks of max_rows(path) rows plus one remainder
-  const int chunk = std::min(L.M, max_rows(path));
-  const int rem = L.M % max_rows(path);
-  size_t part = 0;
-  int ncnt = 0;
-  auto consider = [&](const Mat& m) {
-    part = std::max(part, gemm_part_floats(path, chunk, m));
-    if (rem) part = std::max(part, gemm_part_floats(path, rem, m));
-    ncnt = std::max(ncnt, m.Np / kGroupCols);
-  };
-  for (int l = 0; l < w->n_blocks; ++l) { consider(w->up[l]); consider(w->down[l]); }
-  consider(w->lm);
-  L.ncnt = ncnt;
   size_t off = 0;
   const size_t M = L.M;
   L.h = off; off = align256(off + sizeof(float) * M * L.ldd);
   L.xg = off; off = align256(off + sizeof(float) * M * L.ldd);
-  L.ss = off; off = align256(off + sizeof(float) * M * (L.ldd / kGroupCols));
+  L.ss = off; off = align256(off + sizeof(float) * M * (L.ldd / kSub));
   L.act = off; off = align256(off + sizeof(float) * M * L.ldf);
-  L.part = off; off = align256(off + sizeof(float) * part);
-  L.cnt = off; off = align256(off + sizeof(int) * (size_t)ncnt);
   L.logits = off; off = align256(off + sizeof(float) * M * L.Vs);
   layout_sampling(L, B, gamma, w->V, off);
   L.total = off;
@@ -116,6 +105,7 @@ void free_weights(spec_weights* w) {
   fm(w->lm);
   for (float* g : w->gain)
     if (g) (void)hipFree(g);
+  for (hipEvent_t e : w->ev) (void)hipEventDestroy(e);
   delete w;
 }
 
@@ -128,8 +118,9 @@ spec_status register_matrix(spec_weights* w, const void* src, int K, int N, bool
     if (launch_copy_rowmajor(src, 0, K, N, m.rowmajor, 0, m.Kp, m.Np, st) != hipSuccess) return SPEC_EHIP;
     return SPEC_OK;
   }
+  m.nt = mfma_block_tiles(m.Np);
   if (hipMalloc(&m.mfma, elems * sizeof(uint16_t)) != hipSuccess) { m.mfma = nullptr; return SPEC_ENOMEM; }
-  if (launch_pack_mfma(src, 1, K, N, m.mfma, m.Kp, m.Np, st) != hipSuccess) return SPEC_EHIP;
+  if (launch_pack_mfma(src, 1, K, N, m.mfma, m.Kp, m.Np, m.nt, st) != hipSuccess) return SPEC_EHIP;
   if (keep_rm) {
     if (hipMalloc(&m.rowmajor, elems * sizeof(uint16_t)) != hipSuccess) { m.rowmajor = nullptr; return SPEC_ENOMEM; }
     if (launch_copy_rowmajor(src, 1, K, N, m.rowmajor, 1, m.Kp, m.Np, st) != hipSuccess) return SPEC_EHIP;
@@ -139,9 +130,38 @@ spec_status register_matrix(spec_weights* w, const void* src, int K, int N, bool
 
 const void* mat_ptr(const Mat& m, int path) { return path == PATH_MFMA ? m.mfma : m.rowmajor; }
 
+hipError_t run_gemm_rows(int path, const Mat& W, const float* X, int ldx, int M, EpiArgs e,
+                         hipStream_t st);
+
+hipError_t prof_event(spec_weights* w, size_t idx, hipStream_t st) {
+  while (w->ev.size() <= idx) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return err;
+    w->ev.push_back(e);
+  }
+  return hipEventRecord(w->ev[idx], st);
+}
+
 // One GEMM over all M rows, in row chunks the kernels can hold.
-hipError_t run_gemm(int path, int epi, const Mat& W, const float* X, int ldx, int M, EpiArgs e,
-                    float* part, int* cnt, hipStream_t st) {
+hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, int ldx, int M,
+                    EpiArgs e, hipStream_t st) {
+  if (w->prof) {
+    const hipError_t err = prof_event(w, 2 * w->ev_used, st);
+    if (err != hipSuccess) return err;
+  }
+  const hipError_t err = run_gemm_rows(path, W, X, ldx, M, e, st);
+  if (err != hipSuccess || !w->prof) return err;
+  const hipError_t err2 = prof_event(w, 2 * w->ev_used + 1, st);
+  if (err2 != hipSuccess) return err2;
+  w->ev_bytes.resize(w->ev_used + 1);
+  w->ev_bytes[w->ev_used] = (int64_t)W.K * W.N * (w->wdtype == SPEC_F32 ? 4 : 2);
+  ++w->ev_used;
+  return hipSuccess;
+}
+
+hipError_t run_gemm_rows(int path, const Mat& W, const float* X, int ldx, int M, EpiArgs e,
+                         hipStream_t st) {
   const int chunk = max_rows(path);
   for (int m0 = 0; m0 < M; m0 += chunk) {
     GemmArgs a;
@@ -152,19 +172,16 @@ hipError_t run_gemm(int path, int epi, const Mat& W, const float* X, int ldx, in
     a.W = mat_ptr(W, path);
     a.Np = W.Np;
     a.KS = W.Kp / kKStep;
-    a.G = W.Np / kGroupCols;
-    choose_split(path, a.M, a.KS, a.G, a.S, a.kps);
-    a.part = part;
-    a.cnt = cnt;
     a.e = e;
     a.e.out = e.out + (size_t)m0 * e.ldo;
-    if (epi == EPI_UP) a.e.ss_in = e.ss_in + (size_t)m0 * e.ss_ld;
-    if (epi == EPI_DOWN) {
+    if (e.kind == EPI_UP) a.e.ss_in = e.ss_in + (size_t)m0 * e.ss_ld;
+    if (e.kind == EPI_DOWN) {
       a.e.xg = e.xg + (size_t)m0 * e.ldo;
       a.e.ss_out = e.ss_out + (size_t)m0 * e.ss_ld;
     }
     a.e.row0 = m0;
-    const hipError_t err = launch_gemm(path, epi, a, st);
+    const GemmPlan p = plan_gemm(path, a.M, W);
+    const hipError_t err = launch_gemm(p, a, st);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
@@ -198,34 +215,35 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
   float* xg = at<float>(ws, L.xg);
   float* ss = at<float>(ws, L.ss);
   float* act = at<float>(ws, L.act);
-  float* part = at<float>(ws, L.part);
-  int* cnt = at<int>(ws, L.cnt);
   float* logits = at<float>(ws, L.logits);
-  const int ss_ld = L.ldd / kGroupCols;
+  const int ss_ld = L.ldd / kSub;
   const int tmode = tmode_of(T);
 
   hipError_t err = launch_prep(h, xg, ss, ss_ld, hidden, w->n_blocks ? w->gain[0] : nullptr, M,
-                               w->d, L.ldd, cnt, L.ncnt, st);
+                               w->d, L.ldd, st);
   for (int l = 0; l < w->n_blocks && err == hipSuccess; ++l) {
     EpiArgs up;
+    up.kind = EPI_UP;
     up.out = act; up.ldo = L.ldf; up.N = w->ffn;
     up.ss_in = ss; up.ss_ld = ss_ld; up.ss_n = ss_ld;
     up.inv_d = 1.0f / (float)w->d; up.eps = w->eps;
-    err = run_gemm(path, EPI_UP, w->up[l], xg, L.ldd, M, up, part, cnt, st);
+    err = run_gemm(w, path, w->up[l], xg, L.ldd, M, up, st);
     if (err != hipSuccess) break;
     EpiArgs dn;
+    dn.kind = EPI_DOWN;
     dn.out = h; dn.ldo = L.ldd; dn.N = w->d;
     dn.xg = xg; dn.gain_next = l + 1 < w->n_blocks ? w->gain[l + 1] : nullptr;
     dn.ss_out = ss; dn.ss_ld = ss_ld;
-    err = run_gemm(path, EPI_DOWN, w->down[l], act, L.ldf, M, dn, part, cnt, st);
+    err = run_gemm(w, path, w->down[l], act, L.ldf, M, dn, st);
   }
   if (err == hipSuccess) {
     EpiArgs lm;
+    lm.kind = EPI_LM;
     lm.out = logits; lm.ldo = L.Vs; lm.N = w->V;
     lm.pst = at<float>(ws, L.pst); lm.pidx = at<int>(ws, L.pidx); lm.qst = at<float>(ws, L.qst);
     lm.q = q; lm.G = L.G; lm.G1 = gamma + 1; lm.gamma = gamma; lm.V = w->V;
     lm.tmode = tmode; lm.invT = tmode ? 1.0f / T : 1.0f;
-    err = run_gemm(path, EPI_LM, w->lm, h, L.ldd, M, lm, part, cnt, st);
+    err = run_gemm(w, path, w->lm, h, L.ldd, M, lm, st);
   }
   SampleArgs sa;
   if (err == hipSuccess) {
@@ -318,6 +336,34 @@ spec_status spec_weights_destroy(spec_weights_t w) {
     free_weights(w);
     (void)hipSetDevice(prev);
   }
+  return SPEC_OK;
+}
+
+spec_status spec_profile_enable(spec_weights_t w, int32_t on) {
+  if (!w) return SPEC_EINVAL;
+  w->prof = on != 0;
+  w->ev_used = 0;
+  return SPEC_OK;
+}
+
+spec_status spec_profile_read(spec_weights_t w, double* gemm_ms, int64_t* launches,
+                              int64_t* weight_bytes) {
+  if (!w) return SPEC_EINVAL;
+  double ms = 0.0;
+  int64_t bytes = 0;
+  if (w->ev_used) {
+    if (hipEventSynchronize(w->ev[2 * w->ev_used - 1]) != hipSuccess) return SPEC_EHIP;
+    for (size_t i = 0; i < w->ev_used; ++i) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, w->ev[2 * i], w->ev[2 * i + 1]) != hipSuccess) return SPEC_EHIP;
+      ms += t;
+      bytes += w->ev_bytes[i];
+    }
+  }
+  if (gemm_ms) *gemm_ms = ms;
+  if (launches) *launches = (int64_t)w->ev_used;
+  if (weight_bytes) *weight_bytes = bytes;
+  w->ev_used = 0;
   return SPEC_OK;
 }
 

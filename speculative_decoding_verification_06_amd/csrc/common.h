@@ -11,7 +11,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 namespace sv {
 
 constexpr int kWave = 64;
-constexpr int kGroupCols = 64;     // output columns per GEMM work group / stats tile
+constexpr int kGroupCols = 64;     // columns of one packed weight block (4 MFMA tiles)
+constexpr int kSub = 16;           // columns of one MFMA tile = one statistics subtile
 constexpr int kKStep = 32;         // K rows per MFMA step (16x16x32)
 
 // ---- bfloat16 ------------------------------------------------------------
@@ -131,43 +132,64 @@ __device__ __forceinline__ uint32_t logit_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Per-tile statistics of one logits row tile (64 columns, one value per
-// lane): greedy -> (max, lowest argmax); otherwise (max, sum exp((l - max)/T))
-// for p, and for the matching draft row (i < gamma) the statistics of q':
-// T == 1 -> sum q; else (max y, sum exp(y - max y)) with y = log(q) / T.
-__device__ __forceinline__ void lm_tile_stats(float l, bool valid, int n, int grow, int g,
-                                              int G, int G1, int gamma, int V, int tmode,
-                                              float invT, const float* q, float* pst,
-                                              int* pidx, float* qst) {
-  const int lane = threadIdx.x & 63;
-  const size_t t = (size_t)grow * G + g;
+// ---- 16-lane group reductions (one MFMA column tile = 16 lanes) ----------
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ void argmax16(float& v, int& idx) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(idx, o, kWave);
+    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+  }
+}
+
+// Statistics of one 16-column logits subtile, one column per lane of a
+// 16-lane group (every lane of the wave must call): greedy -> (max, lowest
+// argmax); otherwise (max, sum exp((l - max)/T)) for p and, for draft rows
+// (i < gamma), the statistics of q': T == 1 -> sum q; else
+// (max y, sum exp(y - max y)) with y = log(q) / T.  `live` marks groups that
+// hold a real (row, subtile); lane 16k of a live group writes.
+__device__ __forceinline__ void lm_subtile_stats(float l, bool valid, bool live, int n, int grow,
+                                                 int tile, int G, int G1, int gamma, int V,
+                                                 int tmode, float invT, const float* q,
+                                                 float* pst, int* pidx, float* qst) {
+  const bool writer = live && (threadIdx.x & 15) == 0;
+  const size_t t = (size_t)grow * G + tile;
   if (tmode == 0) {
     float v = valid ? l : -INFINITY;
     int idx = valid ? n : 0x7fffffff;
-    wave_argmax(v, idx);
-    if (lane == 0) { pst[2 * t] = v; pst[2 * t + 1] = 0.f; pidx[t] = idx; }
+    argmax16(v, idx);
+    if (writer) { pst[2 * t] = v; pst[2 * t + 1] = 0.f; pidx[t] = idx; }
     return;
   }
-  const float mx = wave_max(valid ? l : -INFINITY);
-  const float se = wave_sum(valid ? expf((l - mx) * invT) : 0.f);
-  if (lane == 0) { pst[2 * t] = mx; pst[2 * t + 1] = se; }
+  const float mx = max16(valid ? l : -INFINITY);
+  const float se = sum16(valid ? expf((l - mx) * invT) : 0.f);
+  if (writer) { pst[2 * t] = mx; pst[2 * t + 1] = se; }
   const int b = grow / G1, i = grow - b * G1;
-  if (i < gamma) {
-    const size_t qrow = (size_t)b * gamma + i;
-    const float qv = valid ? q[qrow * V + n] : 0.f;
-    float ym = 0.f, sq;
-    if (tmode == 1) {
-      sq = wave_sum(qv);
-    } else {
-      const float y = qv > 0.f ? logf(qv) * invT : -INFINITY;
-      ym = wave_max(y);
-      sq = wave_sum(qv > 0.f ? expf(y - ym) : 0.f);
-    }
-    if (lane == 0) {
-      const size_t tq = qrow * G + g;
-      qst[2 * tq] = ym;
-      qst[2 * tq + 1] = sq;
-    }
+  const bool qrow_ok = live && i < gamma;
+  const size_t qrow = (size_t)b * gamma + i;
+  const float qv = (qrow_ok && valid) ? q[qrow * V + n] : 0.f;
+  float ym = 0.f, sq;
+  if (tmode == 1) {
+    sq = sum16(qv);
+  } else {
+    const float y = qv > 0.f ? logf(qv) * invT : -INFINITY;
+    ym = max16(y);
+    sq = sum16(qv > 0.f ? expf(y - ym) : 0.f);
+  }
+  if (writer && qrow_ok) {
+    const size_t tq = qrow * G + tile;
+    qst[2 * tq] = ym;
+    qst[2 * tq + 1] = sq;
   }
 }
 

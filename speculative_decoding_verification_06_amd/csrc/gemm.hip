@@ -1,4 +1,4 @@
-// Split-K skinny GEMMs of the target pass, with fused epilogues.
+// Skinny GEMMs of the target pass, with fused epilogues.
 //
 // Y[M][N] = X[M][K] @ W[K][N] for M = B * (gamma + 1) rows: the decode
 // mat-vec turned into a small mat-mat by scoring every drafted position in
@@ -9,123 +9,117 @@
 // weight byte is read from HBM once; activations stay fp32 (MFMA path:
 // split into bf16 hi/mid/lo terms) so the logits track a float64 reference.
 //
-// Work decomposition: work group = 4 waves on one column group of 64
-// columns and one k-range (split) of the weights.  When a column group has
-// S > 1 splits, every work group writes its partial tile, and the last one
-// to arrive (device-scope counter) sums the S partials in split order and
-// runs the epilogue, so results do not depend on arrival order.
+// Work decomposition: a work group owns NT MFMA column tiles (16 columns
+// each) over the whole K range.  Its waves are MG row groups x KG k-groups;
+// the k-groups take interleaved 32-row k-steps and are summed through LDS in
+// a fixed order, then the same work group runs the epilogue.  No work group
+// ever reads another's results: there are no partial buffers, counters or
+// device-scope fences (a device-scope release writes back the XCD's L2 and
+// costs far more than the weight stream at these sizes), and the sums are
+// bit-identical from run to run.
 
 #include "common.h"
 #include "internal.h"
 
-namespace sv {
+#ifndef SV_TARGET_WAVES
+#define SV_TARGET_WAVES 2048      // two waves per SIMD over 256 CUs
+#endif
+#ifndef SV_MIN_BLOCKS
+#define SV_MIN_BLOCKS 256         // work groups wanted per GEMM (one per CU)
+#endif
+#ifndef SV_PIPE_VGPRS
+#define SV_PIPE_VGPRS 192         // VGPRs of the load ring per wave
+#endif
 
-constexpr int kThreads = 256;
-constexpr int kResLd = kGroupCols + 1;   // padded LDS row of the result tile
+namespace sv {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
 // ---------------------------------------------------------------- epilogues
-// res: LDS tile [M][kResLd] holding the finished sums for this column group.
-template <int EPI>
-__device__ void run_epilogue(const EpiArgs& e, int M, int g, const float* res, float* sh_rowv) {
+// res: LDS tile [M][ldr] of finished sums for column tiles c0 .. c0+nt-1.
+// Items are (row, 16-column tile) pairs; a wave handles 4 items at a time,
+// one per 16-lane group, with one column per lane.
+__device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const float* res, int ldr,
+                             float* sh_inv, int nwaves) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = g * kGroupCols + lane;
-  const bool valid = n < e.N;
-  if constexpr (EPI == EPI_UP) {
-    for (int r = threadIdx.x; r < M; r += kThreads) {
+  const int q4 = lane >> 4, c = lane & 15;
+  if (e.kind == EPI_UP) {
+    for (int r = threadIdx.x; r < M; r += blockDim.x) {
       float s = 0.f;
       for (int t = 0; t < e.ss_n; ++t) s += e.ss_in[(size_t)r * e.ss_ld + t];
-      sh_rowv[r] = 1.0f / sqrtf(s * e.inv_d + e.eps);
+      sh_inv[r] = 1.0f / sqrtf(s * e.inv_d + e.eps);
     }
     __syncthreads();
-    for (int r = wave; r < M; r += 4) {
-      const float v = res[r * kResLd + lane];
-      e.out[(size_t)r * e.ldo + n] = valid ? silu(v * sh_rowv[r]) : 0.f;
-    }
-  } else if constexpr (EPI == EPI_DOWN) {
-    for (int r = wave; r < M; r += 4) {
+  }
+  const int items = M * nt;
+  for (int base = wave * 4; base < items; base += nwaves * 4) {
+    const int it = base + q4;
+    const bool live = it < items;
+    const int r = live ? it / nt : 0, t = live ? it - r * nt : 0;
+    const int tile = c0 + t;
+    const int n = tile * kSub + c;
+    const bool valid = live && n < e.N;
+    const float v = live ? res[r * ldr + t * kSub + c] : 0.f;
+    const size_t o = (size_t)r * e.ldo + n;
+    if (e.kind == EPI_UP) {
+      if (live) e.out[o] = valid ? silu(v * sh_inv[r]) : 0.f;
+    } else if (e.kind == EPI_DOWN) {
       float hn = 0.f;
-      if (valid) hn = e.out[(size_t)r * e.ldo + n] + res[r * kResLd + lane];
-      e.out[(size_t)r * e.ldo + n] = hn;
+      if (valid) hn = e.out[o] + v;
+      if (live) e.out[o] = hn;
       if (e.gain_next) {
-        e.xg[(size_t)r * e.ldo + n] = valid ? hn * e.gain_next[n] : 0.f;
-        const float sq = wave_sum(hn * hn);
-        if (lane == 0) e.ss_out[(size_t)r * e.ss_ld + g] = sq;
+        if (live) e.xg[o] = valid ? hn * e.gain_next[n] : 0.f;
+        const float sq = sum16(hn * hn);
+        if (live && c == 0) e.ss_out[(size_t)r * e.ss_ld + tile] = sq;
       }
-    }
-  } else {  // EPI_LM
-    for (int r = wave; r < M; r += 4) {
-      const float l = res[r * kResLd + lane];
-      if (valid) e.out[(size_t)r * e.ldo + n] = l;
-      lm_tile_stats(l, valid, n, e.row0 + r, g, e.G, e.G1, e.gamma, e.V, e.tmode, e.invT,
-                    e.q, e.pst, e.pidx, e.qst);
+    } else {
+      if (valid) e.out[o] = v;
+      // padding subtiles past ceil(V / 16) hold no statistics
+      lm_subtile_stats(v, valid, live && tile < e.G, n, e.row0 + r, tile, e.G, e.G1, e.gamma,
+                       e.V, e.tmode, e.invT, e.q, e.pst, e.pidx, e.qst);
     }
   }
-}
-
-// Publish this work group's tile; return true in the work group that must
-// finish the column group (then res holds the split-ordered total).
-__device__ bool splitk_finish(const GemmArgs& a, int g, int s, float* res, int* sh_flag) {
-  if (a.S == 1) return true;
-  const int M = a.M;
-  float* mine = a.part + ((size_t)s * M) * a.Np + (size_t)g * kGroupCols;
-  for (int idx = threadIdx.x; idx < M * kGroupCols; idx += kThreads) {
-    const int r = idx / kGroupCols, c = idx - r * kGroupCols;
-    mine[(size_t)r * a.Np + c] = res[r * kResLd + c];
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = atomicAdd(&a.cnt[g], 1);
-    const int last = (old == a.S - 1);
-    if (last) atomicExch(&a.cnt[g], 0);
-    *sh_flag = last;
-  }
-  __syncthreads();
-  if (!*sh_flag) return false;
-  __threadfence();
-  for (int idx = threadIdx.x; idx < M * kGroupCols; idx += kThreads) {
-    const int r = idx / kGroupCols, c = idx - r * kGroupCols;
-    const float* p = a.part + (size_t)r * a.Np + (size_t)g * kGroupCols + c;
-    float v = 0.f;
-    for (int s2 = 0; s2 < a.S; ++s2) v += p[(size_t)s2 * M * a.Np];
-    res[r * kResLd + c] = v;
-  }
-  __syncthreads();
-  return true;
-}
-
-template <int EPI>
-__device__ void finish(const GemmArgs& a, int g, int s, float* res, float* sh_rowv, int* sh_flag) {
-  if (!splitk_finish(a, g, s, res, sh_flag)) return;
-  run_epilogue<EPI>(a.e, a.M, g, res, sh_rowv);
 }
 
 // ---------------------------------------------------------------- MFMA GEMM
-// bf16 weights in MFMA tiles.  MTW = 16-row M tiles per wave.
-//   MSPLIT = false: the 4 waves take interleaved k-steps of the same rows
-//                   (rows <= 16 * MTW) and are summed in LDS.
-//   MSPLIT = true : the 4 waves share every k-step (the B tile is read once
-//                   from HBM and served to the others from cache) and each
-//                   owns MTW M tiles.
-template <int MTW, bool MSPLIT, int NSPLIT, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemm_mfma(GemmArgs a) {
-  extern __shared__ float smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = blockIdx.x / a.S, s = blockIdx.x - g * a.S;
-  const int ks0 = s * a.kps, ks1 = min(a.KS, ks0 + a.kps);
-  const int M = a.M;
-  const int mt0 = MSPLIT ? wave * MTW : 0;
-  const bf16x8* Wg = reinterpret_cast<const bf16x8*>(a.W) + (size_t)g * a.KS * 256 + lane;
+// bf16 weights in MFMA tiles (layout in internal.h).  MTW = 16-row M tiles
+// per wave, MG row groups, NT column tiles per work group; the number of
+// k-groups KG = waves / MG is a launch parameter.
+// The weight stream is latency bound unless each CU keeps about 170 KiB of
+// loads in flight (8 TB/s over 256 CUs at ~5 us loaded latency), so waves run
+// two per SIMD and hold deep register pipelines: a k-step stage costs
+// 4 * NT VGPRs of weights and 8 * MTW of activations, and PIPE stages stay
+// within a 256-VGPR budget (~190 for the ring).
+template <int MTW, int NT>
+struct MfmaPipe {
+  static constexpr int stage = 4 * NT + 8 * MTW;
+  static constexpr int value = MTW >= 3 ? 2 : (SV_PIPE_VGPRS / stage < 2 ? 2 : SV_PIPE_VGPRS / stage);
+};
 
-  f32x4 acc[MTW][4];
+template <int MTW, int MG, int NT, int NSPLIT>
+__global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
+  constexpr int PIPE = MfmaPipe<MTW, NT>::value;
+  extern __shared__ float smem[];
+  __shared__ float sh_inv[256];
+  const int lane = threadIdx.x & 63;
+  const int nwaves = blockDim.x >> 6;
+  // wave index as a scalar, so the k-loop branches stay uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mg = wave % MG, kg = wave / MG, KG = nwaves / MG;
+  const int c0 = blockIdx.x * NT;                 // first 16-column tile
+  const int M = a.M, KS = a.KS;
+  const int mt0 = mg * MTW;
+  // this work group's column block: one contiguous span of KS * NT KiB
+  const bf16x8* Wg = reinterpret_cast<const bf16x8*>(a.W) + (size_t)blockIdx.x * KS * NT * 64 + lane;
+
+  f32x4 acc[MTW][NT];
 #pragma unroll
   for (int i = 0; i < MTW; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // rows this lane feeds as the A operand, and whether any is live
+  // rows this lane feeds as the A operand; rows past M read row M-1 (a
+  // cached line) and are zeroed before the split, so no load is divergent
   const int arow = lane & 15, akoff = (lane >> 4) * 8;
   const float* xrow[MTW];
   bool xlive[MTW];
@@ -133,109 +127,105 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mfma(GemmArgs a) {
   for (int i = 0; i < MTW; ++i) {
     const int row = (mt0 + i) * 16 + arow;
     xlive[i] = row < M;
-    xrow[i] = a.X + (size_t)(xlive[i] ? row : 0) * a.ldx + akoff;
+    xrow[i] = a.X + (size_t)min(row, M - 1) * a.ldx + akoff;
   }
   const bool wave_live = (mt0 * 16) < M;
 
-  const int kstep = MSPLIT ? 1 : 4;
-  int k = MSPLIT ? ks0 : ks0 + wave;
+  bf16x8 bq[PIPE][NT];
+  float4 xq[PIPE][MTW][2];
 
-  bf16x8 bA[4], bB[4];
-  float4 xA[MTW][2], xB[MTW][2];
-
-#define SV_LOAD(bv, xv, kk)                                                      \
+#define SV_LOAD(u, kk)                                                           \
   {                                                                              \
-    const bf16x8* wp = Wg + (size_t)(kk) * 256;                                  \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) bv[t] = wp[t * 64];            \
+    const bf16x8* wp = Wg + (size_t)(kk) * NT * 64;                              \
+    _Pragma("unroll") for (int t = 0; t < NT; ++t) bq[u][t] = wp[t * 64];        \
     _Pragma("unroll") for (int i = 0; i < MTW; ++i) {                            \
-      if (xlive[i]) {                                                            \
-        const float4* xp = reinterpret_cast<const float4*>(xrow[i] + (kk) * kKStep); \
-        xv[i][0] = xp[0];                                                        \
-        xv[i][1] = xp[1];                                                        \
-      } else {                                                                   \
-        xv[i][0] = make_float4(0.f, 0.f, 0.f, 0.f);                              \
-        xv[i][1] = xv[i][0];                                                     \
-      }                                                                          \
+      const float4* xp = reinterpret_cast<const float4*>(xrow[i] + (kk) * kKStep); \
+      xq[u][i][0] = xp[0];                                                       \
+      xq[u][i][1] = xp[1];                                                       \
     }                                                                            \
   }
 
-#define SV_COMPUTE(bv, xv)                                                       \
+#define SV_COMPUTE(u, on)                                                        \
   {                                                                              \
     _Pragma("unroll") for (int i = 0; i < MTW; ++i) {                            \
       if ((mt0 + i) * 16 < M) {                                                  \
-        const float xs[8] = {xv[i][0].x, xv[i][0].y, xv[i][0].z, xv[i][0].w,      \
-                             xv[i][1].x, xv[i][1].y, xv[i][1].z, xv[i][1].w};     \
+        const float z = (xlive[i] && (on)) ? 1.0f : 0.0f;                        \
+        const float xs[8] = {xq[u][i][0].x * z, xq[u][i][0].y * z, xq[u][i][0].z * z, \
+                             xq[u][i][0].w * z, xq[u][i][1].x * z, xq[u][i][1].y * z, \
+                             xq[u][i][1].z * z, xq[u][i][1].w * z};               \
         bf16x8 av[NSPLIT];                                                       \
         split_bf16x8<NSPLIT>(xs, av);                                            \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t) {                          \
+        _Pragma("unroll") for (int t = 0; t < NT; ++t) {                         \
           _Pragma("unroll") for (int p = 0; p < NSPLIT; ++p)                     \
-            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[p], bv[t],     \
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[p], bq[u][t],  \
                                                                 acc[i][t], 0, 0, 0); \
         }                                                                        \
       }                                                                          \
     }                                                                            \
   }
 
-  if (wave_live) {
-    if (k < ks1) SV_LOAD(bA, xA, k);
-    while (k < ks1) {
-      const int k2 = k + kstep;
-      if (k2 < ks1) SV_LOAD(bB, xB, k2);
-      SV_COMPUTE(bA, xA);
-      k = k2;
-      if (k >= ks1) break;
-      const int k3 = k + kstep;
-      if (k3 < ks1) SV_LOAD(bA, xA, k3);
-      SV_COMPUTE(bB, xB);
-      k = k3;
+  // Software pipeline over a ring of PIPE k-steps: each stage is computed,
+  // then refilled with the k-step PIPE positions ahead, so PIPE - 1 k-steps
+  // of loads stay in flight while one is consumed.  The loop body has no
+  // branches: refills past the wave's last k-step reload that k-step (a
+  // cache hit) and stages past the end compute with a zero A operand, so
+  // every path issues the same loads and each wait covers only the oldest
+  // stage.  sched_barrier keeps the issue order of the stages.
+  int k = kg;
+  if (wave_live && k < KS) {
+    const int n = (KS - k + KG - 1) / KG;            // k-steps of this wave
+    const int klast = k + (n - 1) * KG;
+#pragma unroll
+    for (int u = 0; u < PIPE; ++u) {
+      SV_LOAD(u, min(k + u * KG, klast));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int it = 0; it < n; it += PIPE) {
+#pragma unroll
+      for (int u = 0; u < PIPE; ++u) {
+        SV_COMPUTE(u, it + u < n);
+        SV_LOAD(u, min(k + (it + u + PIPE) * KG, klast));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 #undef SV_LOAD
 #undef SV_COMPUTE
 
-  // C layout of 16x16 MFMA: lane holds rows 4*(lane/16)+j, column lane%16.
-  // LDS: MSPLIT -> res [M][kResLd]; k-split -> red [4][16*MTW][kResLd], res [M][kResLd]
-  constexpr int R = MTW * 16;
-  float* res = MSPLIT ? smem : smem + 4 * R * kResLd;
+  // k-group partial tiles into LDS red[KG][M][ldr], then summed in k-group
+  // order into red[0].  C layout of 16x16 MFMA: lane holds rows
+  // 4*(lane/16)+j of column lane%16.
+  constexpr int NCOL = NT * kSub;
+  constexpr int ldr = NCOL + 1;
+  float* red = smem;
   const int crow = 4 * (lane >> 4), ccol = lane & 15;
-  if constexpr (MSPLIT) {
 #pragma unroll
-    for (int i = 0; i < MTW; ++i)
+  for (int i = 0; i < MTW; ++i)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = (mt0 + i) * 16 + crow + j;
-          if (row < M) res[row * kResLd + t * 16 + ccol] = acc[i][t][j];
-        }
-  } else {
-    float* red = smem;                 // [4 waves][R][kResLd]
-#pragma unroll
-    for (int i = 0; i < MTW; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          red[(wave * R + i * 16 + crow + j) * kResLd + t * 16 + ccol] = acc[i][t][j];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < M * kGroupCols; idx += kThreads) {
-      const int r = idx / kGroupCols, c = idx - r * kGroupCols;
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) v += red[(w * R + r) * kResLd + c];
-      res[r * kResLd + c] = v;
-    }
-  }
+      for (int j = 0; j < 4; ++j) {
+        const int row = (mt0 + i) * 16 + crow + j;
+        if (row < M) red[((size_t)kg * M + row) * ldr + t * kSub + ccol] = acc[i][t][j];
+      }
   __syncthreads();
-  __shared__ float sh_rowv[256];
-  __shared__ int sh_flag;
-  finish<EPI>(a, g, s, res, sh_rowv, &sh_flag);
+  if (KG > 1) {
+    for (int idx = threadIdx.x; idx < M * NCOL; idx += blockDim.x) {
+      const int r = idx / NCOL, col = idx - r * NCOL;
+      float v = 0.f;
+      for (int q = 0; q < KG; ++q) v += red[((size_t)q * M + r) * ldr + col];
+      red[r * ldr + col] = v;
+    }
+    __syncthreads();
+  }
+  run_epilogue(a.e, M, c0, NT, red, ldr, sh_inv, nwaves);
 }
 
 // ---------------------------------------------------------------- vector-FMA GEMM
-// Row-major weights (fp32 or bf16).  Lane = (row r = lane / 8 of an 8-row
-// step, 8 columns at 8 * (lane % 8)); the 4 waves take interleaved 8-row
-// steps of the split's k-range; rows of X are processed 8 at a time.
+// Row-major weights (fp32 or bf16), 4 waves, 4 column tiles (64 columns) per
+// work group.  Lane = (row r = lane / 8 of an 8-row step, 8 columns at
+// 8 * (lane % 8)); the waves take interleaved 8-row steps of K; rows of X
+// are processed 8 at a time.
 template <typename WT>
 __device__ __forceinline__ void load_w8(const WT* p, float (&w)[8]);
 template <>
@@ -252,17 +242,21 @@ __device__ __forceinline__ void load_w8<uint16_t>(const uint16_t* p, float (&w)[
   w[4] = bf16_lo(a.z); w[5] = bf16_hi(a.z); w[6] = bf16_lo(a.w); w[7] = bf16_hi(a.w);
 }
 
-template <typename WT, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemm_fma(GemmArgs a) {
+constexpr int kFmaThreads = 256;
+
+template <typename WT>
+__global__ __launch_bounds__(kFmaThreads) void k_gemm_fma(GemmArgs a) {
   extern __shared__ float smem[];
+  __shared__ float sh_inv[256];
+  constexpr int ldr = kGroupCols + 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = blockIdx.x / a.S, s = blockIdx.x - g * a.S;
-  const int r0 = s * a.kps * kKStep, r1 = min(a.KS, (s + 1) * a.kps) * kKStep;
+  const int g = blockIdx.x;                        // 64-column block
+  const int Kp = a.KS * kKStep;
   const int M = a.M;
   const int rr = lane >> 3, cg = (lane & 7) * 8;
   const WT* W = reinterpret_cast<const WT*>(a.W) + (size_t)g * kGroupCols + cg;
-  float* res = smem;                       // [M][kResLd]
-  float* red = smem + M * kResLd;          // [4][8][kResLd]
+  float* res = smem;                       // [M][ldr]
+  float* red = smem + M * ldr;             // [4][8][ldr]
 
   for (int m0 = 0; m0 < M; m0 += 8) {
     const int mr = min(8, M - m0);
@@ -271,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fma(GemmArgs a) {
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[m][j] = 0.f;
-    for (int k = r0 + wave * 8 + rr; k < r1; k += 32) {
+    for (int k = wave * 8 + rr; k < Kp; k += 32) {
       float w[8];
       load_w8<WT>(W + (size_t)k * a.Np, w);
 #pragma unroll
@@ -298,91 +292,89 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fma(GemmArgs a) {
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) red[(wave * 8 + m) * kResLd + cg + j] = acc[m][j];
+        for (int j = 0; j < 8; ++j) red[(wave * 8 + m) * ldr + cg + j] = acc[m][j];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < mr * kGroupCols; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < mr * kGroupCols; idx += kFmaThreads) {
       const int m = idx / kGroupCols, c = idx - m * kGroupCols;
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v += red[(w * 8 + m) * kResLd + c];
-      res[(m0 + m) * kResLd + c] = v;
+      for (int w = 0; w < 4; ++w) v += red[(w * 8 + m) * ldr + c];
+      res[(m0 + m) * ldr + c] = v;
     }
     __syncthreads();
   }
-  __shared__ float sh_rowv[256];
-  __shared__ int sh_flag;
-  finish<EPI>(a, g, s, res, sh_rowv, &sh_flag);
+  run_epilogue(a.e, M, g * 4, 4, res, ldr, sh_inv, kFmaThreads / kWave);
 }
 
 // ---------------------------------------------------------------- host side
-static int mfma_tiles_per_wave(int M) {
-  const int mt = (M + 15) / 16;
-  if (mt <= 2) return mt;            // k-split inside the work group
-  return (mt + 3) / 4;               // rows split over the 4 waves
+
+int mfma_block_tiles(int Np) {
+  const int tiles = Np / kSub;
+  int nt = 4;
+  while (nt > 1 && tiles / nt < SV_MIN_BLOCKS) nt /= 2;
+  return nt;
 }
 
-void choose_split(int path, int M, int KS, int G, int& S, int& kps) {
-  // Aim for about four work groups per CU over 256 CUs and keep at least
-  // two k-steps per wave.
-  const int target = 1024;
-  const bool msplit = path == PATH_MFMA && (M + 15) / 16 > 2;
-  const int min_kps = msplit ? 2 : 8;
-  int s = (target + G - 1) / G;
-  s = std::min(s, std::max(1, KS / min_kps));
-  // partial tiles S*M*Np*4 bytes kept within 1/8 of the weight bytes Kp*Np*2
-  const int cap = std::max(1, (2 * KS) / std::max(M, 1));
-  s = std::max(1, std::min(s, cap));
-  kps = (KS + s - 1) / s;
-  S = (KS + kps - 1) / kps;
+GemmPlan plan_gemm(int path, int M, const Mat& m) {
+  GemmPlan p;
+  p.path = path;
+  const int tiles = m.Np / kSub;
+  const int KS = m.Kp / kKStep;
+  if (path != PATH_MFMA) {
+    p.nt = 4; p.mg = 1; p.mtw = 1; p.kg = 4;
+    p.blocks = m.Np / kGroupCols;
+    p.lds = ((size_t)M * (kGroupCols + 1) + 4 * 8 * (kGroupCols + 1)) * sizeof(float);
+    return p;
+  }
+  const int MT = (M + 15) / 16;
+  if (MT <= 2) { p.mtw = MT; p.mg = 1; }
+  else if (MT <= 4) { p.mtw = 2; p.mg = 2; }
+  else if (MT <= 6) { p.mtw = 3; p.mg = 2; }
+  else if (MT <= 8) { p.mtw = 4; p.mg = 2; }
+  else if (MT <= 12) { p.mtw = 3; p.mg = 4; }
+  else { p.mtw = 4; p.mg = 4; }
+  p.nt = m.nt;
+  p.blocks = tiles / p.nt;
+  // k-groups: about SV_TARGET_WAVES waves in all, within the work-group
+  // size, the k-steps and 64 KiB of LDS for the k-group tiles
+  const int max_waves = 8;
+  auto lds_of = [&](int kg) { return (size_t)kg * M * (p.nt * kSub + 1) * sizeof(float); };
+  p.kg = 1;
+  while (p.mg * p.kg * 2 <= max_waves && (size_t)p.blocks * p.mg * p.kg * 2 <= SV_TARGET_WAVES &&
+         p.kg * 2 <= KS && lds_of(p.kg * 2) <= 65536)
+    p.kg *= 2;
+  p.lds = lds_of(p.kg);
+  return p;
 }
 
-size_t gemm_part_floats(int path, int M, const Mat& m) {
-  int S, kps;
-  choose_split(path, M, m.Kp / kKStep, m.Np / kGroupCols, S, kps);
-  return S > 1 ? (size_t)S * M * m.Np : 0;
-}
-
-template <int MTW, bool MSPLIT, int NSPLIT>
-static hipError_t launch_mfma_t(int epi, const GemmArgs& a, hipStream_t st) {
-  size_t lds = (size_t)a.M * kResLd * sizeof(float);
-  if (!MSPLIT) lds += (size_t)4 * MTW * 16 * kResLd * sizeof(float);
-  const dim3 grid(a.G * a.S), block(kThreads);
-  switch (epi) {
-    case EPI_UP: hipLaunchKernelGGL((k_gemm_mfma<MTW, MSPLIT, NSPLIT, EPI_UP>), grid, block, lds, st, a); break;
-    case EPI_DOWN: hipLaunchKernelGGL((k_gemm_mfma<MTW, MSPLIT, NSPLIT, EPI_DOWN>), grid, block, lds, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm_mfma<MTW, MSPLIT, NSPLIT, EPI_LM>), grid, block, lds, st, a); break;
+template <int MTW, int MG>
+static hipError_t launch_mfma_mg(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  const dim3 grid(p.blocks), block(64 * p.mg * p.kg);
+  switch (p.nt) {
+    case 1: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 1, 3>), grid, block, p.lds, st, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 2, 3>), grid, block, p.lds, st, a); break;
+    default: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 4, 3>), grid, block, p.lds, st, a); break;
   }
   return hipGetLastError();
 }
 
-template <typename WT>
-static hipError_t launch_fma_t(int epi, const GemmArgs& a, hipStream_t st) {
-  const size_t lds = ((size_t)a.M * kResLd + 4 * 8 * kResLd) * sizeof(float);
-  const dim3 grid(a.G * a.S), block(kThreads);
-  switch (epi) {
-    case EPI_UP: hipLaunchKernelGGL((k_gemm_fma<WT, EPI_UP>), grid, block, lds, st, a); break;
-    case EPI_DOWN: hipLaunchKernelGGL((k_gemm_fma<WT, EPI_DOWN>), grid, block, lds, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm_fma<WT, EPI_LM>), grid, block, lds, st, a); break;
+hipError_t launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+  if (p.path == PATH_FMA_F32 || p.path == PATH_FMA_BF16) {
+    const dim3 grid(p.blocks), block(kFmaThreads);
+    if (p.path == PATH_FMA_F32)
+      hipLaunchKernelGGL((k_gemm_fma<float>), grid, block, p.lds, st, a);
+    else
+      hipLaunchKernelGGL((k_gemm_fma<uint16_t>), grid, block, p.lds, st, a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm(int path, int epi, const GemmArgs& a, hipStream_t st) {
-  if (path == PATH_FMA_F32) return launch_fma_t<float>(epi, a, st);
-  if (path == PATH_FMA_BF16) return launch_fma_t<uint16_t>(epi, a, st);
-  const int mtw = mfma_tiles_per_wave(a.M);
-  const bool msplit = (a.M + 15) / 16 > 2;
-  if (!msplit) {
-    if (mtw == 1) return launch_mfma_t<1, false, 3>(epi, a, st);
-    return launch_mfma_t<2, false, 3>(epi, a, st);
+  if (p.mg == 1) return p.mtw == 1 ? launch_mfma_mg<1, 1>(p, a, st) : launch_mfma_mg<2, 1>(p, a, st);
+  if (p.mg == 2) {
+    if (p.mtw == 2) return launch_mfma_mg<2, 2>(p, a, st);
+    if (p.mtw == 3) return launch_mfma_mg<3, 2>(p, a, st);
+    return launch_mfma_mg<4, 2>(p, a, st);
   }
-  switch (mtw) {
-    case 1: return launch_mfma_t<1, true, 3>(epi, a, st);
-    case 2: return launch_mfma_t<2, true, 3>(epi, a, st);
-    case 3: return launch_mfma_t<3, true, 3>(epi, a, st);
-    default: return launch_mfma_t<4, true, 3>(epi, a, st);
-  }
+  return p.mtw == 3 ? launch_mfma_mg<3, 4>(p, a, st) : launch_mfma_mg<4, 4>(p, a, st);
 }
 
 }  // namespace sv

@@ -12,16 +12,18 @@ __device__ __forceinline__ uint32_t load_bits16(const void* src, int dtype, size
 }
 
 // One thread per 16-byte MFMA chunk (see Mat in internal.h for the layout).
-__global__ void k_pack_mfma(const void* src, int dtype, int K, int N, uint4* dst, int KS, size_t total) {
+__global__ void k_pack_mfma(const void* src, int dtype, int K, int N, uint4* dst, int KS, int nt,
+                            size_t total) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
   const int lane = (int)(idx & 63);
-  const int t = (int)((idx >> 6) & 3);
-  const size_t gs = idx >> 8;
-  const int s = (int)(gs % KS);
-  const int g = (int)(gs / KS);
+  const size_t rest = idx >> 6;
+  const int t = (int)(rest % nt);
+  const size_t bs = rest / nt;
+  const int s = (int)(bs % KS);
+  const int b = (int)(bs / KS);
   const int k0 = s * kKStep + 8 * (lane >> 4);
-  const int n = g * kGroupCols + 16 * t + (lane & 15);
+  const int n = (b * nt + t) * kSub + (lane & 15);
   uint32_t h[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -53,12 +55,12 @@ __global__ void k_vec_to_f32(const void* src, int dtype, int n, float* dst) {
 }
 
 hipError_t launch_pack_mfma(const void* src, int src_dtype, int K, int N, void* dst, int Kp,
-                            int Np, hipStream_t st) {
+                            int Np, int nt, hipStream_t st) {
   const int KS = Kp / kKStep;
-  const size_t total = (size_t)(Np / kGroupCols) * KS * 256;
+  const size_t total = (size_t)(Np / kSub) * KS * 64;
   const unsigned blocks = (unsigned)((total + 255) / 256);
   hipLaunchKernelGGL(k_pack_mfma, dim3(blocks), dim3(256), 0, st, src, src_dtype, K, N,
-                     reinterpret_cast<uint4*>(dst), KS, total);
+                     reinterpret_cast<uint4*>(dst), KS, nt, total);
   return hipGetLastError();
 }
 

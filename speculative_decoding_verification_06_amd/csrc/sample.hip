@@ -58,65 +58,73 @@ __device__ __forceinline__ float q_prime(const float* ri, float qv, int v, int t
 }
 
 // ---------------------------------------------------------------- prep
-// h = hidden (zero-padded rows of ld), xg = h * gain0, per-64-column sums of
-// squares of h, and the split-K counters cleared.
+// h = hidden (zero-padded rows of ld), xg = h * gain0, and the sum of
+// squares of h per 16-column subtile.
 __global__ void k_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
-                       const float* gain0, int d, int ld, int* cnt, int ncnt) {
+                       const float* gain0, int d, int ld) {
   const int lane = threadIdx.x, g = blockIdx.x, m = blockIdx.y;
   const int n = g * kGroupCols + lane;
   const float v = n < d ? hidden[(size_t)m * d + n] : 0.f;
   h[(size_t)m * ld + n] = v;
   if (gain0) {
     xg[(size_t)m * ld + n] = n < d ? v * gain0[n] : 0.f;
-    const float sq = wave_sum(v * v);
-    if (lane == 0) ss[(size_t)m * ss_ld + g] = sq;
+    const float sq = sum16(v * v);
+    if ((lane & 15) == 0) ss[(size_t)m * ss_ld + g * 4 + (lane >> 4)] = sq;
   }
-  if (m == 0)
-    for (int i = g * kWave + lane; i < ncnt; i += gridDim.x * kWave) cnt[i] = 0;
 }
 
 hipError_t launch_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
-                       const float* gain0, int M, int d, int ld, int* cnt, int ncnt,
-                       hipStream_t st) {
+                       const float* gain0, int M, int d, int ld, hipStream_t st) {
   hipLaunchKernelGGL(k_prep, dim3(ld / kGroupCols, M), dim3(kWave), 0, st, h, xg, ss, ss_ld,
-                     hidden, gain0, d, ld, cnt, ncnt);
+                     hidden, gain0, d, ld);
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- tile stats from given logits
+// ---------------------------------------------------------------- subtile stats from given logits
 __global__ void k_tile_stats(SampleArgs a) {
-  const int g = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
-  const int n = g * kGroupCols + lane;
-  const bool valid = n < a.V;
+  const int r = blockIdx.y, lane = threadIdx.x;
+  const int tile = blockIdx.x * 4 + (lane >> 4);
+  const int n = tile * kSub + (lane & 15);
+  const bool live = tile < a.G;
+  const bool valid = live && n < a.V;
   const float l = valid ? a.logits[(size_t)r * a.ldl + n] : 0.f;
-  lm_tile_stats(l, valid, n, r, g, a.G, a.gamma + 1, a.gamma, a.V, a.tmode, a.invT, a.q,
-                a.pst, a.pidx, a.qst);
+  lm_subtile_stats(l, valid, live, n, r, tile, a.G, a.gamma + 1, a.gamma, a.V, a.tmode, a.invT,
+                   a.q, a.pst, a.pidx, a.qst);
 }
 
 hipError_t launch_tile_stats(const SampleArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_tile_stats, dim3(a.G, a.M), dim3(kWave), 0, st, a);
+  hipLaunchKernelGGL(k_tile_stats, dim3((a.G + 3) / 4, a.M), dim3(kWave), 0, st, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- row stats
-__global__ void k_rowstats(SampleArgs a) {
-  const int row = blockIdx.x, lane = threadIdx.x;
+constexpr int kRowThreads = 256;
+
+__global__ __launch_bounds__(kRowThreads) void k_rowstats(SampleArgs a) {
+  __shared__ float sh_m[kRowThreads / kWave], sh_s[kRowThreads / kWave];
+  const int row = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool isq = row >= a.M;
   const float* st = isq ? a.qst + (size_t)(row - a.M) * a.G * 2 : a.pst + (size_t)row * a.G * 2;
-  float m = 0.f, s = 0.f;
-  if (isq && a.tmode == 1) {
-    for (int t = lane; t < a.G; t += kWave) s += st[2 * t + 1];
-    s = wave_sum(s);
-  } else {
-    const float it = isq ? 1.f : a.invT;
-    m = -INFINITY;
-    for (int t = lane; t < a.G; t += kWave) lse_merge(m, s, st[2 * t], st[2 * t + 1], it);
-    wave_lse(m, s, it);
+  const bool plain_sum = isq && a.tmode == 1;
+  const float it = isq ? 1.f : a.invT;
+  float m = plain_sum ? 0.f : -INFINITY, s = 0.f;
+  for (int t = threadIdx.x; t < a.G; t += kRowThreads) {
+    if (plain_sum) s += st[2 * t + 1];
+    else lse_merge(m, s, st[2 * t], st[2 * t + 1], it);
   }
-  if (lane == 0) {
+  if (plain_sum) s = wave_sum(s);
+  else wave_lse(m, s, it);
+  if (lane == 0) { sh_m[wave] = m; sh_s[wave] = s; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mm = sh_m[0], ss = sh_s[0];
+    for (int w = 1; w < kRowThreads / kWave; ++w) {
+      if (plain_sum) ss += sh_s[w];
+      else lse_merge(mm, ss, sh_m[w], sh_s[w], it);
+    }
     float* ri = a.rowinfo + (size_t)row * kRowInfo;
-    ri[RI_M] = m;
-    ri[RI_INVZ] = 1.0f / s;
+    ri[RI_M] = mm;
+    ri[RI_INVZ] = 1.0f / ss;
     ri[RI_THR] = 0.f;
     ri[RI_TIE] = 0.f;
     ri[RI_INVZN] = 1.0f;
@@ -320,7 +328,7 @@ __global__ void k_decide(SampleArgs a) {
 // the sampled token is not moved by summation error even when single
 // tokens carry 1e-6 of the mass.
 constexpr int kResThreads = 256;
-constexpr int kResPer = kResampleChunk / kResThreads;   // 16 contiguous ids per thread
+constexpr int kResPer = kResampleChunk / kResThreads;   // contiguous ids per thread
 
 // Exclusive prefix over the block in thread order (wave scan, then waves in order).
 __device__ double block_excl_scan_f64(double x, double* lds_waves) {
@@ -401,15 +409,22 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const int j = a.dec[4 * b];
   if (j < 0) return;
+  // chunk sums into LDS in parallel ([0, nch) residual, [nch, 2 nch) p'),
+  // then one thread forms the running prefix in chunk order
+  const double* cs = a.csum + 2 * (size_t)b * a.nch;
+  for (int c = tid; c < a.nch; c += kResThreads) {
+    sh_C[c] = cs[2 * c];
+    sh_C[a.nch + c] = cs[2 * c + 1];
+  }
+  __syncthreads();
   if (tid == 0) {
-    const double* cs = a.csum + 2 * (size_t)b * a.nch;
     double C = 0.0;
-    for (int c = 0; c < a.nch; ++c) { C = C + cs[2 * c]; sh_C[c] = C; }
+    for (int c = 0; c < a.nch; ++c) { C = C + sh_C[c]; sh_C[c] = C; }
     int usep = 0;
     if (!(C > 0.0)) {
       usep = 1;
       C = 0.0;
-      for (int c = 0; c < a.nch; ++c) { C = C + cs[2 * c + 1]; sh_C[c] = C; }
+      for (int c = 0; c < a.nch; ++c) { C = C + sh_C[a.nch + c]; sh_C[c] = C; }
     }
     float r, u;
     row_uniforms(a.seed, b, j, r, u);
@@ -479,14 +494,14 @@ hipError_t launch_dump_probs(const SampleArgs& a, hipStream_t st) {
 hipError_t launch_sampling(const SampleArgs& a, hipStream_t st) {
   const int qrows = a.B * a.gamma;
   if (a.tmode != 0) {
-    hipLaunchKernelGGL(k_rowstats, dim3(a.M + qrows), dim3(kWave), 0, st, a);
+    hipLaunchKernelGGL(k_rowstats, dim3(a.M + qrows), dim3(kRowThreads), 0, st, a);
     if (a.top_p < 1.0f)
       hipLaunchKernelGGL(k_topp, dim3(a.M + qrows), dim3(kToppThreads), 0, st, a);
   }
   hipLaunchKernelGGL(k_decide, dim3(a.B), dim3(256), (a.gamma + 1) * sizeof(int), st, a);
   if (a.tmode != 0) {
     hipLaunchKernelGGL(k_res_chunks, dim3(a.nch, a.B), dim3(kResThreads), 0, st, a);
-    hipLaunchKernelGGL(k_res_select, dim3(a.B), dim3(kResThreads), a.nch * sizeof(double), st, a);
+    hipLaunchKernelGGL(k_res_select, dim3(a.B), dim3(kResThreads), 2 * a.nch * sizeof(double), st, a);
   }
   return hipGetLastError();
 }
