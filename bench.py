@@ -95,6 +95,8 @@ def build_inputs(torch, sv, synth, wl, w, key):
     logits = []
     for h in hid:
         _, _, lg, _, _ = sv.verify_debug(w, h, zero_d, flat_q, 1.0, 1.0, 0, want_probs=False)
+        if not bool(torch.isfinite(lg).all()):
+            raise RuntimeError("target logits are not finite: the GEMM path is broken")
         logits.append(lg)
     z = [synth.normal_torch((*key, synth.T_NOISE, i), (B, gamma, V), 1.0, "cuda") for i in range(POOL)]
     Tq = T if T > 0 else 1.0
@@ -200,6 +202,10 @@ def main():
         copy_probe(args.copy_probe)
         return
 
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    progress("importing torch")
     import torch
     import synth
     import speculative_decoding_verification_06_amd as sv
@@ -210,6 +216,7 @@ def main():
     t_setup = time.perf_counter()
     model = synth.model_torch(key, wl.d, wl.ffn, wl.n_blocks, wl.V, wl.wdtype, "cuda")
     w = sv.Weights(model["blocks"], model["lm_head"])
+    progress(f"weights registered {time.perf_counter() - t_setup:.1f}s")
     host = None
     if not args.no_cpu_baseline:
         f64 = lambda t: t.detach().to("cpu").to(torch.float64).numpy()
@@ -232,6 +239,7 @@ def main():
         sv.verify(w, hid[k % POOL], drafts[k % POOL], qarg[k % POOL], T, top_p, 10 ** 6 + k,
                   workspace=ws, n_accepted=n_out[k % K], emitted=e_out[k % K])
     torch.cuda.synchronize()
+    progress("warmup done")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for k in range(K):
@@ -240,6 +248,7 @@ def main():
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
+    progress(f"timed {K} steps: {ms / K:.4f} ms/step")
     n_acc = n_out.cpu()
     tokens = int((n_acc + 1).sum())
     passes_s = K / (ms / 1e3)
@@ -253,6 +262,7 @@ def main():
                   workspace=ws, n_accepted=n_out[k], emitted=e_out[k])
     gemm_ms, launches, wbytes = w.profile_read()
     w.profile(False)
+    progress("kernel timing done")
     per_launch_bytes = wbytes / launches
     per_launch_s = gemm_ms / 1e3 / launches
     achieved = per_launch_bytes / per_launch_s / 1e9
@@ -278,7 +288,7 @@ def main():
         "algorithmic_bytes_per_step": weight_bytes + other,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "split-K GEMMs (MLP up/down, LM head)",
+                     "kernel": "weight-streaming GEMMs (MLP up/down, LM head)",
                      "bytes_per_launch": per_launch_bytes, "launches": launches,
                      "avg_launch_us": per_launch_s * 1e6},
         "cpu_baseline": None,

@@ -39,9 +39,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int M = 0, ldd = 0, ldf = 0, Vs = 0, G = 0, nch = 0;
+  int ksd = 0, ksf = 0;       // k-steps of the d- and ffn-wide split inputs
   size_t h = 0, xg = 0, ss = 0, act = 0, logits = 0, pst = 0, pidx = 0, qst = 0, rowinfo = 0,
-         dec = 0, csum = 0, total = 0;
+         dec = 0, csum = 0, xsd = 0, xsf = 0, total = 0;
 };
+
+// Bytes of one split-activation buffer: ceil(M / 16) row tiles of KS + 1
+// k-steps of three 1 KiB fragments.
+size_t xs_bytes(int M, int ks) { return (size_t)((M + 15) / 16) * (ks + 1) * 3 * 1024; }
 
 int gemm_path(const spec_weights* w, int M) {
   if (w->wdtype == SPEC_F32) return PATH_FMA_F32;
@@ -77,6 +82,12 @@ Layout make_layout(const spec_weights* w, int B, int gamma) {
   L.ss = off; off = align256(off + sizeof(float) * M * (L.ldd / kSub));
   L.act = off; off = align256(off + sizeof(float) * M * L.ldf);
   L.logits = off; off = align256(off + sizeof(float) * M * L.Vs);
+  if (w->wdtype == SPEC_BF16) {
+    L.ksd = roundup(w->d, kKStep) / kKStep;
+    L.ksf = roundup(w->ffn, kKStep) / kKStep;
+    L.xsd = off; off = align256(off + xs_bytes(L.M, L.ksd));
+    L.xsf = off; off = align256(off + xs_bytes(L.M, L.ksf));
+  }
   layout_sampling(L, B, gamma, w->V, off);
   L.total = off;
   return L;
@@ -130,8 +141,8 @@ spec_status register_matrix(spec_weights* w, const void* src, int K, int N, bool
 
 const void* mat_ptr(const Mat& m, int path) { return path == PATH_MFMA ? m.mfma : m.rowmajor; }
 
-hipError_t run_gemm_rows(int path, const Mat& W, const float* X, int ldx, int M, EpiArgs e,
-                         hipStream_t st);
+hipError_t run_gemm_rows(int path, const Mat& W, const float* X, const uint16_t* XS, int ldx,
+                         int M, EpiArgs e, hipStream_t st);
 
 hipError_t prof_event(spec_weights* w, size_t idx, hipStream_t st) {
   while (w->ev.size() <= idx) {
@@ -144,13 +155,13 @@ hipError_t prof_event(spec_weights* w, size_t idx, hipStream_t st) {
 }
 
 // One GEMM over all M rows, in row chunks the kernels can hold.
-hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, int ldx, int M,
-                    EpiArgs e, hipStream_t st) {
+hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, const uint16_t* XS,
+                    int ldx, int M, EpiArgs e, hipStream_t st) {
   if (w->prof) {
     const hipError_t err = prof_event(w, 2 * w->ev_used, st);
     if (err != hipSuccess) return err;
   }
-  const hipError_t err = run_gemm_rows(path, W, X, ldx, M, e, st);
+  const hipError_t err = run_gemm_rows(path, W, X, XS, ldx, M, e, st);
   if (err != hipSuccess || !w->prof) return err;
   const hipError_t err2 = prof_event(w, 2 * w->ev_used + 1, st);
   if (err2 != hipSuccess) return err2;
@@ -160,12 +171,16 @@ hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, int
   return hipSuccess;
 }
 
-hipError_t run_gemm_rows(int path, const Mat& W, const float* X, int ldx, int M, EpiArgs e,
-                         hipStream_t st) {
+// Row chunks start on 16-row tiles (the chunk sizes are multiples of 16),
+// so a chunk's split fragments begin at tile m0 / 16.
+hipError_t run_gemm_rows(int path, const Mat& W, const float* X, const uint16_t* XS, int ldx,
+                         int M, EpiArgs e, hipStream_t st) {
   const int chunk = max_rows(path);
+  static_assert(kMaxRowsMfma % 16 == 0, "MFMA row chunks must start on row tiles");
   for (int m0 = 0; m0 < M; m0 += chunk) {
     GemmArgs a;
     a.X = X + (size_t)m0 * ldx;
+    a.XS = XS ? XS + (size_t)(m0 / 16) * (W.Kp / kKStep + 1) * 3 * 512 : nullptr;
     a.ldx = ldx;
     a.M = std::min(chunk, M - m0);
     a.K = W.K;
@@ -179,6 +194,7 @@ hipError_t run_gemm_rows(int path, const Mat& W, const float* X, int ldx, int M,
       a.e.xg = e.xg + (size_t)m0 * e.ldo;
       a.e.ss_out = e.ss_out + (size_t)m0 * e.ss_ld;
     }
+    if (e.xs) a.e.xs = e.xs + (size_t)(m0 / 16) * (e.xs_ks + 1) * 3 * 512;
     a.e.row0 = m0;
     const GemmPlan p = plan_gemm(path, a.M, W);
     const hipError_t err = launch_gemm(p, a, st);
@@ -218,23 +234,28 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
   float* logits = at<float>(ws, L.logits);
   const int ss_ld = L.ldd / kSub;
   const int tmode = tmode_of(T);
+  // split activations, for the MFMA path only
+  uint16_t* xsd = path == PATH_MFMA ? at<uint16_t>(ws, L.xsd) : nullptr;
+  uint16_t* xsf = path == PATH_MFMA ? at<uint16_t>(ws, L.xsf) : nullptr;
 
   hipError_t err = launch_prep(h, xg, ss, ss_ld, hidden, w->n_blocks ? w->gain[0] : nullptr, M,
-                               w->d, L.ldd, st);
+                               w->d, L.ldd, xsd, L.ksd, xsf, L.ksf, st);
   for (int l = 0; l < w->n_blocks && err == hipSuccess; ++l) {
     EpiArgs up;
     up.kind = EPI_UP;
     up.out = act; up.ldo = L.ldf; up.N = w->ffn;
     up.ss_in = ss; up.ss_ld = ss_ld; up.ss_n = ss_ld;
     up.inv_d = 1.0f / (float)w->d; up.eps = w->eps;
-    err = run_gemm(w, path, w->up[l], xg, L.ldd, M, up, st);
+    up.xs = xsf; up.xs_ks = L.ksf;
+    err = run_gemm(w, path, w->up[l], xg, xsd, L.ldd, M, up, st);
     if (err != hipSuccess) break;
     EpiArgs dn;
     dn.kind = EPI_DOWN;
     dn.out = h; dn.ldo = L.ldd; dn.N = w->d;
     dn.xg = xg; dn.gain_next = l + 1 < w->n_blocks ? w->gain[l + 1] : nullptr;
     dn.ss_out = ss; dn.ss_ld = ss_ld;
-    err = run_gemm(w, path, w->down[l], act, L.ldf, M, dn, st);
+    dn.xs = xsd; dn.xs_ks = L.ksd;
+    err = run_gemm(w, path, w->down[l], act, xsf, L.ldf, M, dn, st);
   }
   if (err == hipSuccess) {
     EpiArgs lm;
@@ -243,7 +264,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
     lm.pst = at<float>(ws, L.pst); lm.pidx = at<int>(ws, L.pidx); lm.qst = at<float>(ws, L.qst);
     lm.q = q; lm.G = L.G; lm.G1 = gamma + 1; lm.gamma = gamma; lm.V = w->V;
     lm.tmode = tmode; lm.invT = tmode ? 1.0f / T : 1.0f;
-    err = run_gemm(w, path, w->lm, h, L.ldd, M, lm, st);
+    err = run_gemm(w, path, w->lm, h, xsd, L.ldd, M, lm, st);
   }
   SampleArgs sa;
   if (err == hipSuccess) {

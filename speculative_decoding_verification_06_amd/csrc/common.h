@@ -27,30 +27,39 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
   return b >> 16;
 }
 
-// Split 8 fp32 values into NSPLIT bf16 vectors whose sum reproduces them:
-// hi = bf16(x), mid = bf16(x - hi), lo = bf16(x - hi - mid).  Each
-// difference is exact in fp32, so three terms carry the full 24-bit
-// significand and two carry 16 bits.
-template <int NSPLIT>
-__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8 (&out)[NSPLIT]) {
-  float r[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = x[j];
-#pragma unroll
-  for (int s = 0; s < NSPLIT; ++s) {
-    u32x4 packed;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t b0 = bf16_bits_rne(r[2 * p]);
-      uint32_t b1 = bf16_bits_rne(r[2 * p + 1]);
-      packed[p] = b0 | (b1 << 16);
-      if (s + 1 < NSPLIT) {
-        r[2 * p] -= __uint_as_float(b0 << 16);
-        r[2 * p + 1] -= __uint_as_float(b1 << 16);
-      }
-    }
-    out[s] = __builtin_bit_cast(bf16x8, packed);
-  }
+// Exact split of an fp32 value into three bf16 terms, x = hi + mid + lo, by
+// truncation: hi keeps the top 8 significant bits, x - hi is exact in fp32
+// and holds at most 16 significant bits, mid keeps its top 8, and the rest
+// (at most 8 bits) is a bf16 exactly.  The three products with a bf16
+// weight are therefore exact, and an MFMA over the three terms reproduces
+// an fp32 x fp32 dot product up to the accumulation rounding.
+__device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t b0 = __float_as_uint(x) & 0xffff0000u;
+  const float r1 = x - __uint_as_float(b0);
+  const uint32_t b1 = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(b1);
+  hi = b0 >> 16;
+  mid = b1 >> 16;
+  lo = __float_as_uint(r2) >> 16;
+}
+
+// Split activations in MFMA A-operand order.  For a GEMM input X[M][K]
+// with KS k-steps of 32: 16-row tile mt, k-step s (0..KS, step KS is all
+// zero) and term p (hi, mid, lo) form one 1 KiB fragment of 64 lanes x 8
+// bf16, lane L holding row 16 mt + L % 16, columns 32 s + 8 (L / 16) + j.
+// Returns the bf16 index of (row, col) in term 0; terms 1 and 2 follow at
+// +512 and +1024.
+__device__ __forceinline__ size_t xs_index(int row, int col, int ks) {
+  const size_t frag = ((size_t)(row >> 4) * (ks + 1) + (col >> 5)) * 3;
+  return (frag * 64 + 16 * ((col & 31) >> 3) + (row & 15)) * 8 + (col & 7);
+}
+__device__ __forceinline__ void xs_store(uint16_t* xs, int row, int col, int ks, float x) {
+  uint32_t a, b, c;
+  split3_bf16(x, a, b, c);
+  const size_t i = xs_index(row, col, ks);
+  xs[i] = (uint16_t)a;
+  xs[i + 512] = (uint16_t)b;
+  xs[i + 1024] = (uint16_t)c;
 }
 
 // ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) -------------------

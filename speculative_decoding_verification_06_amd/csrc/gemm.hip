@@ -6,8 +6,9 @@
 // lattice-ai-eng.pages.dev: the single target call over k+1 positions is one
 // weight read; "Speculative Decoding: Speeding Sequential Generation",
 // aicomputerinstitute.com, Why Generation Is Slow: A Roofline View).  Each
-// weight byte is read from HBM once; activations stay fp32 (MFMA path:
-// split into bf16 hi/mid/lo terms) so the logits track a float64 reference.
+// weight byte is read from HBM once; activations stay fp32-exact (MFMA
+// path: three bf16 terms per value, split once by the kernel that produces
+// them) so the logits track a float64 reference.
 //
 // Work decomposition: a work group owns NT MFMA column tiles (16 columns
 // each) over the whole K range.  Its waves are MG row groups x KG k-groups;
@@ -61,17 +62,24 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
     const bool valid = live && n < e.N;
     const float v = live ? res[r * ldr + t * kSub + c] : 0.f;
     const size_t o = (size_t)r * e.ldo + n;
+    // columns past the next GEMM's k-steps have no fragment
+    const bool to_xs = e.xs != nullptr && live && n < kKStep * e.xs_ks;
     if (e.kind == EPI_UP) {
-      if (live) e.out[o] = valid ? silu(v * sh_inv[r]) : 0.f;
+      const float y = valid ? silu(v * sh_inv[r]) : 0.f;
+      if (live) e.out[o] = y;
+      if (to_xs) xs_store(e.xs, r, n, e.xs_ks, y);
     } else if (e.kind == EPI_DOWN) {
       float hn = 0.f;
       if (valid) hn = e.out[o] + v;
       if (live) e.out[o] = hn;
+      float y = hn;
       if (e.gain_next) {
-        if (live) e.xg[o] = valid ? hn * e.gain_next[n] : 0.f;
+        y = valid ? hn * e.gain_next[n] : 0.f;
+        if (live) e.xg[o] = y;
         const float sq = sum16(hn * hn);
         if (live && c == 0) e.ss_out[(size_t)r * e.ss_ld + tile] = sq;
       }
+      if (to_xs) xs_store(e.xs, r, n, e.xs_ks, y);
     } else {
       if (valid) e.out[o] = v;
       // padding subtiles past ceil(V / 16) hold no statistics
@@ -82,21 +90,23 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
 }
 
 // ---------------------------------------------------------------- MFMA GEMM
-// bf16 weights in MFMA tiles (layout in internal.h).  MTW = 16-row M tiles
-// per wave, MG row groups, NT column tiles per work group; the number of
-// k-groups KG = waves / MG is a launch parameter.
-// The weight stream is latency bound unless each CU keeps about 170 KiB of
-// loads in flight (8 TB/s over 256 CUs at ~5 us loaded latency), so waves run
-// two per SIMD and hold deep register pipelines: a k-step stage costs
-// 4 * NT VGPRs of weights and 8 * MTW of activations, and PIPE stages stay
-// within a 256-VGPR budget (~190 for the ring).
+// bf16 weights in MFMA tiles (layout in internal.h); the activations come
+// already split into three bf16 terms in A-fragment order (xs_index), so a
+// k-step is NT weight fragments + 3 activation fragments per 16-row tile
+// and 3 NT MFMAs, with no vector ALU work.  MTW = 16-row M tiles per wave,
+// MG row groups, NT column tiles per work group; the number of k-groups
+// KG = waves / MG is a launch parameter.
+// The weight stream is latency bound unless each CU keeps well over 100 KiB
+// of loads in flight, so waves run two per SIMD and hold deep register
+// pipelines: a k-step stage costs 4 * NT VGPRs of weights and 12 * MTW of
+// activations, and PIPE stages stay within the register budget.
 template <int MTW, int NT>
 struct MfmaPipe {
-  static constexpr int stage = 4 * NT + 8 * MTW;
+  static constexpr int stage = 4 * NT + 12 * MTW;
   static constexpr int value = MTW >= 3 ? 2 : (SV_PIPE_VGPRS / stage < 2 ? 2 : SV_PIPE_VGPRS / stage);
 };
 
-template <int MTW, int MG, int NT, int NSPLIT>
+template <int MTW, int MG, int NT>
 __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
   constexpr int PIPE = MfmaPipe<MTW, NT>::value;
   extern __shared__ float smem[];
@@ -109,6 +119,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
   const int c0 = blockIdx.x * NT;                 // first 16-column tile
   const int M = a.M, KS = a.KS;
   const int mt0 = mg * MTW;
+  const int MT = (M + 15) / 16;
   // this work group's column block: one contiguous span of KS * NT KiB
   const bf16x8* Wg = reinterpret_cast<const bf16x8*>(a.W) + (size_t)blockIdx.x * KS * NT * 64 + lane;
 
@@ -118,46 +129,41 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // rows this lane feeds as the A operand; rows past M read row M-1 (a
-  // cached line) and are zeroed before the split, so no load is divergent
-  const int arow = lane & 15, akoff = (lane >> 4) * 8;
-  const float* xrow[MTW];
-  bool xlive[MTW];
+  // A fragments of each row tile; lanes of rows past M (and tiles past the
+  // last) read the last real row, so every load is uniform and touches only
+  // cache lines the real rows use.  Their products land in output rows that
+  // are never stored.
+  const bf16x8* xsrow[MTW];
 #pragma unroll
   for (int i = 0; i < MTW; ++i) {
-    const int row = (mt0 + i) * 16 + arow;
-    xlive[i] = row < M;
-    xrow[i] = a.X + (size_t)min(row, M - 1) * a.ldx + akoff;
+    const int mt = min(mt0 + i, MT - 1);
+    const int rows = min(16, M - mt * 16);
+    const int al = (lane & 48) + min(lane & 15, rows - 1);
+    xsrow[i] = reinterpret_cast<const bf16x8*>(a.XS) + (size_t)mt * (KS + 1) * 3 * 64 + al;
   }
   const bool wave_live = (mt0 * 16) < M;
 
   bf16x8 bq[PIPE][NT];
-  float4 xq[PIPE][MTW][2];
+  bf16x8 xq[PIPE][MTW][3];
 
-#define SV_LOAD(u, kk)                                                           \
+  // kw: weight k-step; ka: activation k-step (KS = the all-zero step)
+#define SV_LOAD(u, kw, ka)                                                       \
   {                                                                              \
-    const bf16x8* wp = Wg + (size_t)(kk) * NT * 64;                              \
+    const bf16x8* wp = Wg + (size_t)(kw) * NT * 64;                              \
     _Pragma("unroll") for (int t = 0; t < NT; ++t) bq[u][t] = wp[t * 64];        \
     _Pragma("unroll") for (int i = 0; i < MTW; ++i) {                            \
-      const float4* xp = reinterpret_cast<const float4*>(xrow[i] + (kk) * kKStep); \
-      xq[u][i][0] = xp[0];                                                       \
-      xq[u][i][1] = xp[1];                                                       \
+      const bf16x8* xp = xsrow[i] + (size_t)(ka) * 3 * 64;                       \
+      _Pragma("unroll") for (int p = 0; p < 3; ++p) xq[u][i][p] = xp[p * 64];    \
     }                                                                            \
   }
 
-#define SV_COMPUTE(u, on)                                                        \
+#define SV_COMPUTE(u)                                                            \
   {                                                                              \
     _Pragma("unroll") for (int i = 0; i < MTW; ++i) {                            \
       if ((mt0 + i) * 16 < M) {                                                  \
-        const float z = (xlive[i] && (on)) ? 1.0f : 0.0f;                        \
-        const float xs[8] = {xq[u][i][0].x * z, xq[u][i][0].y * z, xq[u][i][0].z * z, \
-                             xq[u][i][0].w * z, xq[u][i][1].x * z, xq[u][i][1].y * z, \
-                             xq[u][i][1].z * z, xq[u][i][1].w * z};               \
-        bf16x8 av[NSPLIT];                                                       \
-        split_bf16x8<NSPLIT>(xs, av);                                            \
         _Pragma("unroll") for (int t = 0; t < NT; ++t) {                         \
-          _Pragma("unroll") for (int p = 0; p < NSPLIT; ++p)                     \
-            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[p], bq[u][t],  \
+          _Pragma("unroll") for (int p = 0; p < 3; ++p)                          \
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xq[u][i][p], bq[u][t], \
                                                                 acc[i][t], 0, 0, 0); \
         }                                                                        \
       }                                                                          \
@@ -167,24 +173,26 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
   // Software pipeline over a ring of PIPE k-steps: each stage is computed,
   // then refilled with the k-step PIPE positions ahead, so PIPE - 1 k-steps
   // of loads stay in flight while one is consumed.  The loop body has no
-  // branches: refills past the wave's last k-step reload that k-step (a
-  // cache hit) and stages past the end compute with a zero A operand, so
-  // every path issues the same loads and each wait covers only the oldest
-  // stage.  sched_barrier keeps the issue order of the stages.
+  // branches: a refill past the wave's last k-step reloads that step's
+  // weights (a cache hit) with the all-zero activation step, so its MFMAs
+  // add nothing, every path issues the same loads and each wait covers only
+  // the oldest stage.  sched_barrier keeps the issue order of the stages.
   int k = kg;
   if (wave_live && k < KS) {
     const int n = (KS - k + KG - 1) / KG;            // k-steps of this wave
     const int klast = k + (n - 1) * KG;
 #pragma unroll
     for (int u = 0; u < PIPE; ++u) {
-      SV_LOAD(u, min(k + u * KG, klast));
+      const int kk = k + u * KG;
+      SV_LOAD(u, min(kk, klast), kk <= klast ? kk : KS);
       __builtin_amdgcn_sched_barrier(0);
     }
     for (int it = 0; it < n; it += PIPE) {
 #pragma unroll
       for (int u = 0; u < PIPE; ++u) {
-        SV_COMPUTE(u, it + u < n);
-        SV_LOAD(u, min(k + (it + u + PIPE) * KG, klast));
+        SV_COMPUTE(u);
+        const int kk = k + (it + u + PIPE) * KG;
+        SV_LOAD(u, min(kk, klast), kk <= klast ? kk : KS);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -352,9 +360,9 @@ template <int MTW, int MG>
 static hipError_t launch_mfma_mg(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
   const dim3 grid(p.blocks), block(64 * p.mg * p.kg);
   switch (p.nt) {
-    case 1: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 1, 3>), grid, block, p.lds, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 2, 3>), grid, block, p.lds, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 4, 3>), grid, block, p.lds, st, a); break;
+    case 1: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 1>), grid, block, p.lds, st, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 2>), grid, block, p.lds, st, a); break;
+    default: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 4>), grid, block, p.lds, st, a); break;
   }
   return hipGetLastError();
 }

@@ -58,10 +58,17 @@ struct EpiArgs {
   int row0 = 0;               // global index of this launch's first row
   int tmode = 0;              // 0 greedy, 1 T == 1, 2 general T
   float invT = 1.f;
+  // the output again as split bf16 A fragments for the next GEMM (xs_index
+  // order, xs_ks k-steps; null when that GEMM is not an MFMA one): UP
+  // writes act, DOWN the next block's normalised input or, after the last
+  // block, h for the LM head
+  uint16_t* xs = nullptr;
+  int xs_ks = 0;
 };
 
 struct GemmArgs {
-  const float* X = nullptr;   // [M][ldx] fp32, columns >= K are zero
+  const float* X = nullptr;   // [M][ldx] fp32, columns >= K are zero (FMA path)
+  const void* XS = nullptr;   // X as split bf16 A fragments, KS + 1 k-steps (MFMA path)
   int ldx = 0, M = 0, K = 0;
   const void* W = nullptr;
   int Np = 0, KS = 0;         // KS = Kp / 32
@@ -101,8 +108,13 @@ struct SampleArgs {
   float* p_out = nullptr; float* q_out = nullptr;   // debug dumps
 };
 
+// Copies hidden into h, forms xg = h * gain0 and its per-16-column sums of
+// squares; with xs0 non-null also writes the first GEMM's split input (xg,
+// or h when there is no MLP block) and clears the zero k-step of each of
+// the split buffers xs0 (ks0 k-steps) and xs1 (ks1 k-steps).
 hipError_t launch_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
-                       const float* gain0, int M, int d, int ld, hipStream_t st);
+                       const float* gain0, int M, int d, int ld, uint16_t* xs0, int ks0,
+                       uint16_t* xs1, int ks1, hipStream_t st);
 hipError_t launch_tile_stats(const SampleArgs& a, hipStream_t st);
 hipError_t launch_sampling(const SampleArgs& a, hipStream_t st);
 hipError_t launch_dump_probs(const SampleArgs& a, hipStream_t st);

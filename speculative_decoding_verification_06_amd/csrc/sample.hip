@@ -58,25 +58,44 @@ __device__ __forceinline__ float q_prime(const float* ri, float qv, int v, int t
 }
 
 // ---------------------------------------------------------------- prep
-// h = hidden (zero-padded rows of ld), xg = h * gain0, and the sum of
-// squares of h per 16-column subtile.
+// h = hidden (zero-padded rows of ld), xg = h * gain0, the sum of squares of
+// h per 16-column subtile, and the split A fragments of the first GEMM's
+// input.  Work group (0, m) with m < ceil(M / 16) also clears the zero
+// k-step of row tile m in both split buffers.
+__device__ __forceinline__ void clear_zero_step(uint16_t* xs, int mt, int ks, int lane) {
+  uint4* f = reinterpret_cast<uint4*>(xs + ((size_t)mt * (ks + 1) + ks) * 3 * 512);
+#pragma unroll
+  for (int p = 0; p < 3; ++p) f[p * 64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 __global__ void k_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
-                       const float* gain0, int d, int ld) {
+                       const float* gain0, int d, int ld, uint16_t* xs0, int ks0, uint16_t* xs1,
+                       int ks1) {
   const int lane = threadIdx.x, g = blockIdx.x, m = blockIdx.y;
   const int n = g * kGroupCols + lane;
   const float v = n < d ? hidden[(size_t)m * d + n] : 0.f;
   h[(size_t)m * ld + n] = v;
+  float x = v;
   if (gain0) {
-    xg[(size_t)m * ld + n] = n < d ? v * gain0[n] : 0.f;
+    x = n < d ? v * gain0[n] : 0.f;
+    xg[(size_t)m * ld + n] = x;
     const float sq = sum16(v * v);
     if ((lane & 15) == 0) ss[(size_t)m * ss_ld + g * 4 + (lane >> 4)] = sq;
+  }
+  if (xs0) {
+    if (n < kKStep * ks0) xs_store(xs0, m, n, ks0, x);
+    if (g == 0 && m * 16 < gridDim.y) {
+      clear_zero_step(xs0, m, ks0, lane);
+      if (xs1) clear_zero_step(xs1, m, ks1, lane);
+    }
   }
 }
 
 hipError_t launch_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
-                       const float* gain0, int M, int d, int ld, hipStream_t st) {
+                       const float* gain0, int M, int d, int ld, uint16_t* xs0, int ks0,
+                       uint16_t* xs1, int ks1, hipStream_t st) {
   hipLaunchKernelGGL(k_prep, dim3(ld / kGroupCols, M), dim3(kWave), 0, st, h, xg, ss, ss_ld,
-                     hidden, gain0, d, ld);
+                     hidden, gain0, d, ld, xs0, ks0, xs1, ks1);
   return hipGetLastError();
 }
 
