@@ -45,10 +45,24 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q4 = lane >> 4, c = lane & 15;
   if (e.kind == EPI_UP) {
-    for (int r = threadIdx.x; r < M; r += blockDim.x) {
-      float s = 0.f;
-      for (int t = 0; t < e.ss_n; ++t) s += e.ss_in[(size_t)r * e.ss_ld + t];
-      sh_inv[r] = 1.0f / sqrtf(s * e.inv_d + e.eps);
+    // 1 / rms per row from its per-16-column sums of squares: one wave per
+    // row, each lane summing a fixed strided subset (8 independent loads in
+    // flight), then a butterfly; the order is fixed, so the bits are too
+    for (int r = wave; r < M; r += nwaves) {
+      const float* ps = e.ss_in + (size_t)r * e.ss_ld;
+      float part[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part[j] = 0.f;
+      for (int t0 = 0; t0 < e.ss_n; t0 += 8 * kWave) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = t0 + j * kWave + lane;
+          part[j] += t < e.ss_n ? ps[t] : 0.f;
+        }
+      }
+      float s = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+      s = wave_sum(s);
+      if (lane == 0) sh_inv[r] = 1.0f / sqrtf(s * e.inv_d + e.eps);
     }
     __syncthreads();
   }
