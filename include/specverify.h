@@ -162,9 +162,10 @@ spec_status spec_verify_from_logits(int32_t B, int32_t gamma, int32_t vocab,
                                     void* stream);
 
 /* Kernel timing for benchmarks.  While enabled, every GEMM launch that
- * spec_verify / spec_verify_debug make with these weights is bracketed by a
- * pair of HIP events recorded on the launch stream (the library creates the
- * events; a call may grow the pool).  spec_profile_read synchronises those
+ * spec_verify / spec_verify_debug make with these weights carries a pair of
+ * HIP events that take the kernel's own start and end timestamps
+ * (hipExtLaunchKernel; the library creates the events, and a call may grow
+ * the pool).  spec_profile_read synchronises those
  * events and returns, since the previous read or enable: the summed GEMM
  * time in milliseconds, the number of GEMM launches, and the algorithmic
  * weight bytes they streamed (K * N * bytes per weight, padding excluded);

@@ -38,15 +38,11 @@ inline int roundup(int x, int m) { return (x + m - 1) / m * m; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  int M = 0, ldd = 0, ldf = 0, Vs = 0, G = 0, nch = 0;
+  int M = 0, ldd = 0, ldf = 0, Vs = 0, G = 0, Gu = 0, nch = 0;
   int ksd = 0, ksf = 0;       // k-steps of the d- and ffn-wide split inputs
   size_t h = 0, xg = 0, ss = 0, act = 0, logits = 0, pst = 0, pidx = 0, qst = 0, rowinfo = 0,
          dec = 0, csum = 0, xsd = 0, xsf = 0, total = 0;
 };
-
-// Bytes of one split-activation buffer: ceil(M / 16) row tiles of KS + 1
-// k-steps of three 1 KiB fragments.
-size_t xs_bytes(int M, int ks) { return (size_t)((M + 15) / 16) * (ks + 1) * 3 * 1024; }
 
 int gemm_path(const spec_weights* w, int M) {
   if (w->wdtype == SPEC_F32) return PATH_FMA_F32;
@@ -54,11 +50,22 @@ int gemm_path(const spec_weights* w, int M) {
   return (M >= w->mfma_min_rows || !have_rm) ? PATH_MFMA : PATH_FMA_BF16;
 }
 
+// Statistics units per logits row: one per LM-head work group (nt tiles of
+// 16 columns; the vector-FMA path covers 4 tiles per work group).
+int lm_units(const spec_weights* w, int M) {
+  const int path = gemm_path(w, M);
+  const int nt = path == PATH_MFMA ? w->lm.nt : kGroupCols / kSub;
+  return w->lm.Np / kSub / nt;
+}
+
 int max_rows(int path) { return path == PATH_MFMA ? kMaxRowsMfma : kMaxRowsFma; }
 
 // Sampling-side buffers, shared by both entry points.
-void layout_sampling(Layout& L, int B, int gamma, int V, size_t& off) {
-  L.G = (V + kSub - 1) / kSub;
+// G statistics units per row, stored at an even stride Gs so rows load in
+// 16-byte pairs.
+void layout_sampling(Layout& L, int B, int gamma, int V, int G, size_t& off) {
+  L.Gu = G;
+  L.G = (G + 1) & ~1;
   L.nch = (V + kResampleChunk - 1) / kResampleChunk;
   const size_t qrows = (size_t)B * gamma;
   L.pst = off; off = align256(off + sizeof(float) * 2 * (size_t)L.M * L.G);
@@ -88,7 +95,7 @@ Layout make_layout(const spec_weights* w, int B, int gamma) {
     L.xsd = off; off = align256(off + xs_bytes(L.M, L.ksd));
     L.xsf = off; off = align256(off + xs_bytes(L.M, L.ksf));
   }
-  layout_sampling(L, B, gamma, w->V, off);
+  layout_sampling(L, B, gamma, w->V, lm_units(w, L.M), off);
   L.total = off;
   return L;
 }
@@ -141,41 +148,28 @@ spec_status register_matrix(spec_weights* w, const void* src, int K, int N, bool
 
 const void* mat_ptr(const Mat& m, int path) { return path == PATH_MFMA ? m.mfma : m.rowmajor; }
 
-hipError_t run_gemm_rows(int path, const Mat& W, const float* X, const uint16_t* XS, int ldx,
-                         int M, EpiArgs e, hipStream_t st);
-
-hipError_t prof_event(spec_weights* w, size_t idx, hipStream_t st) {
-  while (w->ev.size() <= idx) {
+// Events for timed launch idx (created on first use).
+hipError_t prof_events(spec_weights* w, size_t idx, hipEvent_t& e0, hipEvent_t& e1) {
+  while (w->ev.size() < 2 * (idx + 1)) {
     hipEvent_t e;
     const hipError_t err = hipEventCreate(&e);
     if (err != hipSuccess) return err;
     w->ev.push_back(e);
   }
-  return hipEventRecord(w->ev[idx], st);
-}
-
-// One GEMM over all M rows, in row chunks the kernels can hold.
-hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, const uint16_t* XS,
-                    int ldx, int M, EpiArgs e, hipStream_t st) {
-  if (w->prof) {
-    const hipError_t err = prof_event(w, 2 * w->ev_used, st);
-    if (err != hipSuccess) return err;
-  }
-  const hipError_t err = run_gemm_rows(path, W, X, XS, ldx, M, e, st);
-  if (err != hipSuccess || !w->prof) return err;
-  const hipError_t err2 = prof_event(w, 2 * w->ev_used + 1, st);
-  if (err2 != hipSuccess) return err2;
-  w->ev_bytes.resize(w->ev_used + 1);
-  w->ev_bytes[w->ev_used] = (int64_t)W.K * W.N * (w->wdtype == SPEC_F32 ? 4 : 2);
-  ++w->ev_used;
+  e0 = w->ev[2 * idx];
+  e1 = w->ev[2 * idx + 1];
   return hipSuccess;
 }
 
-// Row chunks start on 16-row tiles (the chunk sizes are multiples of 16),
-// so a chunk's split fragments begin at tile m0 / 16.
-hipError_t run_gemm_rows(int path, const Mat& W, const float* X, const uint16_t* XS, int ldx,
-                         int M, EpiArgs e, hipStream_t st) {
+// One GEMM over all M rows, in row chunks the kernels can hold.  Row chunks
+// start on 16-row tiles (the chunk sizes are multiples of 16), so a
+// chunk's split fragments begin at tile m0 / 16.  With timing on, every
+// launch carries a pair of events and its algorithmic weight bytes.
+hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, const uint16_t* XS,
+                    int ldx, int M, EpiArgs e, hipStream_t st) {
   const int chunk = max_rows(path);
+  // the packing follows the whole pass's row count (a stacked pass is one chunk)
+  const bool stack = path == PATH_MFMA && xs_stacked(M);
   static_assert(kMaxRowsMfma % 16 == 0, "MFMA row chunks must start on row tiles");
   for (int m0 = 0; m0 < M; m0 += chunk) {
     GemmArgs a;
@@ -195,10 +189,21 @@ hipError_t run_gemm_rows(int path, const Mat& W, const float* X, const uint16_t*
       a.e.ss_out = e.ss_out + (size_t)m0 * e.ss_ld;
     }
     if (e.xs) a.e.xs = e.xs + (size_t)(m0 / 16) * (e.xs_ks + 1) * 3 * 512;
+    a.e.xs_stack = stack;
     a.e.row0 = m0;
-    const GemmPlan p = plan_gemm(path, a.M, W);
-    const hipError_t err = launch_gemm(p, a, st);
+    const GemmPlan p = plan_gemm(path, a.M, W, stack);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (w->prof) {
+      const hipError_t err = prof_events(w, w->ev_used, e0, e1);
+      if (err != hipSuccess) return err;
+    }
+    const hipError_t err = launch_gemm(p, a, st, e0, e1);
     if (err != hipSuccess) return err;
+    if (w->prof) {
+      w->ev_bytes.resize(w->ev_used + 1);
+      w->ev_bytes[w->ev_used] = (int64_t)W.K * W.N * (w->wdtype == SPEC_F32 ? 4 : 2);
+      ++w->ev_used;
+    }
   }
   return hipSuccess;
 }
@@ -268,7 +273,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
   }
   SampleArgs sa;
   if (err == hipSuccess) {
-    sa.B = B; sa.gamma = gamma; sa.V = w->V; sa.G = L.G; sa.M = M;
+    sa.B = B; sa.gamma = gamma; sa.V = w->V; sa.G = L.G; sa.Gu = L.Gu; sa.M = M;
     sa.logits = logits; sa.ldl = L.Vs; sa.q = q; sa.draft = draft;
     sa.T = T; sa.invT = tmode ? 1.0f / T : 1.0f; sa.top_p = top_p; sa.tmode = tmode; sa.seed = seed;
     sa.n_acc = n_acc; sa.emitted = emitted;
@@ -415,7 +420,7 @@ size_t spec_workspace_size_from_logits(int32_t B, int32_t gamma, int32_t vocab) 
   Layout L;
   L.M = B * (gamma + 1);
   size_t off = 0;
-  layout_sampling(L, B, gamma, vocab, off);
+  layout_sampling(L, B, gamma, vocab, (vocab + 4 * kSub - 1) / (4 * kSub), off);
   return off;
 }
 
@@ -432,14 +437,14 @@ spec_status spec_verify_from_logits(int32_t B, int32_t gamma, int32_t vocab, con
   Layout L;
   L.M = B * (gamma + 1);
   size_t off = 0;
-  layout_sampling(L, B, gamma, vocab, off);
+  layout_sampling(L, B, gamma, vocab, (vocab + 4 * kSub - 1) / (4 * kSub), off);
   if (!workspace || workspace_bytes < off || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return SPEC_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const int tmode = tmode_of(temperature);
   SampleArgs sa;
-  sa.B = B; sa.gamma = gamma; sa.V = vocab; sa.G = L.G; sa.M = L.M;
+  sa.B = B; sa.gamma = gamma; sa.V = vocab; sa.G = L.G; sa.Gu = L.Gu; sa.M = L.M;
   sa.logits = logits; sa.ldl = vocab; sa.q = q; sa.draft = draft_tokens;
   sa.T = temperature; sa.invT = tmode ? 1.0f / temperature : 1.0f; sa.top_p = top_p;
   sa.tmode = tmode; sa.seed = seed;

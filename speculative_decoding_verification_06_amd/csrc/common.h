@@ -44,22 +44,37 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid
 }
 
 // Split activations in MFMA A-operand order.  For a GEMM input X[M][K]
-// with KS k-steps of 32: 16-row tile mt, k-step s (0..KS, step KS is all
-// zero) and term p (hi, mid, lo) form one 1 KiB fragment of 64 lanes x 8
-// bf16, lane L holding row 16 mt + L % 16, columns 32 s + 8 (L / 16) + j.
-// Returns the bf16 index of (row, col) in term 0; terms 1 and 2 follow at
-// +512 and +1024.
-__device__ __forceinline__ size_t xs_index(int row, int col, int ks) {
-  const size_t frag = ((size_t)(row >> 4) * (ks + 1) + (col >> 5)) * 3;
-  return (frag * 64 + 16 * ((col & 31) >> 3) + (row & 15)) * 8 + (col & 7);
+// with KS k-steps of 32 (step KS is all zero), one 1 KiB fragment holds 64
+// lanes x 8 bf16, lane L holding A-rows L % 16 at columns
+// 32 s + 8 (L / 16) + j of k-step s.  Two packings of the three terms:
+//   plain   : row tile mt = 16 rows; k-step s of the tile is three
+//             fragments (hi, mid, lo), all multiplied into one accumulator
+//   stacked : row tile mt = kStackRows rows; one fragment per k-step whose
+//             A-row 5 p + r holds term p of row 5 mt + r (A-row 15 unused),
+//             so a single MFMA covers every term of five rows and the
+//             terms are summed after the k-loop
+// xs_index returns the bf16 index of term 0 of (row, col); term p sits at
+// +p * xs_term_step(stacked).
+constexpr int kStackRows = 5;
+__device__ __forceinline__ int xs_term_step(bool stacked) { return stacked ? 8 * kStackRows : 512; }
+__device__ __forceinline__ size_t xs_index(int row, int col, int ks, bool stacked) {
+  const int lane_hi = 16 * ((col & 31) >> 3), s = col >> 5, j = col & 7;
+  if (stacked) {
+    const size_t frag = (size_t)(row / kStackRows) * (ks + 1) + s;
+    return (frag * 64 + lane_hi + row % kStackRows) * 8 + j;
+  }
+  const size_t frag = ((size_t)(row >> 4) * (ks + 1) + s) * 3;
+  return (frag * 64 + lane_hi + (row & 15)) * 8 + j;
 }
-__device__ __forceinline__ void xs_store(uint16_t* xs, int row, int col, int ks, float x) {
+__device__ __forceinline__ void xs_store(uint16_t* xs, int row, int col, int ks, bool stacked,
+                                         float x) {
   uint32_t a, b, c;
   split3_bf16(x, a, b, c);
-  const size_t i = xs_index(row, col, ks);
+  const size_t i = xs_index(row, col, ks, stacked);
+  const int st = xs_term_step(stacked);
   xs[i] = (uint16_t)a;
-  xs[i + 512] = (uint16_t)b;
-  xs[i + 1024] = (uint16_t)c;
+  xs[i + st] = (uint16_t)b;
+  xs[i + 2 * st] = (uint16_t)c;
 }
 
 // ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) -------------------
@@ -161,32 +176,40 @@ __device__ __forceinline__ void argmax16(float& v, int& idx) {
   }
 }
 
-// Statistics of one 16-column logits subtile, one column per lane of a
-// 16-lane group (every lane of the wave must call): greedy -> (max, lowest
-// argmax); otherwise (max, sum exp((l - max)/T)) for p and, for draft rows
-// (i < gamma), the statistics of q': T == 1 -> sum q; else
-// (max y, sum exp(y - max y)) with y = log(q) / T.  `live` marks groups that
-// hold a real (row, subtile); lane 16k of a live group writes.
-__device__ __forceinline__ void lm_subtile_stats(float l, bool valid, bool live, int n, int grow,
-                                                 int tile, int G, int G1, int gamma, int V,
-                                                 int tmode, float invT, const float* q,
-                                                 float* pst, int* pidx, float* qst) {
-  const bool writer = live && (threadIdx.x & 15) == 0;
-  const size_t t = (size_t)grow * G + tile;
+// Softmax / argmax statistics of one unit of U adjacent 16-column logits
+// tiles of a row (U = 1, 2 or 4), one column per lane; the U tiles sit in
+// 16-lane groups k U .. k U + U - 1 of the wave, and every lane of the wave
+// must call.  Greedy -> (max, lowest argmax); otherwise (max, sum exp((l -
+// max)/T)) for p and, for draft rows (i < gamma), the statistics of q' from
+// the lane's draft probability qv: T == 1 -> sum q; else (max y, sum exp(y -
+// max y)) with y = log(q) / T.  Each tile is reduced over its 16 lanes, then
+// the U tiles are merged in a lane-independent order, so every lane holds
+// the same bits; the unit's first lane writes when `live`.
+__device__ __forceinline__ void lm_unit_stats(float l, bool valid, bool live, int n, int grow,
+                                              int unit, int U, int G, int G1, int gamma, int tmode,
+                                              float invT, float qv, float* pst, int* pidx,
+                                              float* qst) {
+  const int lane = threadIdx.x & 63;
+  const bool writer = live && (lane & (16 * U - 1)) == 0;
+  const size_t t = (size_t)grow * G + unit;
   if (tmode == 0) {
     float v = valid ? l : -INFINITY;
     int idx = valid ? n : 0x7fffffff;
     argmax16(v, idx);
+    for (int o = 16; o < 16 * U; o <<= 1) {
+      const float ov = __shfl_xor(v, o, kWave);
+      const int oi = __shfl_xor(idx, o, kWave);
+      if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+    }
     if (writer) { pst[2 * t] = v; pst[2 * t + 1] = 0.f; pidx[t] = idx; }
     return;
   }
-  const float mx = max16(valid ? l : -INFINITY);
-  const float se = sum16(valid ? expf((l - mx) * invT) : 0.f);
-  if (writer) { pst[2 * t] = mx; pst[2 * t + 1] = se; }
+  float mx = max16(valid ? l : -INFINITY);
+  float se = sum16(valid ? expf((l - mx) * invT) : 0.f);
   const int b = grow / G1, i = grow - b * G1;
   const bool qrow_ok = live && i < gamma;
   const size_t qrow = (size_t)b * gamma + i;
-  const float qv = (qrow_ok && valid) ? q[qrow * V + n] : 0.f;
+  if (!(qrow_ok && valid)) qv = 0.f;
   float ym = 0.f, sq;
   if (tmode == 1) {
     sq = sum16(qv);
@@ -195,8 +218,24 @@ __device__ __forceinline__ void lm_subtile_stats(float l, bool valid, bool live,
     ym = max16(y);
     sq = sum16(qv > 0.f ? expf(y - ym) : 0.f);
   }
+  for (int o = 16; o < 16 * U; o <<= 1) {
+    const bool swap = (lane & o) != 0;
+    float m2 = __shfl_xor(mx, o, kWave), s2 = __shfl_xor(se, o, kWave);
+    float am = swap ? m2 : mx, as = swap ? s2 : se, bm = swap ? mx : m2, bs = swap ? se : s2;
+    lse_merge(am, as, bm, bs, invT);
+    mx = am; se = as;
+    const float y2 = __shfl_xor(ym, o, kWave), q2 = __shfl_xor(sq, o, kWave);
+    if (tmode == 1) {
+      sq = swap ? q2 + sq : sq + q2;
+    } else {
+      am = swap ? y2 : ym; as = swap ? q2 : sq; bm = swap ? ym : y2; bs = swap ? sq : q2;
+      lse_merge(am, as, bm, bs, 1.0f);
+      ym = am; sq = as;
+    }
+  }
+  if (writer) { pst[2 * t] = mx; pst[2 * t + 1] = se; }
   if (writer && qrow_ok) {
-    const size_t tq = qrow * G + tile;
+    const size_t tq = qrow * G + unit;
     qst[2 * tq] = ym;
     qst[2 * tq + 1] = sq;
   }

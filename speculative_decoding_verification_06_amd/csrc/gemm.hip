@@ -19,6 +19,8 @@
 // costs far more than the weight stream at these sizes), and the sums are
 // bit-identical from run to run.
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "internal.h"
 
@@ -29,7 +31,7 @@
 #define SV_MIN_BLOCKS 256         // work groups wanted per GEMM (one per CU)
 #endif
 #ifndef SV_PIPE_VGPRS
-#define SV_PIPE_VGPRS 192         // VGPRs of the load ring per wave
+#define SV_PIPE_VGPRS 64          // VGPRs of the load ring per wave
 #endif
 
 namespace sv {
@@ -38,12 +40,79 @@ __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
 // ---------------------------------------------------------------- epilogues
 // res: LDS tile [M][ldr] of finished sums for column tiles c0 .. c0+nt-1.
-// Items are (row, 16-column tile) pairs; a wave handles 4 items at a time,
-// one per 16-lane group, with one column per lane.
-__device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const float* res, int ldr,
-                             float* sh_inv, int nwaves) {
+// Items are (row, 16-column tile) pairs; a wave handles 4 items at a time
+// (a round), one per 16-lane group, with one column per lane.
+//
+// What an epilogue reads from global memory does not depend on the GEMM,
+// so epi_prefetch loads it before the k-loop and its latency hides under
+// the weight stream instead of adding a round trip to every work group's
+// tail.  pv holds, for UP, the first 8 * 64 per-16-column sums of squares
+// of the wave's first row; for DOWN and LM, per item of the first
+// kPreRounds rounds, the residual h and next gain (DOWN) or the draft
+// probability q of the item's column (LM).  Later rounds load on demand.
+constexpr int kPreRounds = 4;
+
+struct EpiItem {
+  bool live, valid;
+  int r, t, tile, n;
+  size_t o;
+};
+
+__device__ __forceinline__ EpiItem epi_item(const EpiArgs& e, int M, int c0, int nt, int base) {
+  const int lane = threadIdx.x & 63;
+  EpiItem x;
+  const int items = M * nt;
+  const int it = base + (lane >> 4);
+  x.live = it < items;
+  x.r = x.live ? it / nt : 0;
+  x.t = x.live ? it - x.r * nt : 0;
+  x.tile = c0 + x.t;
+  x.n = x.tile * kSub + (lane & 15);
+  x.valid = x.live && x.n < e.N;
+  x.o = (size_t)x.r * e.ldo + x.n;
+  return x;
+}
+
+// q value of an LM item (0 for the bonus row, invalid columns or greedy).
+__device__ __forceinline__ float lm_item_q(const EpiArgs& e, const EpiItem& x) {
+  if (e.tmode == 0 || !x.valid) return 0.f;
+  const int grow = e.row0 + x.r;
+  const int b = grow / e.G1, i = grow - b * e.G1;
+  return i < e.gamma ? e.q[((size_t)b * e.gamma + i) * e.V + x.n] : 0.f;
+}
+
+__device__ __forceinline__ void epi_prefetch(const EpiArgs& e, int M, int c0, int nt, int nwaves,
+                                             float (&pv)[8]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q4 = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pv[j] = 0.f;
+  if (e.kind == EPI_UP) {
+    if (wave < M) {
+      const float* ps = e.ss_in + (size_t)wave * e.ss_ld;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = j * kWave + lane;
+        pv[j] = t < e.ss_n ? ps[t] : 0.f;
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < kPreRounds; ++k) {
+    const EpiItem x = epi_item(e, M, c0, nt, wave * 4 + k * nwaves * 4);
+    if (e.kind == EPI_DOWN) {
+      pv[2 * k] = x.valid ? e.out[x.o] : 0.f;
+      pv[2 * k + 1] = (x.valid && e.gain_next) ? e.gain_next[x.n] : 0.f;
+    } else {
+      pv[2 * k] = lm_item_q(e, x);
+    }
+  }
+}
+
+__device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const float* res, int ldr,
+                             float* sh_inv, int nwaves, const float (&pv)[8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15;
   if (e.kind == EPI_UP) {
     // 1 / rms per row from its per-16-column sums of squares: one wave per
     // row, each lane summing a fixed strided subset (8 independent loads in
@@ -52,8 +121,11 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
       const float* ps = e.ss_in + (size_t)r * e.ss_ld;
       float part[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) part[j] = 0.f;
-      for (int t0 = 0; t0 < e.ss_n; t0 += 8 * kWave) {
+      for (int j = 0; j < 8; ++j) {
+        const int t = j * kWave + lane;
+        part[j] = r == wave ? pv[j] : (t < e.ss_n ? ps[t] : 0.f);
+      }
+      for (int t0 = 8 * kWave; t0 < e.ss_n; t0 += 8 * kWave) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = t0 + j * kWave + lane;
@@ -67,38 +139,39 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
     __syncthreads();
   }
   const int items = M * nt;
-  for (int base = wave * 4; base < items; base += nwaves * 4) {
-    const int it = base + q4;
-    const bool live = it < items;
-    const int r = live ? it / nt : 0, t = live ? it - r * nt : 0;
-    const int tile = c0 + t;
-    const int n = tile * kSub + c;
-    const bool valid = live && n < e.N;
-    const float v = live ? res[r * ldr + t * kSub + c] : 0.f;
-    const size_t o = (size_t)r * e.ldo + n;
+  int k = 0;
+  for (int base = wave * 4; base < items; base += nwaves * 4, ++k) {
+    const EpiItem x = epi_item(e, M, c0, nt, base);
+    const bool pre = k < kPreRounds;
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kPreRounds; ++kk)
+      if (k == kk) { p0 = pv[2 * kk]; p1 = pv[2 * kk + 1]; }
+    const float v = x.live ? res[x.r * ldr + x.t * kSub + c] : 0.f;
     // columns past the next GEMM's k-steps have no fragment
-    const bool to_xs = e.xs != nullptr && live && n < kKStep * e.xs_ks;
+    const bool to_xs = e.xs != nullptr && x.live && x.n < kKStep * e.xs_ks;
     if (e.kind == EPI_UP) {
-      const float y = valid ? silu(v * sh_inv[r]) : 0.f;
-      if (live) e.out[o] = y;
-      if (to_xs) xs_store(e.xs, r, n, e.xs_ks, y);
+      const float y = x.valid ? silu(v * sh_inv[x.r]) : 0.f;
+      if (x.live && !e.xs) e.out[x.o] = y;   // the MFMA path reads only the split copy
+      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, e.xs_stack, y);
     } else if (e.kind == EPI_DOWN) {
       float hn = 0.f;
-      if (valid) hn = e.out[o] + v;
-      if (live) e.out[o] = hn;
+      if (x.valid) hn = (pre ? p0 : e.out[x.o]) + v;
+      if (x.live) e.out[x.o] = hn;
       float y = hn;
       if (e.gain_next) {
-        y = valid ? hn * e.gain_next[n] : 0.f;
-        if (live) e.xg[o] = y;
+        y = x.valid ? hn * (pre ? p1 : e.gain_next[x.n]) : 0.f;
+        if (x.live && !e.xs) e.xg[x.o] = y;
         const float sq = sum16(hn * hn);
-        if (live && c == 0) e.ss_out[(size_t)r * e.ss_ld + tile] = sq;
+        if (x.live && c == 0) e.ss_out[(size_t)x.r * e.ss_ld + x.tile] = sq;
       }
-      if (to_xs) xs_store(e.xs, r, n, e.xs_ks, y);
+      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, e.xs_stack, y);
     } else {
-      if (valid) e.out[o] = v;
-      // padding subtiles past ceil(V / 16) hold no statistics
-      lm_subtile_stats(v, valid, live && tile < e.G, n, e.row0 + r, tile, e.G, e.G1, e.gamma,
-                       e.V, e.tmode, e.invT, e.q, e.pst, e.pidx, e.qst);
+      if (x.valid) e.out[x.o] = v;
+      const float qv = pre ? p0 : lm_item_q(e, x);
+      // one statistics unit per work group and row (its nt tiles)
+      lm_unit_stats(v, x.valid, x.live, x.n, e.row0 + x.r, x.tile / nt, nt, e.G, e.G1, e.gamma,
+                    e.tmode, e.invT, qv, e.pst, e.pidx, e.qst);
     }
   }
 }
@@ -106,23 +179,29 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
 // ---------------------------------------------------------------- MFMA GEMM
 // bf16 weights in MFMA tiles (layout in internal.h); the activations come
 // already split into three bf16 terms in A-fragment order (xs_index), so a
-// k-step is NT weight fragments + 3 activation fragments per 16-row tile
-// and 3 NT MFMAs, with no vector ALU work.  MTW = 16-row M tiles per wave,
+// k-step is NT weight fragments + FPT activation fragments per row tile and
+// FPT * NT MFMAs, with no vector ALU work.  STACK selects the stacked
+// packing (five rows, all three terms in one fragment), which cuts the
+// activation loads and MFMAs of a B = 1 pass by three; the plain packing
+// (16 rows, three fragments) serves many rows.  MTW = row tiles per wave,
 // MG row groups, NT column tiles per work group; the number of k-groups
 // KG = waves / MG is a launch parameter.
 // The weight stream is latency bound unless each CU keeps well over 100 KiB
 // of loads in flight, so waves run two per SIMD and hold deep register
-// pipelines: a k-step stage costs 4 * NT VGPRs of weights and 12 * MTW of
-// activations, and PIPE stages stay within the register budget.
-template <int MTW, int NT>
+// pipelines: a k-step stage costs 4 * NT VGPRs of weights and 4 * FPT * MTW
+// of activations, and PIPE stages stay within the register budget.
+template <int MTW, int NT, bool STACK>
 struct MfmaPipe {
-  static constexpr int stage = 4 * NT + 12 * MTW;
-  static constexpr int value = MTW >= 3 ? 2 : (SV_PIPE_VGPRS / stage < 2 ? 2 : SV_PIPE_VGPRS / stage);
+  static constexpr int stage = 4 * NT + 4 * (STACK ? 1 : 3) * MTW;
+  static constexpr int value = (!STACK && MTW >= 3) ? 2 : (SV_PIPE_VGPRS / stage < 2 ? 2 : SV_PIPE_VGPRS / stage);
 };
 
-template <int MTW, int MG, int NT>
+template <int MTW, int MG, int NT, bool STACK>
 __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
-  constexpr int PIPE = MfmaPipe<MTW, NT>::value;
+  constexpr int PIPE = MfmaPipe<MTW, NT, STACK>::value;
+  constexpr int FPT = STACK ? 1 : 3;            // A fragments per row tile and k-step
+  constexpr int RPT = STACK ? kStackRows : 16;  // rows per row tile
+  constexpr int TERMS = STACK ? 3 : 1;          // LDS planes per row before the term sum
   extern __shared__ float smem[];
   __shared__ float sh_inv[256];
   const int lane = threadIdx.x & 63;
@@ -133,7 +212,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
   const int c0 = blockIdx.x * NT;                 // first 16-column tile
   const int M = a.M, KS = a.KS;
   const int mt0 = mg * MTW;
-  const int MT = (M + 15) / 16;
+  const int MT = (M + RPT - 1) / RPT;
   // this work group's column block: one contiguous span of KS * NT KiB
   const bf16x8* Wg = reinterpret_cast<const bf16x8*>(a.W) + (size_t)blockIdx.x * KS * NT * 64 + lane;
 
@@ -143,22 +222,32 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // A fragments of each row tile; lanes of rows past M (and tiles past the
-  // last) read the last real row, so every load is uniform and touches only
-  // cache lines the real rows use.  Their products land in output rows that
-  // are never stored.
+  // A fragments of each row tile.  Lanes whose A-row holds no real row
+  // (past M, or A-row 15 of a stacked tile) read a real row of the same
+  // term instead, so every load touches only written memory; their
+  // products land in accumulator rows that are never stored.  Tiles past
+  // the last read the last one and are not computed.
   const bf16x8* xsrow[MTW];
 #pragma unroll
   for (int i = 0; i < MTW; ++i) {
     const int mt = min(mt0 + i, MT - 1);
-    const int rows = min(16, M - mt * 16);
-    const int al = (lane & 48) + min(lane & 15, rows - 1);
-    xsrow[i] = reinterpret_cast<const bf16x8*>(a.XS) + (size_t)mt * (KS + 1) * 3 * 64 + al;
+    const int rows = min(RPT, M - mt * RPT);
+    const int ar = lane & 15;
+    int al;
+    if (STACK) {
+      const int p = min(ar / kStackRows, 2);
+      al = (lane & 48) + p * kStackRows + min(ar - p * kStackRows, rows - 1);
+    } else {
+      al = (lane & 48) + min(ar, rows - 1);
+    }
+    xsrow[i] = reinterpret_cast<const bf16x8*>(a.XS) + (size_t)mt * (KS + 1) * FPT * 64 + al;
   }
-  const bool wave_live = (mt0 * 16) < M;
+  const bool wave_live = mt0 < MT;
+  float pv[8];
+  epi_prefetch(a.e, M, c0, NT, nwaves, pv);
 
   bf16x8 bq[PIPE][NT];
-  bf16x8 xq[PIPE][MTW][3];
+  bf16x8 xq[PIPE][MTW][FPT];
 
   // kw: weight k-step; ka: activation k-step (KS = the all-zero step)
 #define SV_LOAD(u, kw, ka)                                                       \
@@ -166,17 +255,17 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
     const bf16x8* wp = Wg + (size_t)(kw) * NT * 64;                              \
     _Pragma("unroll") for (int t = 0; t < NT; ++t) bq[u][t] = wp[t * 64];        \
     _Pragma("unroll") for (int i = 0; i < MTW; ++i) {                            \
-      const bf16x8* xp = xsrow[i] + (size_t)(ka) * 3 * 64;                       \
-      _Pragma("unroll") for (int p = 0; p < 3; ++p) xq[u][i][p] = xp[p * 64];    \
+      const bf16x8* xp = xsrow[i] + (size_t)(ka) * FPT * 64;                     \
+      _Pragma("unroll") for (int p = 0; p < FPT; ++p) xq[u][i][p] = xp[p * 64];  \
     }                                                                            \
   }
 
 #define SV_COMPUTE(u)                                                            \
   {                                                                              \
     _Pragma("unroll") for (int i = 0; i < MTW; ++i) {                            \
-      if ((mt0 + i) * 16 < M) {                                                  \
+      if (mt0 + i < MT) {                                                        \
         _Pragma("unroll") for (int t = 0; t < NT; ++t) {                         \
-          _Pragma("unroll") for (int p = 0; p < 3; ++p)                          \
+          _Pragma("unroll") for (int p = 0; p < FPT; ++p)                        \
             acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xq[u][i][p], bq[u][t], \
                                                                 acc[i][t], 0, 0, 0); \
         }                                                                        \
@@ -205,6 +294,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
       for (int u = 0; u < PIPE; ++u) {
         SV_COMPUTE(u);
+
         const int kk = k + (it + u + PIPE) * KG;
         SV_LOAD(u, min(kk, klast), kk <= klast ? kk : KS);
         __builtin_amdgcn_sched_barrier(0);
@@ -214,8 +304,9 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 #undef SV_LOAD
 #undef SV_COMPUTE
 
-  // k-group partial tiles into LDS red[KG][M][ldr], then summed in k-group
-  // order into red[0].  C layout of 16x16 MFMA: lane holds rows
+  // Partial tiles into LDS red[KG][M][TERMS][ldr] (k-group, row, term),
+  // then summed in a fixed order (terms lo + mid + hi, then k-groups in
+  // order) into res[M][ldr].  C layout of 16x16 MFMA: lane holds A-rows
   // 4*(lane/16)+j of column lane%16.
   constexpr int NCOL = NT * kSub;
   constexpr int ldr = NCOL + 1;
@@ -227,11 +318,33 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = (mt0 + i) * 16 + crow + j;
-        if (row < M) red[((size_t)kg * M + row) * ldr + t * kSub + ccol] = acc[i][t][j];
+        const int ar = crow + j;
+        int row, p = 0;
+        if (STACK) {
+          p = ar / kStackRows;
+          row = (mt0 + i) * kStackRows + (ar - p * kStackRows);
+          if (p > 2) row = M;                     // A-row 15: no row
+        } else {
+          row = (mt0 + i) * 16 + ar;
+        }
+        if (mt0 + i < MT && row < M)
+          red[(((size_t)kg * M + row) * TERMS + p) * ldr + t * kSub + ccol] = acc[i][t][j];
       }
   __syncthreads();
-  if (KG > 1) {
+  float* res = red;
+  if (STACK) {
+    res = red + (size_t)KG * M * TERMS * ldr;
+    for (int idx = threadIdx.x; idx < M * NCOL; idx += blockDim.x) {
+      const int r = idx / NCOL, col = idx - r * NCOL;
+      float v = 0.f;
+      for (int q = 0; q < KG; ++q) {
+        const float* pr = red + (((size_t)q * M + r) * TERMS) * ldr + col;
+        v += (pr[2 * ldr] + pr[ldr]) + pr[0];
+      }
+      res[r * ldr + col] = v;
+    }
+    __syncthreads();
+  } else if (KG > 1) {
     for (int idx = threadIdx.x; idx < M * NCOL; idx += blockDim.x) {
       const int r = idx / NCOL, col = idx - r * NCOL;
       float v = 0.f;
@@ -240,7 +353,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
     }
     __syncthreads();
   }
-  run_epilogue(a.e, M, c0, NT, red, ldr, sh_inv, nwaves);
+  run_epilogue(a.e, M, c0, NT, res, ldr, sh_inv, nwaves, pv);
 }
 
 // ---------------------------------------------------------------- vector-FMA GEMM
@@ -279,6 +392,8 @@ __global__ __launch_bounds__(kFmaThreads) void k_gemm_fma(GemmArgs a) {
   const WT* W = reinterpret_cast<const WT*>(a.W) + (size_t)g * kGroupCols + cg;
   float* res = smem;                       // [M][ldr]
   float* red = smem + M * ldr;             // [4][8][ldr]
+  float pv[8];
+  epi_prefetch(a.e, M, g * 4, 4, kFmaThreads / kWave, pv);
 
   for (int m0 = 0; m0 < M; m0 += 8) {
     const int mr = min(8, M - m0);
@@ -326,7 +441,7 @@ __global__ __launch_bounds__(kFmaThreads) void k_gemm_fma(GemmArgs a) {
     }
     __syncthreads();
   }
-  run_epilogue(a.e, M, g * 4, 4, res, ldr, sh_inv, kFmaThreads / kWave);
+  run_epilogue(a.e, M, g * 4, 4, res, ldr, sh_inv, kFmaThreads / kWave, pv);
 }
 
 // ---------------------------------------------------------------- host side
@@ -338,7 +453,7 @@ int mfma_block_tiles(int Np) {
   return nt;
 }
 
-GemmPlan plan_gemm(int path, int M, const Mat& m) {
+GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack) {
   GemmPlan p;
   p.path = path;
   const int tiles = m.Np / kSub;
@@ -349,19 +464,30 @@ GemmPlan plan_gemm(int path, int M, const Mat& m) {
     p.lds = ((size_t)M * (kGroupCols + 1) + 4 * 8 * (kGroupCols + 1)) * sizeof(float);
     return p;
   }
-  const int MT = (M + 15) / 16;
-  if (MT <= 2) { p.mtw = MT; p.mg = 1; }
-  else if (MT <= 4) { p.mtw = 2; p.mg = 2; }
-  else if (MT <= 6) { p.mtw = 3; p.mg = 2; }
-  else if (MT <= 8) { p.mtw = 4; p.mg = 2; }
-  else if (MT <= 12) { p.mtw = 3; p.mg = 4; }
-  else { p.mtw = 4; p.mg = 4; }
+  p.stack = stack;
+  if (p.stack) {
+    p.mtw = (M + kStackRows - 1) / kStackRows;
+    p.mg = 1;
+  } else {
+    const int MT = (M + 15) / 16;
+    if (MT <= 2) { p.mtw = MT; p.mg = 1; }
+    else if (MT <= 4) { p.mtw = 2; p.mg = 2; }
+    else if (MT <= 6) { p.mtw = 3; p.mg = 2; }
+    else if (MT <= 8) { p.mtw = 4; p.mg = 2; }
+    else if (MT <= 12) { p.mtw = 3; p.mg = 4; }
+    else { p.mtw = 4; p.mg = 4; }
+  }
   p.nt = m.nt;
   p.blocks = tiles / p.nt;
   // k-groups: about SV_TARGET_WAVES waves in all, within the work-group
-  // size, the k-steps and 64 KiB of LDS for the k-group tiles
+  // size, the k-steps and 64 KiB of LDS for the k-group tiles (plus the
+  // summed tile of the stacked packing)
   const int max_waves = 8;
-  auto lds_of = [&](int kg) { return (size_t)kg * M * (p.nt * kSub + 1) * sizeof(float); };
+  const size_t ldr = (size_t)p.nt * kSub + 1;
+  auto lds_of = [&](int kg) {
+    return p.stack ? ((size_t)kg * M * 3 + M) * ldr * sizeof(float)
+                   : (size_t)kg * M * ldr * sizeof(float);
+  };
   p.kg = 1;
   while (p.mg * p.kg * 2 <= max_waves && (size_t)p.blocks * p.mg * p.kg * 2 <= SV_TARGET_WAVES &&
          p.kg * 2 <= KS && lds_of(p.kg * 2) <= 65536)
@@ -370,33 +496,44 @@ GemmPlan plan_gemm(int path, int M, const Mat& m) {
   return p;
 }
 
-template <int MTW, int MG>
-static hipError_t launch_mfma_mg(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+// Launches go through hipExtLaunchKernelGGL so that, when timing is on, the
+// two events take the kernel's own start and end timestamps (no extra
+// packets between kernels).
+template <int MTW, int MG, bool STACK>
+static hipError_t launch_mfma_mg(const GemmPlan& p, const GemmArgs& a, hipStream_t st,
+                                 hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(p.blocks), block(64 * p.mg * p.kg);
   switch (p.nt) {
-    case 1: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 1>), grid, block, p.lds, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 2>), grid, block, p.lds, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm_mfma<MTW, MG, 4>), grid, block, p.lds, st, a); break;
+    case 1: hipExtLaunchKernelGGL((k_gemm_mfma<MTW, MG, 1, STACK>), grid, block, p.lds, st, e0, e1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((k_gemm_mfma<MTW, MG, 2, STACK>), grid, block, p.lds, st, e0, e1, 0, a); break;
+    default: hipExtLaunchKernelGGL((k_gemm_mfma<MTW, MG, 4, STACK>), grid, block, p.lds, st, e0, e1, 0, a); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t st, hipEvent_t e0,
+                       hipEvent_t e1) {
   if (p.path == PATH_FMA_F32 || p.path == PATH_FMA_BF16) {
     const dim3 grid(p.blocks), block(kFmaThreads);
     if (p.path == PATH_FMA_F32)
-      hipLaunchKernelGGL((k_gemm_fma<float>), grid, block, p.lds, st, a);
+      hipExtLaunchKernelGGL((k_gemm_fma<float>), grid, block, p.lds, st, e0, e1, 0, a);
     else
-      hipLaunchKernelGGL((k_gemm_fma<uint16_t>), grid, block, p.lds, st, a);
+      hipExtLaunchKernelGGL((k_gemm_fma<uint16_t>), grid, block, p.lds, st, e0, e1, 0, a);
     return hipGetLastError();
   }
-  if (p.mg == 1) return p.mtw == 1 ? launch_mfma_mg<1, 1>(p, a, st) : launch_mfma_mg<2, 1>(p, a, st);
+  if (p.stack)
+    return p.mtw == 1 ? launch_mfma_mg<1, 1, true>(p, a, st, e0, e1)
+                      : launch_mfma_mg<2, 1, true>(p, a, st, e0, e1);
+  if (p.mg == 1)
+    return p.mtw == 1 ? launch_mfma_mg<1, 1, false>(p, a, st, e0, e1)
+                      : launch_mfma_mg<2, 1, false>(p, a, st, e0, e1);
   if (p.mg == 2) {
-    if (p.mtw == 2) return launch_mfma_mg<2, 2>(p, a, st);
-    if (p.mtw == 3) return launch_mfma_mg<3, 2>(p, a, st);
-    return launch_mfma_mg<4, 2>(p, a, st);
+    if (p.mtw == 2) return launch_mfma_mg<2, 2, false>(p, a, st, e0, e1);
+    if (p.mtw == 3) return launch_mfma_mg<3, 2, false>(p, a, st, e0, e1);
+    return launch_mfma_mg<4, 2, false>(p, a, st, e0, e1);
   }
-  return p.mtw == 3 ? launch_mfma_mg<3, 4>(p, a, st) : launch_mfma_mg<4, 4>(p, a, st);
+  return p.mtw == 3 ? launch_mfma_mg<3, 4, false>(p, a, st, e0, e1)
+                    : launch_mfma_mg<4, 4, false>(p, a, st, e0, e1);
 }
 
 }  // namespace sv

@@ -7,6 +7,8 @@
 
 #include <vector>
 
+#include "common.h"
+
 namespace sv {
 
 enum WeightFormat { FMT_ROWMAJOR_F32 = 0, FMT_ROWMAJOR_BF16 = 1, FMT_MFMA_BF16 = 2 };
@@ -53,7 +55,7 @@ struct EpiArgs {
   int* pidx = nullptr;        // [rows][G]   (greedy)
   float* qst = nullptr;       // [B*gamma][G][2]
   const float* q = nullptr;   // [B][gamma][V]
-  int G = 0;                  // statistics subtiles per row
+  int G = 0;                  // row stride of the statistics (units, even)
   int G1 = 1, gamma = 0, V = 0;
   int row0 = 0;               // global index of this launch's first row
   int tmode = 0;              // 0 greedy, 1 T == 1, 2 general T
@@ -64,6 +66,7 @@ struct EpiArgs {
   // block, h for the LM head
   uint16_t* xs = nullptr;
   int xs_ks = 0;
+  bool xs_stack = false;      // stacked packing (xs_index)
 };
 
 struct GemmArgs {
@@ -82,16 +85,32 @@ struct GemmPlan {
   int path = PATH_MFMA;
   int mtw = 1, mg = 1, kg = 1;   // M tiles per wave, row groups, k-groups
   int nt = 4;                    // 16-column tiles per work group
+  bool stack = false;            // stacked activation packing (MFMA)
   int blocks = 0;                // work groups
   size_t lds = 0;                // dynamic LDS bytes
 };
 
-GemmPlan plan_gemm(int path, int M, const Mat& m);
-hipError_t launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t st);
+// The MFMA path packs the split activations of up to 10 rows stacked (two
+// five-row tiles, one fragment per k-step each); more rows use the plain
+// packing, which needs no more fragments from 11 rows on.
+inline bool xs_stacked(int M) { return M <= 10; }
+
+// Bytes of one split-activation buffer of M rows and ks k-steps (plus the
+// all-zero step): one 1 KiB fragment per row tile and k-step stacked, three
+// plain.
+inline size_t xs_bytes(int M, int ks) {
+  return xs_stacked(M) ? (size_t)((M + kStackRows - 1) / kStackRows) * (ks + 1) * 1024
+                       : (size_t)((M + 15) / 16) * (ks + 1) * 3 * 1024;
+}
+
+GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack);
+// e0 / e1: null, or events that take the launch's start and end timestamps.
+hipError_t launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t st, hipEvent_t e0,
+                       hipEvent_t e1);
 
 // Sampling-side launchers (sample.hip).
 struct SampleArgs {
-  int B = 0, gamma = 0, V = 0, G = 0;
+  int B = 0, gamma = 0, V = 0, G = 0, Gu = 0;   // G: statistics row stride, Gu: units
   int M = 0;                  // B * (gamma + 1)
   const float* logits = nullptr; int ldl = 0;
   const float* q = nullptr;
@@ -111,7 +130,8 @@ struct SampleArgs {
 // Copies hidden into h, forms xg = h * gain0 and its per-16-column sums of
 // squares; with xs0 non-null also writes the first GEMM's split input (xg,
 // or h when there is no MLP block) and clears the zero k-step of each of
-// the split buffers xs0 (ks0 k-steps) and xs1 (ks1 k-steps).
+// the split buffers xs0 (ks0 k-steps) and xs1 (ks1 k-steps), packed as
+// xs_stacked(M) says.
 hipError_t launch_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
                        const float* gain0, int M, int d, int ld, uint16_t* xs0, int ks0,
                        uint16_t* xs1, int ks1, hipStream_t st);

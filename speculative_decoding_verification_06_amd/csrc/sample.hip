@@ -1,14 +1,16 @@
 // The acceptance rule over the vocabulary, after the target pass.
 //
-//   rowstats : combine per-tile (max, sum exp) of each logits row into
-//              softmax(l / T), and the per-tile sums of each draft row into
+//   rowstats : combine per-unit (max, sum exp) of each logits row (one
+//              unit per LM-head work group) into softmax(l / T), and the
+//              per-unit sums of each draft row into
 //              q' = q^(1/T) / sum ("Speculative decoding" pigeon guide, When it
 //              breaks: the same temperature / top-p on p and q)
 //   topp     : nucleus of each row by an 8-bit-digit radix select on an
 //              order-preserving key, with masses in 2^-40 fixed point so the
 //              histogram sums are exact and order independent
 //   decide   : ratio test r * q'(x) < p'(x) per drafted position, first
-//              rejection per sequence (lattice-ai-eng explainer, acceptance
+//              rejection per sequence, then the chunk sums of the resample
+//              row (lattice-ai-eng explainer, acceptance
 //              rule; pigeon guide, How it works, step 3); at T = 0 the draft
 //              is compared to the argmax
 //   resample : inverse CDF over max(0, p' - q') at the first rejection, or
@@ -60,17 +62,16 @@ __device__ __forceinline__ float q_prime(const float* ri, float qv, int v, int t
 // ---------------------------------------------------------------- prep
 // h = hidden (zero-padded rows of ld), xg = h * gain0, the sum of squares of
 // h per 16-column subtile, and the split A fragments of the first GEMM's
-// input.  Work group (0, m) with m < ceil(M / 16) also clears the zero
-// k-step of row tile m in both split buffers.
-__device__ __forceinline__ void clear_zero_step(uint16_t* xs, int mt, int ks, int lane) {
-  uint4* f = reinterpret_cast<uint4*>(xs + ((size_t)mt * (ks + 1) + ks) * 3 * 512);
-#pragma unroll
-  for (int p = 0; p < 3; ++p) f[p * 64 + lane] = make_uint4(0u, 0u, 0u, 0u);
+// input.  Work group (0, m) with m < the number of row tiles also clears
+// the zero k-step of row tile m in both split buffers.
+__device__ __forceinline__ void clear_zero_step(uint16_t* xs, int mt, int ks, int fpt, int lane) {
+  uint4* f = reinterpret_cast<uint4*>(xs + ((size_t)mt * (ks + 1) + ks) * fpt * 512);
+  for (int p = 0; p < fpt; ++p) f[p * 64 + lane] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __global__ void k_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
                        const float* gain0, int d, int ld, uint16_t* xs0, int ks0, uint16_t* xs1,
-                       int ks1) {
+                       int ks1, bool stacked) {
   const int lane = threadIdx.x, g = blockIdx.x, m = blockIdx.y;
   const int n = g * kGroupCols + lane;
   const float v = n < d ? hidden[(size_t)m * d + n] : 0.f;
@@ -83,10 +84,11 @@ __global__ void k_prep(float* h, float* xg, float* ss, int ss_ld, const float* h
     if ((lane & 15) == 0) ss[(size_t)m * ss_ld + g * 4 + (lane >> 4)] = sq;
   }
   if (xs0) {
-    if (n < kKStep * ks0) xs_store(xs0, m, n, ks0, x);
-    if (g == 0 && m * 16 < gridDim.y) {
-      clear_zero_step(xs0, m, ks0, lane);
-      if (xs1) clear_zero_step(xs1, m, ks1, lane);
+    if (n < kKStep * ks0) xs_store(xs0, m, n, ks0, stacked, x);
+    const int rpt = stacked ? kStackRows : 16, fpt = stacked ? 1 : 3;
+    if (g == 0 && m * rpt < gridDim.y) {
+      clear_zero_step(xs0, m, ks0, fpt, lane);
+      if (xs1) clear_zero_step(xs1, m, ks1, fpt, lane);
     }
   }
 }
@@ -95,55 +97,96 @@ hipError_t launch_prep(float* h, float* xg, float* ss, int ss_ld, const float* h
                        const float* gain0, int M, int d, int ld, uint16_t* xs0, int ks0,
                        uint16_t* xs1, int ks1, hipStream_t st) {
   hipLaunchKernelGGL(k_prep, dim3(ld / kGroupCols, M), dim3(kWave), 0, st, h, xg, ss, ss_ld,
-                     hidden, gain0, d, ld, xs0, ks0, xs1, ks1);
+                     hidden, gain0, d, ld, xs0, ks0, xs1, ks1, xs_stacked(M));
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- subtile stats from given logits
+// ---------------------------------------------------------------- unit stats from given logits
+// One 64-lane work group per (row, unit of four 16-column tiles).
 __global__ void k_tile_stats(SampleArgs a) {
-  const int r = blockIdx.y, lane = threadIdx.x;
-  const int tile = blockIdx.x * 4 + (lane >> 4);
-  const int n = tile * kSub + (lane & 15);
-  const bool live = tile < a.G;
-  const bool valid = live && n < a.V;
+  const int r = blockIdx.y, lane = threadIdx.x, unit = blockIdx.x;
+  const int n = unit * 4 * kSub + lane;
+  const bool valid = n < a.V;
   const float l = valid ? a.logits[(size_t)r * a.ldl + n] : 0.f;
-  lm_subtile_stats(l, valid, live, n, r, tile, a.G, a.gamma + 1, a.gamma, a.V, a.tmode, a.invT,
-                   a.q, a.pst, a.pidx, a.qst);
+  const int b = r / (a.gamma + 1), i = r - b * (a.gamma + 1);
+  const float qv = (valid && a.tmode != 0 && i < a.gamma)
+                       ? a.q[((size_t)b * a.gamma + i) * a.V + n] : 0.f;
+  lm_unit_stats(l, valid, true, n, r, unit, 4, a.G, a.gamma + 1, a.gamma, a.tmode, a.invT, qv,
+                a.pst, a.pidx, a.qst);
 }
 
 hipError_t launch_tile_stats(const SampleArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_tile_stats, dim3((a.G + 3) / 4, a.M), dim3(kWave), 0, st, a);
+  hipLaunchKernelGGL(k_tile_stats, dim3(a.Gu, a.M), dim3(kWave), 0, st, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- row stats
-constexpr int kRowThreads = 256;
+// One work group per row combines the row's G subtile statistics (G is
+// even, so each 16-byte load carries two subtiles; padding subtiles hold
+// neutral statistics).  Every thread issues its loads in batches of 8
+// before merging, so a row costs one or two memory round trips.  T > 0:
+// (max, 1 / Z) of p, or of q' for draft rows; T == 0: the argmax of p (in
+// RI_M, as int bits).
+constexpr int kRowThreads = 512;
+constexpr int kRowBatch = 8;
 
 __global__ __launch_bounds__(kRowThreads) void k_rowstats(SampleArgs a) {
   __shared__ float sh_m[kRowThreads / kWave], sh_s[kRowThreads / kWave];
+  __shared__ int sh_i[kRowThreads / kWave];
   const int row = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool isq = row >= a.M;
-  const float* st = isq ? a.qst + (size_t)(row - a.M) * a.G * 2 : a.pst + (size_t)row * a.G * 2;
+  const size_t srow = isq ? (size_t)(row - a.M) : (size_t)row;
+  const float4* st = reinterpret_cast<const float4*>((isq ? a.qst : a.pst) + srow * a.G * 2);
+  const int2* sidx = reinterpret_cast<const int2*>(a.pidx + srow * a.G);
+  const int n2 = a.G / 2;
+  const bool greedy = a.tmode == 0;
   const bool plain_sum = isq && a.tmode == 1;
   const float it = isq ? 1.f : a.invT;
-  float m = plain_sum ? 0.f : -INFINITY, s = 0.f;
-  for (int t = threadIdx.x; t < a.G; t += kRowThreads) {
-    if (plain_sum) s += st[2 * t + 1];
-    else lse_merge(m, s, st[2 * t], st[2 * t + 1], it);
+  float m = (plain_sum || greedy) ? (greedy ? -INFINITY : 0.f) : -INFINITY, s = 0.f;
+  int idx = INT_MAX;
+  for (int t0 = threadIdx.x; t0 < n2; t0 += kRowThreads * kRowBatch) {
+    float4 v[kRowBatch];
+    int2 ix[kRowBatch];
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) {
+      const int t = t0 + u * kRowThreads;
+      v[u] = t < n2 ? st[t] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+      if (greedy) ix[u] = t < n2 ? sidx[t] : make_int2(INT_MAX, INT_MAX);
+      if (2 * t + 1 >= a.Gu) { v[u].z = -INFINITY; v[u].w = 0.f; ix[u].y = INT_MAX; }   // stride padding
+    }
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) {
+      if (greedy) {
+        if (v[u].x > m || (v[u].x == m && ix[u].x < idx)) { m = v[u].x; idx = ix[u].x; }
+        if (v[u].z > m || (v[u].z == m && ix[u].y < idx)) { m = v[u].z; idx = ix[u].y; }
+      } else if (plain_sum) {
+        s += v[u].y + v[u].w;
+      } else {
+        lse_merge(m, s, v[u].x, v[u].y, it);
+        lse_merge(m, s, v[u].z, v[u].w, it);
+      }
+    }
   }
-  if (plain_sum) s = wave_sum(s);
+  if (greedy) wave_argmax(m, idx);
+  else if (plain_sum) s = wave_sum(s);
   else wave_lse(m, s, it);
-  if (lane == 0) { sh_m[wave] = m; sh_s[wave] = s; }
+  if (lane == 0) { sh_m[wave] = m; sh_s[wave] = s; sh_i[wave] = idx; }
   __syncthreads();
   if (threadIdx.x == 0) {
     float mm = sh_m[0], ss = sh_s[0];
+    int ii = sh_i[0];
     for (int w = 1; w < kRowThreads / kWave; ++w) {
-      if (plain_sum) ss += sh_s[w];
-      else lse_merge(mm, ss, sh_m[w], sh_s[w], it);
+      if (greedy) {
+        if (sh_m[w] > mm || (sh_m[w] == mm && sh_i[w] < ii)) { mm = sh_m[w]; ii = sh_i[w]; }
+      } else if (plain_sum) {
+        ss += sh_s[w];
+      } else {
+        lse_merge(mm, ss, sh_m[w], sh_s[w], it);
+      }
     }
     float* ri = a.rowinfo + (size_t)row * kRowInfo;
-    ri[RI_M] = mm;
-    ri[RI_INVZ] = 1.0f / ss;
+    ri[RI_M] = greedy ? __int_as_float(ii) : mm;
+    ri[RI_INVZ] = greedy ? 0.f : 1.0f / ss;
     ri[RI_THR] = 0.f;
     ri[RI_TIE] = 0.f;
     ri[RI_INVZN] = 1.0f;
@@ -153,6 +196,8 @@ __global__ __launch_bounds__(kRowThreads) void k_rowstats(SampleArgs a) {
 
 // ---------------------------------------------------------------- top-p
 constexpr int kToppThreads = 1024;
+constexpr int kHistCopies = 8;
+constexpr int kToppBatch = 4;            // loads issued before their atomics
 typedef unsigned long long u64;
 
 __device__ __forceinline__ u64 fixed_mass(float p) { return (u64)(p * 0x1.0p40f); }
@@ -183,7 +228,10 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
   const float m = ri[RI_M], invZ = ri[RI_INVZ], invT = a.invT;
   const int tmode = a.tmode, V = a.V;
 
-  __shared__ u64 hist[256];
+  // kHistCopies copies of the 256-bin histogram, lane L adding to copy
+  // L % kHistCopies, so lanes of a wave that share a digit collide at most
+  // 64 / kHistCopies ways in the LDS atomic unit
+  __shared__ u64 hist[kHistCopies * 256];
   __shared__ u64 sh_above, sh_total, sh_zn;
   __shared__ uint32_t sh_prefix;
   __shared__ int sh_found, sh_tie;
@@ -200,19 +248,33 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
   double thr = 0.0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kToppThreads) hist[i] = 0;
+    for (int i = tid; i < kHistCopies * 256; i += kToppThreads) hist[i] = 0;
     __syncthreads();
-    for (int v = tid; v < V; v += kToppThreads) {
-      const float x = src[v];
-      const uint32_t k = key_of(x);
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], mass_of(x));
+    u64* myhist = hist + (lane % kHistCopies) * 256;
+    for (int v0 = tid; v0 < V; v0 += kToppBatch * kToppThreads) {
+      float xs[kToppBatch];
+#pragma unroll
+      for (int u = 0; u < kToppBatch; ++u) {
+        const int v = v0 + u * kToppThreads;
+        xs[u] = v < V ? src[v] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kToppBatch; ++u) {
+        if (v0 + u * kToppThreads < V) {
+          const uint32_t k = key_of(xs[u]);
+          if ((k & pmask) == prefix) atomicAdd(&myhist[(k >> shift) & 255u], mass_of(xs[u]));
+        }
+      }
     }
     __syncthreads();
     if (wave == 0) {
       // lane L holds bins 4L..4L+3; masses of higher bins live in higher lanes
       u64 h[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = hist[4 * lane + j];
+      for (int j = 0; j < 4; ++j) {
+        h[j] = 0;
+        for (int c = 0; c < kHistCopies; ++c) h[j] += hist[c * 256 + 4 * lane + j];
+      }
       const u64 S = h[0] + h[1] + h[2] + h[3];
       u64 inc = S;   // inclusive suffix sum over lanes >= L
 #pragma unroll
@@ -282,76 +344,17 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- decide
-__global__ void k_decide(SampleArgs a) {
-  extern __shared__ int sh_am[];          // [gamma + 1] argmax per row (greedy)
-  __shared__ int sh_bad, sh_first;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int gamma = a.gamma, G1 = gamma + 1;
-  if (tid == 0) { sh_bad = 0; sh_first = INT_MAX; }
-  __syncthreads();
-  for (int i = tid; i < gamma; i += blockDim.x) {
-    const int x = a.draft[(size_t)b * gamma + i];
-    if (x < 0 || x >= a.V) atomicOr(&sh_bad, 1);
-  }
-  __syncthreads();
-  if (sh_bad) {
-    for (int i = tid; i < G1; i += blockDim.x) a.emitted[(size_t)b * G1 + i] = -1;
-    if (tid == 0) { a.n_acc[b] = -1; a.dec[4 * b] = -1; }
-    return;
-  }
-  int first = INT_MAX;
-  if (a.tmode == 0) {
-    for (int i = wave; i < G1; i += blockDim.x / kWave) {
-      const size_t row = (size_t)b * G1 + i;
-      float v = -INFINITY;
-      int idx = INT_MAX;
-      for (int t = lane; t < a.G; t += kWave) {
-        const float tv = a.pst[2 * (row * a.G + t)];
-        const int ti = a.pidx[row * a.G + t];
-        if (tv > v || (tv == v && ti < idx)) { v = tv; idx = ti; }
-      }
-      wave_argmax(v, idx);
-      if (lane == 0) sh_am[i] = idx;
-    }
-    __syncthreads();
-    for (int i = tid; i < gamma; i += blockDim.x)
-      if (a.draft[(size_t)b * gamma + i] != sh_am[i]) first = min(first, i);
-  } else {
-    for (int i = tid; i < gamma; i += blockDim.x) {
-      const int x = a.draft[(size_t)b * gamma + i];
-      const size_t prow = (size_t)b * G1 + i, qrow = (size_t)b * gamma + i;
-      const float pp = p_prime(a.rowinfo + prow * kRowInfo, a.logits[prow * a.ldl + x], x, a.invT);
-      const float qq = q_prime(a.rowinfo + ((size_t)a.M + qrow) * kRowInfo, a.q[qrow * a.V + x],
-                               x, a.tmode, a.invT);
-      float r, u;
-      row_uniforms(a.seed, b, i, r, u);
-      if (!(r * qq < pp)) first = min(first, i);
-    }
-  }
-  first = wave_min_int(first);
-  if (lane == 0) atomicMin(&sh_first, first);
-  __syncthreads();
-  const int n = min(sh_first, gamma);
-  for (int i = tid; i < G1; i += blockDim.x) {
-    int tok = -1;
-    if (i < n) tok = a.draft[(size_t)b * gamma + i];
-    else if (i == n && a.tmode == 0) tok = sh_am[n];
-    a.emitted[(size_t)b * G1 + i] = tok;
-  }
-  if (tid == 0) { a.n_acc[b] = n; a.dec[4 * b] = n; }
-}
-
-// ---------------------------------------------------------------- resample
+// ---------------------------------------------------------------- resample helpers
 // Token weights are fp32; every prefix sum of the inverse CDF is fp64, so
 // the sampled token is not moved by summation error even when single
 // tokens carry 1e-6 of the mass.
 constexpr int kResThreads = 256;
 constexpr int kResPer = kResampleChunk / kResThreads;   // contiguous ids per thread
 
-// Exclusive prefix over the block in thread order (wave scan, then waves in order).
-__device__ double block_excl_scan_f64(double x, double* lds_waves) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Exclusive prefix over the block in thread order (wave scan, then waves in
+// order); *total receives the block sum.
+__device__ double block_excl_scan_f64(double x, double* lds_waves, double* total = nullptr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   double inc = x;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -364,6 +367,11 @@ __device__ double block_excl_scan_f64(double x, double* lds_waves) {
   __syncthreads();
   double base = 0.0;
   for (int w = 0; w < wave; ++w) base += lds_waves[w];
+  if (total) {
+    double t = 0.0;
+    for (int w = 0; w < nw; ++w) t += lds_waves[w];
+    *total = t;
+  }
   __syncthreads();
   return base + excl_lane;
 }
@@ -373,11 +381,11 @@ struct ResRow {
   const float* l; const float* q; const float* rip; const float* riq;
   bool hasq; bool use_p; int tmode; float invT;
 };
-__device__ __forceinline__ float res_weight(const ResRow& rr, int v, float& pv) {
-  pv = p_prime(rr.rip, rr.l[v], v, rr.invT);
+__device__ __forceinline__ float res_weight_lq(const ResRow& rr, int v, float l, float qv, float& pv) {
+  pv = p_prime(rr.rip, l, v, rr.invT);
   if (!rr.hasq || rr.use_p) return pv;
-  const float qv = q_prime(rr.riq, rr.q[v], v, rr.tmode, rr.invT);
-  return fmaxf(pv - qv, 0.f);
+  const float qq = q_prime(rr.riq, qv, v, rr.tmode, rr.invT);
+  return fmaxf(pv - qq, 0.f);
 }
 
 __device__ __forceinline__ ResRow make_row(const SampleArgs& a, int b, int j, bool use_p) {
@@ -396,88 +404,183 @@ __device__ __forceinline__ ResRow make_row(const SampleArgs& a, int b, int j, bo
   return rr;
 }
 
-__global__ __launch_bounds__(kResThreads) void k_res_chunks(SampleArgs a) {
-  __shared__ double lds_w[4], lds_p[4];
-  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int j = a.dec[4 * b];
-  if (j < 0) return;
-  const ResRow rr = make_row(a, b, j, false);
-  double sw = 0.0, sp = 0.0;
-  const int v0 = c * kResampleChunk + tid * kResPer;
+// The kResPer contiguous logits and q values of this thread in chunk c
+// (16-byte loads when the rows allow them).
+__device__ __forceinline__ void load_chunk(const SampleArgs& a, const ResRow& rr, int c, float (&l)[kResPer],
+                                           float (&qv)[kResPer]) {
+  const int v0 = c * kResampleChunk + threadIdx.x * kResPer;
+  const bool need_q = rr.hasq && !rr.use_p;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(rr.l + v0) |
+                         (need_q ? reinterpret_cast<uintptr_t>(rr.q + v0) : 0)) & 15) == 0;
+  if (v0 + kResPer <= a.V && aligned) {
+    const float4 lv = *reinterpret_cast<const float4*>(rr.l + v0);
+    l[0] = lv.x; l[1] = lv.y; l[2] = lv.z; l[3] = lv.w;
+    if (need_q) {
+      const float4 qq = *reinterpret_cast<const float4*>(rr.q + v0);
+      qv[0] = qq.x; qv[1] = qq.y; qv[2] = qq.z; qv[3] = qq.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < kResPer; ++e) qv[e] = 0.f;
+    }
+    return;
+  }
+#pragma unroll
   for (int e = 0; e < kResPer; ++e) {
     const int v = v0 + e;
-    if (v < a.V) {
-      float pv;
-      sw += (double)res_weight(rr, v, pv);
-      sp += (double)pv;
-    }
-  }
-  const double ew = block_excl_scan_f64(sw, lds_w);
-  const double ep = block_excl_scan_f64(sp, lds_p);
-  if (tid == kResThreads - 1) {
-    a.csum[2 * ((size_t)b * a.nch + c)] = ew + sw;
-    a.csum[2 * ((size_t)b * a.nch + c) + 1] = ep + sp;
+    l[e] = v < a.V ? rr.l[v] : 0.f;
+    qv[e] = (need_q && v < a.V) ? rr.q[v] : 0.f;
   }
 }
 
+// ---------------------------------------------------------------- decide + chunk sums
+// Grid (chunks, B).  Every work group of sequence b takes the same decision
+// (ratio test r * q'(x) < p'(x) per drafted position, first rejection;
+// lattice-ai-eng explainer, acceptance rule; pigeon guide, How it works,
+// step 3; at T = 0 the draft is compared to the argmax), chunk 0 writes
+// it, and each work group then sums the weights of its 1024-token chunk of
+// the resample row: the residual max(0, p' - q') at the first rejection,
+// p' for the bonus slot, plus p' itself for a zero residual (pigeon guide,
+// steps 4-5; scalablesystem article, The Accept/Reject Mechanism).
+__global__ __launch_bounds__(kResThreads) void k_decide_chunks(SampleArgs a) {
+  __shared__ int sh_bad, sh_first;
+  __shared__ double lds_w[kResThreads / kWave], lds_p[kResThreads / kWave];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int gamma = a.gamma, G1 = gamma + 1;
+  if (tid == 0) { sh_bad = 0; sh_first = INT_MAX; }
+  __syncthreads();
+  for (int i = tid; i < gamma; i += blockDim.x) {
+    const int x = a.draft[(size_t)b * gamma + i];
+    if (x < 0 || x >= a.V) { atomicOr(&sh_bad, 1); continue; }
+    const size_t prow = (size_t)b * G1 + i;
+    bool reject;
+    if (a.tmode == 0) {
+      reject = x != __float_as_int(a.rowinfo[prow * kRowInfo + RI_M]);
+    } else {
+      const size_t qrow = (size_t)b * gamma + i;
+      const float pp = p_prime(a.rowinfo + prow * kRowInfo, a.logits[prow * a.ldl + x], x, a.invT);
+      const float qq = q_prime(a.rowinfo + ((size_t)a.M + qrow) * kRowInfo, a.q[qrow * a.V + x], x,
+                               a.tmode, a.invT);
+      float r, u;
+      row_uniforms(a.seed, b, i, r, u);
+      reject = !(r * qq < pp);
+    }
+    if (reject) atomicMin(&sh_first, i);
+  }
+  __syncthreads();
+  if (sh_bad) {
+    if (c == 0) {
+      for (int i = tid; i < G1; i += blockDim.x) a.emitted[(size_t)b * G1 + i] = -1;
+      if (tid == 0) { a.n_acc[b] = -1; a.dec[4 * b] = -1; }
+    }
+    return;
+  }
+  const int n = min(sh_first, gamma);
+  if (c == 0) {
+    for (int i = tid; i < G1; i += blockDim.x) {
+      int tok = -1;
+      if (i < n) tok = a.draft[(size_t)b * gamma + i];
+      else if (i == n && a.tmode == 0)
+        tok = __float_as_int(a.rowinfo[((size_t)b * G1 + n) * kRowInfo + RI_M]);
+      a.emitted[(size_t)b * G1 + i] = tok;
+    }
+    if (tid == 0) { a.n_acc[b] = n; a.dec[4 * b] = n; }
+  }
+  if (a.tmode == 0) return;
+  const ResRow rr = make_row(a, b, n, false);
+  float l[kResPer], qv[kResPer];
+  load_chunk(a, rr, c, l, qv);
+  const int v0 = c * kResampleChunk + tid * kResPer;
+  double sw = 0.0, sp = 0.0;
+#pragma unroll
+  for (int e = 0; e < kResPer; ++e) {
+    if (v0 + e < a.V) {
+      float pv;
+      sw += (double)res_weight_lq(rr, v0 + e, l[e], qv[e], pv);
+      sp += (double)pv;
+    }
+  }
+  double tw, tp;
+  (void)block_excl_scan_f64(sw, lds_w, &tw);
+  (void)block_excl_scan_f64(sp, lds_p, &tp);
+  if (tid == 0) {
+    a.csum[2 * ((size_t)b * a.nch + c)] = tw;
+    a.csum[2 * ((size_t)b * a.nch + c) + 1] = tp;
+  }
+}
+
+// ---------------------------------------------------------------- select
+// Inverse CDF in token-id order: the chunk prefix is a block scan over the
+// chunk sums; the chunk that crosses u * R is rescanned with the same
+// per-thread weights, and the smallest id whose running fp64 prefix
+// exceeds u * R is emitted.
 __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
-  extern __shared__ double sh_C[];         // [nch] running chunk prefix
-  __shared__ double lds_w[4];
-  __shared__ int sh_c, sh_usep, sh_cand, sh_last;
-  __shared__ double sh_base, sh_t;
+  __shared__ double lds_w[kResThreads / kWave];
+  __shared__ int sh_c, sh_cand, sh_last;
+  __shared__ double sh_base, sh_lastbase;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int j = a.dec[4 * b];
   if (j < 0) return;
-  // chunk sums into LDS in parallel ([0, nch) residual, [nch, 2 nch) p'),
-  // then one thread forms the running prefix in chunk order
+  float r, u;
+  row_uniforms(a.seed, b, j, r, u);
   const double* cs = a.csum + 2 * (size_t)b * a.nch;
-  for (int c = tid; c < a.nch; c += kResThreads) {
-    sh_C[c] = cs[2 * c];
-    sh_C[a.nch + c] = cs[2 * c + 1];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double C = 0.0;
-    for (int c = 0; c < a.nch; ++c) { C = C + sh_C[c]; sh_C[c] = C; }
-    int usep = 0;
-    if (!(C > 0.0)) {
-      usep = 1;
-      C = 0.0;
-      for (int c = 0; c < a.nch; ++c) { C = C + sh_C[a.nch + c]; sh_C[c] = C; }
+  if (tid == 0) { sh_c = INT_MAX; sh_cand = INT_MAX; sh_last = -1; sh_base = 0.0; sh_lastbase = 0.0; }
+  // total of the residual chunk sums; the p' sums when it is exactly zero
+  int usep = 0;
+  double total = 0.0;
+  for (int pass = 0; pass < 2; ++pass) {
+    total = 0.0;
+    for (int c0 = 0; c0 < a.nch; c0 += kResThreads) {
+      double t;
+      const double x = c0 + tid < a.nch ? cs[2 * (c0 + tid) + pass] : 0.0;
+      (void)block_excl_scan_f64(x, lds_w, &t);
+      total += t;
     }
-    float r, u;
-    row_uniforms(a.seed, b, j, r, u);
-    const double t = (double)u * C;
-    int cs_ = a.nch - 1;
-    for (int c = 0; c < a.nch; ++c)
-      if (sh_C[c] > t) { cs_ = c; break; }
-    sh_c = cs_;
-    sh_base = cs_ > 0 ? sh_C[cs_ - 1] : 0.0;
-    sh_t = t;
-    sh_usep = usep;
-    sh_cand = INT_MAX;
-    sh_last = -1;
+    usep = pass;
+    if (total > 0.0) break;
+  }
+  const double target = (double)u * total;
+  // the first chunk whose inclusive prefix exceeds the target (the last
+  // chunk when rounding leaves none)
+  double run = 0.0;
+  for (int c0 = 0; c0 < a.nch; c0 += kResThreads) {
+    double t;
+    const bool in = c0 + tid < a.nch;
+    const double x = in ? cs[2 * (c0 + tid) + usep] : 0.0;
+    const double ex = run + block_excl_scan_f64(x, lds_w, &t);
+    if (in && ex + x > target) atomicMin(&sh_c, c0 + tid);
+    if (c0 + tid == a.nch - 1) sh_lastbase = ex;
+    __syncthreads();
+    if (sh_c != INT_MAX) {
+      if (c0 + tid == sh_c) sh_base = ex;
+      break;
+    }
+    run += t;
   }
   __syncthreads();
-  const ResRow rr = make_row(a, b, j, sh_usep != 0);
-  const int v0 = sh_c * kResampleChunk + tid * kResPer;
+  const int c = sh_c != INT_MAX ? sh_c : a.nch - 1;
+  const double base = sh_c != INT_MAX ? sh_base : sh_lastbase;
+  const ResRow rr = make_row(a, b, j, usep != 0);
+  float l[kResPer], qv[kResPer];
+  load_chunk(a, rr, c, l, qv);
+  const int v0 = c * kResampleChunk + tid * kResPer;
+  float w[kResPer];
   double s = 0.0;
+#pragma unroll
   for (int e = 0; e < kResPer; ++e) {
-    const int v = v0 + e;
-    if (v < a.V) { float pv; s += (double)res_weight(rr, v, pv); }
+    float pv;
+    w[e] = v0 + e < a.V ? res_weight_lq(rr, v0 + e, l[e], qv[e], pv) : 0.f;
+    s += (double)w[e];
   }
   const double E = block_excl_scan_f64(s, lds_w);
-  const double base = sh_base, t = sh_t;
-  double run = 0.0;
+  double acc = 0.0;
   int cand = INT_MAX, last_pos = -1;
+#pragma unroll
   for (int e = 0; e < kResPer; ++e) {
     const int v = v0 + e;
-    if (v >= a.V) break;
-    float pv;
-    const float w = res_weight(rr, v, pv);
-    run += (double)w;
-    if (w > 0.f) last_pos = v;
-    if (base + (E + run) > t) { cand = v; break; }
+    if (v >= a.V || cand != INT_MAX) continue;
+    acc += (double)w[e];
+    if (w[e] > 0.f) last_pos = v;
+    if (base + (E + acc) > target) cand = v;
   }
   cand = wave_min_int(cand);
   if ((tid & 63) == 0) atomicMin(&sh_cand, cand);
@@ -512,16 +615,12 @@ hipError_t launch_dump_probs(const SampleArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------- sequencing
 hipError_t launch_sampling(const SampleArgs& a, hipStream_t st) {
   const int qrows = a.B * a.gamma;
-  if (a.tmode != 0) {
-    hipLaunchKernelGGL(k_rowstats, dim3(a.M + qrows), dim3(kRowThreads), 0, st, a);
-    if (a.top_p < 1.0f)
-      hipLaunchKernelGGL(k_topp, dim3(a.M + qrows), dim3(kToppThreads), 0, st, a);
-  }
-  hipLaunchKernelGGL(k_decide, dim3(a.B), dim3(256), (a.gamma + 1) * sizeof(int), st, a);
-  if (a.tmode != 0) {
-    hipLaunchKernelGGL(k_res_chunks, dim3(a.nch, a.B), dim3(kResThreads), 0, st, a);
-    hipLaunchKernelGGL(k_res_select, dim3(a.B), dim3(kResThreads), 2 * a.nch * sizeof(double), st, a);
-  }
+  hipLaunchKernelGGL(k_rowstats, dim3(a.tmode != 0 ? a.M + qrows : a.M), dim3(kRowThreads), 0, st, a);
+  if (a.tmode != 0 && a.top_p < 1.0f)
+    hipLaunchKernelGGL(k_topp, dim3(a.M + qrows), dim3(kToppThreads), 0, st, a);
+  hipLaunchKernelGGL(k_decide_chunks, dim3(a.tmode != 0 ? a.nch : 1, a.B), dim3(kResThreads), 0, st, a);
+  if (a.tmode != 0)
+    hipLaunchKernelGGL(k_res_select, dim3(a.B), dim3(kResThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -145,7 +145,8 @@ def test_repeat_calls_are_bit_identical():
 RULE_CASES = [
     (4, 4, 512, 1.0, 1.0), (8, 8, 5000, 0.7, 0.9), (3, 6, 1000, 0.0, 1.0),
     (16, 2, 130, 1.3, 0.6), (6, 0, 300, 1.0, 1.0), (5, 3, 64, 1.0, 0.5), (7, 3, 1, 1.0, 1.0),
-    (2, 5, 70000, 0.9, 0.95),
+    (2, 5, 70000, 0.9, 0.95), (1, 4, 32000, 1.0, 1.0), (1, 5, 128256, 1.0, 1.0),
+    (2, 3, 128256, 0.7, 0.9), (1, 2, 600000, 1.0, 1.0), (3, 4, 129, 0.0, 1.0),
 ]
 
 
