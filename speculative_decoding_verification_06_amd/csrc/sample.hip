@@ -197,7 +197,8 @@ __global__ __launch_bounds__(kRowThreads) void k_rowstats(SampleArgs a) {
 // ---------------------------------------------------------------- top-p
 constexpr int kToppThreads = 1024;
 constexpr int kHistCopies = 8;
-constexpr int kToppBatch = 4;            // loads issued before their atomics
+constexpr int kToppBatch = 8;            // loads issued before their atomics
+constexpr int kTieCap = 64;              // tied keys ordered by one thread
 typedef unsigned long long u64;
 
 __device__ __forceinline__ u64 fixed_mass(float p) { return (u64)(p * 0x1.0p40f); }
@@ -234,12 +235,22 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
   __shared__ u64 hist[kHistCopies * 256];
   __shared__ u64 sh_above, sh_total, sh_zn;
   __shared__ uint32_t sh_prefix;
-  __shared__ int sh_found, sh_tie;
+  __shared__ int sh_found, sh_tie, sh_nt;
+  __shared__ int tie_id[kTieCap];
+  __shared__ u64 tie_m[kTieCap];
   __shared__ u64 lds_waves[kToppThreads / 64];
 
+  // Masses only place the cut, so they use the hardware exp2 / log2: p rows
+  // exp2((l - m) c) / Z with c = log2(e) / T; draft rows q / Z at T == 1,
+  // else exp2(log2(q) / T - m log2(e)) / Z.
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float c = invT * kLog2e, mq = m * kLog2e;
   auto key_of = [&](float x) -> uint32_t { return isq ? q_key(x) : logit_key(x); };
   auto mass_of = [&](float x) -> u64 {
-    const float p = isq ? q_tempered(ri, x, tmode, invT) : expf((x - m) * invT) * invZ;
+    float p;
+    if (!isq) p = __builtin_amdgcn_exp2f((x - m) * c) * invZ;
+    else if (tmode == 1) p = x * invZ;
+    else p = x > 0.f ? __builtin_amdgcn_exp2f(__builtin_amdgcn_logf(x) * invT - mq) * invZ : 0.f;
     return fixed_mass(p);
   };
 
@@ -312,30 +323,72 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
   }
 
   // Tokens whose key equals the threshold key join in ascending id order.
-  const int per = (V + kToppThreads - 1) / kToppThreads;
-  const int v0 = min(V, tid * per), v1 = min(V, v0 + per);
-  u64 local = 0;
-  for (int v = v0; v < v1; ++v) {
-    const float x = src[v];
-    if (key_of(x) == prefix) local += mass_of(x);
-  }
-  if (tid == 0) sh_tie = INT_MAX;
-  const u64 excl = block_excl_scan_u64(local, lds_waves);
-  u64 cum = above + excl;
-  for (int v = v0; v < v1; ++v) {
-    const float x = src[v];
-    if (key_of(x) != prefix) continue;
-    cum += mass_of(x);
-    if ((double)cum >= thr) {
-      atomicMin(&sh_tie, v);
-      break;
+  // They are gathered (id, mass) in one coalesced pass; up to kTieCap of
+  // them are ordered by one thread, more fall back to an ordered scan over
+  // per-thread id ranges.
+  if (tid == 0) { sh_tie = INT_MAX; sh_nt = 0; }
+  __syncthreads();
+  for (int v0 = tid; v0 < V; v0 += kToppBatch * kToppThreads) {
+    float xs[kToppBatch];
+#pragma unroll
+    for (int u = 0; u < kToppBatch; ++u) {
+      const int v = v0 + u * kToppThreads;
+      xs[u] = v < V ? src[v] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kToppBatch; ++u) {
+      const int v = v0 + u * kToppThreads;
+      if (v < V && key_of(xs[u]) == prefix) {
+        const int slot = atomicAdd(&sh_nt, 1);
+        if (slot < kTieCap) { tie_id[slot] = v; tie_m[slot] = mass_of(xs[u]); }
+      }
     }
   }
   __syncthreads();
-  // the thread that owns the tie cut reports the nucleus mass
-  const int tie = sh_tie;
-  if (tie >= v0 && tie < v1 && tie != INT_MAX) sh_zn = cum;
+  const int nt = sh_nt;
+  if (nt <= kTieCap) {
+    if (tid == 0) {
+      // insertion sort by id, then the running mass in id order
+      for (int i = 1; i < nt; ++i) {
+        const int id = tie_id[i];
+        const u64 ms = tie_m[i];
+        int j = i - 1;
+        while (j >= 0 && tie_id[j] > id) { tie_id[j + 1] = tie_id[j]; tie_m[j + 1] = tie_m[j]; --j; }
+        tie_id[j + 1] = id;
+        tie_m[j + 1] = ms;
+      }
+      u64 cum = above;
+      for (int i = 0; i < nt; ++i) {
+        cum += tie_m[i];
+        if ((double)cum >= thr) { sh_tie = tie_id[i]; sh_zn = cum; break; }
+      }
+    }
+  } else {
+    const int per = (V + kToppThreads - 1) / kToppThreads;
+    const int v0 = min(V, tid * per), v1 = min(V, v0 + per);
+    u64 local = 0;
+    for (int v = v0; v < v1; ++v) {
+      const float x = src[v];
+      if (key_of(x) == prefix) local += mass_of(x);
+    }
+    const u64 excl = block_excl_scan_u64(local, lds_waves);
+    u64 cum = above + excl;
+    for (int v = v0; v < v1; ++v) {
+      const float x = src[v];
+      if (key_of(x) != prefix) continue;
+      cum += mass_of(x);
+      if ((double)cum >= thr) {
+        atomicMin(&sh_tie, v);
+        break;
+      }
+    }
+    __syncthreads();
+    // the thread that owns the tie cut reports the nucleus mass
+    const int tie = sh_tie;
+    if (tie >= v0 && tie < v1 && tie != INT_MAX) sh_zn = cum;
+  }
   __syncthreads();
+  const int tie = sh_tie;
   if (tid == 0 && tie != INT_MAX) {
     ri[RI_THR] = __uint_as_float(prefix);
     ri[RI_TIE] = __int_as_float(tie);
