@@ -41,7 +41,7 @@ struct Layout {
   int M = 0, ldd = 0, ldf = 0, Vs = 0, G = 0, Gu = 0, nch = 0;
   int ksd = 0, ksf = 0;       // k-steps of the d- and ffn-wide split inputs
   size_t h = 0, xg = 0, ss = 0, act = 0, logits = 0, pst = 0, pidx = 0, qst = 0, rowinfo = 0,
-         dec = 0, csum = 0, xsd = 0, xsf = 0, total = 0;
+         dec = 0, csum = 0, xsd = 0, xsf = 0, part = 0, total = 0;
 };
 
 int gemm_path(const spec_weights* w, int M) {
@@ -54,11 +54,29 @@ int gemm_path(const spec_weights* w, int M) {
 // 16 columns; the vector-FMA path covers 4 tiles per work group).
 int lm_units(const spec_weights* w, int M) {
   const int path = gemm_path(w, M);
-  const int nt = path == PATH_MFMA ? w->lm.nt : kGroupCols / kSub;
+  const bool wide = path == PATH_MFMA && wide_rows(M);   // epilogue in 64-column blocks
+  const int nt = (path == PATH_MFMA && !wide) ? w->lm.nt : kGroupCols / kSub;
   return w->lm.Np / kSub / nt;
 }
 
 int max_rows(int path) { return path == PATH_MFMA ? kMaxRowsMfma : kMaxRowsFma; }
+
+// fp32 partial-sum buffer of the wide GEMMs: the largest S x rows x Np over
+// the pass's GEMMs (rows of one chunk).
+size_t wide_part_bytes(const spec_weights* w, int M) {
+  const int path = gemm_path(w, M);
+  if (path != PATH_MFMA || !wide_rows(M)) return 0;
+  const int rows = M;
+  size_t best = 0;
+  auto one = [&](const Mat& m) {
+    const WidePlan p = plan_wide(rows, m);
+    best = std::max(best, (size_t)p.S * rows * m.Np * sizeof(float));
+  };
+  for (const Mat& m : w->up) one(m);
+  for (const Mat& m : w->down) one(m);
+  one(w->lm);
+  return best;
+}
 
 // Sampling-side buffers, shared by both entry points.
 // G statistics units per row, stored at an even stride Gs so rows load in
@@ -94,6 +112,7 @@ Layout make_layout(const spec_weights* w, int B, int gamma) {
     L.ksf = roundup(w->ffn, kKStep) / kKStep;
     L.xsd = off; off = align256(off + xs_bytes(L.M, L.ksd));
     L.xsf = off; off = align256(off + xs_bytes(L.M, L.ksf));
+    L.part = off; off = align256(off + wide_part_bytes(w, L.M));
   }
   layout_sampling(L, B, gamma, w->V, lm_units(w, L.M), off);
   L.total = off;
@@ -166,10 +185,12 @@ hipError_t prof_events(spec_weights* w, size_t idx, hipEvent_t& e0, hipEvent_t& 
 // chunk's split fragments begin at tile m0 / 16.  With timing on, every
 // launch carries a pair of events and its algorithmic weight bytes.
 hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, const uint16_t* XS,
-                    int ldx, int M, EpiArgs e, hipStream_t st) {
+                    int ldx, int M, EpiArgs e, float* part, hipStream_t st) {
   const int chunk = max_rows(path);
-  // the packing follows the whole pass's row count (a stacked pass is one chunk)
+  // the packing and the kernel follow the whole pass's row count (stacked
+  // and wide passes are one chunk)
   const bool stack = path == PATH_MFMA && xs_stacked(M);
+  const bool wide = path == PATH_MFMA && wide_rows(M);
   static_assert(kMaxRowsMfma % 16 == 0, "MFMA row chunks must start on row tiles");
   for (int m0 = 0; m0 < M; m0 += chunk) {
     GemmArgs a;
@@ -191,13 +212,22 @@ hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, con
     if (e.xs) a.e.xs = e.xs + (size_t)(m0 / 16) * (e.xs_ks + 1) * 3 * 512;
     a.e.xs_stack = stack;
     a.e.row0 = m0;
-    const GemmPlan p = plan_gemm(path, a.M, W, stack);
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (w->prof) {
       const hipError_t err = prof_events(w, w->ev_used, e0, e1);
       if (err != hipSuccess) return err;
     }
-    const hipError_t err = launch_gemm(p, a, st, e0, e1);
+    hipError_t err;
+    if (wide) {
+      const WidePlan wp = plan_wide(a.M, W);
+      WideArgs wa;
+      wa.XS = a.XS; wa.W = W.mfma; wa.M = a.M; wa.MT = wp.MT; wa.KS = a.KS;
+      wa.nt = W.nt; wa.tiles = W.Np / kSub; wa.ks_slice = wp.ks_slice; wa.S = wp.S;
+      wa.P = part; wa.ldp = W.Np; wa.slice_stride = (size_t)a.M * W.Np;
+      err = launch_wide(wp, wa, a.e, st, e0, e1);
+    } else {
+      err = launch_gemm(plan_gemm(path, a.M, W, stack), a, st, e0, e1);
+    }
     if (err != hipSuccess) return err;
     if (w->prof) {
       w->ev_bytes.resize(w->ev_used + 1);
@@ -237,6 +267,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
   float* ss = at<float>(ws, L.ss);
   float* act = at<float>(ws, L.act);
   float* logits = at<float>(ws, L.logits);
+  float* part = L.part ? at<float>(ws, L.part) : nullptr;
   const int ss_ld = L.ldd / kSub;
   const int tmode = tmode_of(T);
   // split activations, for the MFMA path only
@@ -252,7 +283,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
     up.ss_in = ss; up.ss_ld = ss_ld; up.ss_n = ss_ld;
     up.inv_d = 1.0f / (float)w->d; up.eps = w->eps;
     up.xs = xsf; up.xs_ks = L.ksf;
-    err = run_gemm(w, path, w->up[l], xg, xsd, L.ldd, M, up, st);
+    err = run_gemm(w, path, w->up[l], xg, xsd, L.ldd, M, up, part, st);
     if (err != hipSuccess) break;
     EpiArgs dn;
     dn.kind = EPI_DOWN;
@@ -260,7 +291,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
     dn.xg = xg; dn.gain_next = l + 1 < w->n_blocks ? w->gain[l + 1] : nullptr;
     dn.ss_out = ss; dn.ss_ld = ss_ld;
     dn.xs = xsd; dn.xs_ks = L.ksd;
-    err = run_gemm(w, path, w->down[l], act, xsf, L.ldf, M, dn, st);
+    err = run_gemm(w, path, w->down[l], act, xsf, L.ldf, M, dn, part, st);
   }
   if (err == hipSuccess) {
     EpiArgs lm;
@@ -269,7 +300,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
     lm.pst = at<float>(ws, L.pst); lm.pidx = at<int>(ws, L.pidx); lm.qst = at<float>(ws, L.qst);
     lm.q = q; lm.G = L.G; lm.G1 = gamma + 1; lm.gamma = gamma; lm.V = w->V;
     lm.tmode = tmode; lm.invT = tmode ? 1.0f / T : 1.0f;
-    err = run_gemm(w, path, w->lm, h, xsd, L.ldd, M, lm, st);
+    err = run_gemm(w, path, w->lm, h, xsd, L.ldd, M, lm, part, st);
   }
   SampleArgs sa;
   if (err == hipSuccess) {

@@ -356,6 +356,198 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
   run_epilogue(a.e, M, c0, NT, res, ldr, sh_inv, nwaves, pv);
 }
 
+// ---------------------------------------------------------------- wide MFMA GEMM
+// Many rows (plain packing, M > 10): the split activations of a k-step,
+// MT row tiles x 3 terms, are staged once per work group in LDS and shared
+// by every column tile of the group (8 tiles = 128 columns), instead of
+// being read from L2 by every 16-column tile.  MG x CG waves: row groups of
+// MTW tiles times column groups of NTC tiles.  A fragments are loaded two
+// k-steps ahead into registers, written to a double-buffered LDS tile, and
+// read with ds_read_b128; weights stream into a 4-deep register ring.  When
+// the column blocks cannot fill the chip, K is split over blockIdx.y and the
+// slices are summed, in slice order, by k_epi_wide.  Output: fp32 partial
+// sums P[slice][row][col].
+constexpr int kWideTiles = 8;      // 16-column tiles per work group
+
+template <int MTW, int NTC, int MG, int CG>
+__global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
+  // weight k-steps in flight per wave (even: the LDS buffer alternates)
+  constexpr int kWideRing = NTC >= 4 ? 2 : 4;
+  constexpr int NW = MG * CG, THREADS = 64 * NW;
+  constexpr int CPT = (MTW * MG * 3 * 64 + THREADS - 1) / THREADS;   // A chunks per thread
+  extern __shared__ bf16x8 lds_a[];                                   // [2][NFRP]
+  const int lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mg = wave / CG, cg = wave - mg * CG;
+  const int KS = a.KS, MT = a.MT, M = a.M;
+  const int s0 = blockIdx.y * a.ks_slice;
+  const int s1 = min(KS, s0 + a.ks_slice);
+  const int nsteps = s1 - s0;
+  const int nfr = MT * 3 * 64;
+  const bf16x8* XS = reinterpret_cast<const bf16x8*>(a.XS);
+  const bf16x8* W = reinterpret_cast<const bf16x8*>(a.W);
+
+  // weight fragments of this wave's tiles: tile t of layout block b = t / nt
+  const bf16x8* wp[NTC];
+  bool tval[NTC];
+#pragma unroll
+  for (int t = 0; t < NTC; ++t) {
+    const int tile = blockIdx.x * (NTC * CG) + cg * NTC + t;
+    tval[t] = tile < a.tiles;
+    const int tt = min(tile, a.tiles - 1);
+    const int b = tt / a.nt, tp = tt - b * a.nt;
+    wp[t] = W + ((size_t)b * KS * a.nt + tp) * 64 + lane;
+  }
+  const size_t wstep = (size_t)a.nt * 64;
+
+  f32x4 acc[MTW][NTC];
+#pragma unroll
+  for (int i = 0; i < MTW; ++i)
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 areg[2][CPT];
+  bf16x8 bq[kWideRing][NTC];
+  // chunk c of a k-step: fragment (mt, p) = (c / 192, c / 64 % 3), lane
+  // c % 64.  The LDS tile is padded to CPT * THREADS chunks so the copy has
+  // no per-thread branch; chunks past the real ones copy the last real one.
+  constexpr int NFRP = CPT * THREADS;
+  const bf16x8* asrc[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = min(tid + i * THREADS, nfr - 1);
+    const int mt = c / 192, rem = c - mt * 192;
+    asrc[i] = XS + (size_t)mt * (KS + 1) * 192 + rem;
+  }
+  auto load_a = [&](int set, int s) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) areg[set][i] = asrc[i][(size_t)s * 192];
+  };
+  auto store_a = [&](int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) lds_a[buf * NFRP + tid + i * THREADS] = areg[set][i];
+  };
+  auto load_b = [&](int slot, int s) {
+    const int ss = min(s, s1 - 1);
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) bq[slot][t] = wp[t][(size_t)ss * wstep];
+  };
+
+  if (nsteps > 0) {
+    load_a(0, s0);
+#pragma unroll
+    for (int u = 0; u < kWideRing; ++u) load_b(u, s0 + u);
+    store_a(0, 0);
+    if (nsteps > 1) load_a(1, s0 + 1);
+    __syncthreads();
+    for (int it = 0; it < nsteps; it += kWideRing) {
+#pragma unroll
+      for (int u = 0; u < kWideRing; ++u) {
+        const int k = it + u;                 // k-step s0 + k; LDS buffer and A set k & 1
+        if (k < nsteps) {
+          if (k + 2 < nsteps) load_a(u & 1, s0 + k + 2);
+          // A fragments come from LDS one term at a time, the next term's
+          // reads issued before the current term's MFMAs
+          const bf16x8* abuf = lds_a + (u & 1) * NFRP + lane;
+          bf16x8 af[2][MTW];
+#pragma unroll
+          for (int i = 0; i < MTW; ++i) af[0][i] = abuf[(min(mg * MTW + i, MT - 1) * 3) * 64];
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            if (p < 2) {
+#pragma unroll
+              for (int i = 0; i < MTW; ++i)
+                af[(p + 1) & 1][i] = abuf[(min(mg * MTW + i, MT - 1) * 3 + p + 1) * 64];
+            }
+            // tiles past MT repeat the last tile (no branch in the MFMA
+            // stream); their rows are never stored
+#pragma unroll
+            for (int i = 0; i < MTW; ++i)
+#pragma unroll
+              for (int t = 0; t < NTC; ++t)
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[p & 1][i], bq[u][t], acc[i][t], 0, 0, 0);
+          }
+          load_b(u, s0 + k + kWideRing);
+          if (k + 1 < nsteps) store_a((u + 1) & 1, (u + 1) & 1);
+          __syncthreads();
+        }
+      }
+    }
+  }
+
+  // partial sums to P[slice][row][col]; C layout: lane holds rows
+  // 4 (lane / 16) + j of column lane % 16
+  float* P = a.P + (size_t)blockIdx.y * a.slice_stride;
+#pragma unroll
+  for (int i = 0; i < MTW; ++i)
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+      const int tile = blockIdx.x * (NTC * CG) + cg * NTC + t;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = (mg * MTW + i) * 16 + 4 * (lane >> 4) + j;
+        if (tval[t] && row < M) P[(size_t)row * a.ldp + tile * kSub + (lane & 15)] = acc[i][t][j];
+      }
+    }
+}
+
+// Epilogue arguments of the rows from m0 on (m0 a multiple of 16).
+__device__ __forceinline__ EpiArgs epi_rows(const EpiArgs& e, int m0) {
+  EpiArgs r = e;
+  r.out = e.out + (size_t)m0 * e.ldo;
+  if (e.kind == EPI_UP) r.ss_in = e.ss_in + (size_t)m0 * e.ss_ld;
+  if (e.kind == EPI_DOWN) {
+    r.xg = e.xg + (size_t)m0 * e.ldo;
+    r.ss_out = e.ss_out + (size_t)m0 * e.ss_ld;
+  }
+  if (e.xs) r.xs = e.xs + (size_t)(m0 / 16) * (e.xs_ks + 1) * 3 * 512;
+  r.row0 = e.row0 + m0;
+  return r;
+}
+
+// Work group (64-column block, 16-row tile): sums the S slices of P (in
+// slice order) into an LDS tile and runs the GEMM's epilogue on it.
+constexpr int kEpiThreads = 256;
+__global__ __launch_bounds__(kEpiThreads) void k_epi_wide(WideArgs a, EpiArgs e0) {
+  constexpr int ldr = 4 * kSub + 1;
+  __shared__ float res[16 * ldr];
+  __shared__ float sh_inv[16];
+  const int c0 = blockIdx.x * 4, m0 = blockIdx.y * 16;
+  const int M = min(16, a.M - m0);
+  const EpiArgs e = epi_rows(e0, m0);
+  float pv[8];
+  epi_prefetch(e, M, c0, 4, kEpiThreads / kWave, pv);
+  // 4 items per thread, all slice loads of a batch of slices in flight
+  const int idx0 = threadIdx.x;
+  float v[4];
+  const float* p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = min(idx0 + j * kEpiThreads, M * 64 - 1);
+    p[j] = a.P + (size_t)(m0 + (idx >> 6)) * a.ldp + c0 * kSub + (idx & 63);
+    v[j] = 0.f;
+  }
+  for (int sl = 0; sl < a.S; sl += 4) {
+    float x[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        x[q][j] = sl + q < a.S ? p[j][(size_t)(sl + q) * a.slice_stride] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += x[q][j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int idx = idx0 + j * kEpiThreads;
+    if (idx < M * 64) res[(idx >> 6) * ldr + (idx & 63)] = v[j];
+  }
+  __syncthreads();
+  run_epilogue(e, M, c0, 4, res, ldr, sh_inv, kEpiThreads / kWave, pv);
+}
+
 // ---------------------------------------------------------------- vector-FMA GEMM
 // Row-major weights (fp32 or bf16), 4 waves, 4 column tiles (64 columns) per
 // work group.  Lane = (row r = lane / 8 of an 8-row step, 8 columns at
@@ -494,6 +686,50 @@ GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack) {
     p.kg *= 2;
   p.lds = lds_of(p.kg);
   return p;
+}
+
+WidePlan plan_wide(int M, const Mat& m) {
+  WidePlan p;
+  p.MT = (M + 15) / 16;
+  p.mtw = p.MT <= 4 ? 4 : p.MT;      // one row group; wide_rows() keeps MT <= 7
+  p.mg = 1; p.ntc = 2; p.cg = 4;
+  const int tiles = m.Np / kSub;
+  p.colblocks = (tiles + kWideTiles - 1) / kWideTiles;
+  const int KS = m.Kp / kKStep;
+  int S = 1;
+  while (p.colblocks * S < SV_MIN_BLOCKS && S < 8 && KS / (2 * S) >= 16) S *= 2;
+  p.ks_slice = (KS + S - 1) / S;
+  p.S = (KS + p.ks_slice - 1) / p.ks_slice;
+  const int threads = 64 * p.mg * p.cg;
+  const int cpt = (p.mtw * p.mg * 3 * 64 + threads - 1) / threads;
+  p.lds = (size_t)2 * cpt * threads * 16;
+  return p;
+}
+
+template <int MTW, int NTC, int MG, int CG>
+static void launch_wide_t(const WidePlan& p, const WideArgs& a, hipStream_t st, hipEvent_t e0,
+                          hipEvent_t e1) {
+  // the double-buffered activation tile can exceed the default 64 KiB
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_gemm_wide<MTW, NTC, MG, CG>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  (void)attr;
+  hipExtLaunchKernelGGL((k_gemm_wide<MTW, NTC, MG, CG>), dim3(p.colblocks, p.S),
+                        dim3(64 * MG * CG), p.lds, st, e0, e1, 0, a);
+}
+
+hipError_t launch_wide(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
+                       hipEvent_t e0, hipEvent_t e1) {
+  switch (p.mtw) {
+    case 4: launch_wide_t<4, 2, 1, 4>(p, a, st, e0, e1); break;
+    case 5: launch_wide_t<5, 2, 1, 4>(p, a, st, e0, e1); break;
+    case 6: launch_wide_t<6, 2, 1, 4>(p, a, st, e0, e1); break;
+    default: launch_wide_t<7, 2, 1, 4>(p, a, st, e0, e1); break;
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_epi_wide, dim3(a.tiles / 4, (a.M + 15) / 16), dim3(kEpiThreads), 0, st, a, e);
+  return hipGetLastError();
 }
 
 // Launches go through hipExtLaunchKernelGGL so that, when timing is on, the

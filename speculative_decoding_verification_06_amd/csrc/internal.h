@@ -104,6 +104,31 @@ inline size_t xs_bytes(int M, int ks) {
 }
 
 GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack);
+
+// Wide MFMA GEMM (plain packing): work groups of 8 column tiles with the
+// activations staged in LDS, K split over S slices when the column blocks
+// alone cannot fill the chip.
+struct WidePlan {
+  int MT = 0, mtw = 0, ntc = 0, mg = 0, cg = 0;
+  int colblocks = 0, S = 1, ks_slice = 0;
+  size_t lds = 0;
+};
+struct WideArgs {
+  const void* XS = nullptr;   // split activations, plain packing
+  const void* W = nullptr;    // MFMA weight tiles
+  int M = 0, MT = 0, KS = 0;
+  int nt = 1, tiles = 0;      // layout column-block width (tiles) and tiles of Np
+  int ks_slice = 0, S = 1;
+  float* P = nullptr;         // [S][M][ldp] fp32 partial sums
+  int ldp = 0;
+  size_t slice_stride = 0;    // floats between slices
+};
+WidePlan plan_wide(int M, const Mat& m);
+// Row counts the wide GEMM serves: plain packing up to 7 row tiles.
+inline bool wide_rows(int M) { return !xs_stacked(M) && M <= 7 * 16; }
+// The GEMM (timed by e0 / e1 when given) and then its epilogue kernel.
+hipError_t launch_wide(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
+                       hipEvent_t e0, hipEvent_t e1);
 // e0 / e1: null, or events that take the launch's start and end timestamps.
 hipError_t launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t st, hipEvent_t e0,
                        hipEvent_t e1);
