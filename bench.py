@@ -27,6 +27,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verify passes/sec & accepted tokens/sec at B=1, γ=4; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
+MFMA_BOUND_ROWS = 112            # above this many rows the three-term MFMA work exceeds the weight stream
 POOL = 8
 
 
@@ -266,6 +268,10 @@ def main():
     per_launch_bytes = wbytes / launches
     per_launch_s = gemm_ms / 1e3 / launches
     achieved = per_launch_bytes / per_launch_s / 1e9
+    # executed bf16 MFMA flops: every fp32 x bf16 product is three bf16
+    # products (hi, mid, lo terms), 2 flops each, for M = B (gamma + 1) rows
+    M = B * G1
+    mfma_tflops = 6.0 * M * (per_launch_bytes / 2) / per_launch_s / 1e12
 
     weight_bytes = wbytes / kp
     other = 4 * (B * G1 * wl.d + (B * gamma * wl.V if T > 0 else 0) + B * gamma)
@@ -286,11 +292,17 @@ def main():
         "hbm_gbs_whole_step": step_gbs,
         "hbm_frac_whole_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": weight_bytes + other,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "weight-streaming GEMMs (MLP up/down, LM head)",
-                     "bytes_per_launch": per_launch_bytes, "launches": launches,
-                     "avg_launch_us": per_launch_s * 1e6},
+        "roofline": ({"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+                     if wl.wdtype == "f32" or M <= MFMA_BOUND_ROWS else
+                     {"bound": "mfma", "achieved": mfma_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS,
+                      "traffic": traffic, "hbm_gbs": achieved}),
+        "gemm": {"kernel": "weight-streaming GEMMs (MLP up/down, LM head)",
+                 "bytes_per_launch": per_launch_bytes, "launches": launches,
+                 "avg_launch_us": per_launch_s * 1e6, "hbm_gbs": achieved,
+                 "hbm_frac": achieved / HBM_PEAK_GBS, "mfma_tflops": mfma_tflops,
+                 "mfma_frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
     }
     if host is not None:
