@@ -260,12 +260,14 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
     }                                                                            \
   }
 
+  // terms outermost: consecutive MFMAs write different accumulators, so none
+  // waits on the one before it
 #define SV_COMPUTE(u)                                                            \
   {                                                                              \
-    _Pragma("unroll") for (int i = 0; i < MTW; ++i) {                            \
-      if (mt0 + i < MT) {                                                        \
-        _Pragma("unroll") for (int t = 0; t < NT; ++t) {                         \
-          _Pragma("unroll") for (int p = 0; p < FPT; ++p)                        \
+    _Pragma("unroll") for (int p = 0; p < FPT; ++p) {                            \
+      _Pragma("unroll") for (int i = 0; i < MTW; ++i) {                          \
+        if (mt0 + i < MT) {                                                      \
+          _Pragma("unroll") for (int t = 0; t < NT; ++t)                         \
             acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xq[u][i][p], bq[u][t], \
                                                                 acc[i][t], 0, 0, 0); \
         }                                                                        \
@@ -357,18 +359,17 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------- wide MFMA GEMM
-// Many rows (plain packing, M > 10): the split activations of a k-step,
-// MT row tiles x 3 terms, are staged once per work group in LDS and shared
-// by every column tile of the group (8 tiles = 128 columns), instead of
-// being read from L2 by every 16-column tile.  MG x CG waves: row groups of
-// MTW tiles times column groups of NTC tiles.  A fragments are loaded two
-// k-steps ahead into registers, written to a double-buffered LDS tile, and
-// read with ds_read_b128; weights stream into a 4-deep register ring.  When
-// the column blocks cannot fill the chip, K is split over blockIdx.y and the
-// slices are summed, in slice order, by k_epi_wide.  Output: fp32 partial
-// sums P[slice][row][col].
-constexpr int kWideTiles = 8;      // 16-column tiles per work group
-
+// Many rows (plain packing, 11 to 224 rows): the split activations of a
+// k-step, MT row tiles x 3 terms, are staged once per work group in LDS and
+// shared by every column tile of the group (8 tiles = 128 columns up to 7
+// row tiles; 16 tiles with two row groups above), instead of being read
+// from L2 by every 16-column tile.  MG x CG waves: row groups of MTW tiles
+// times column groups of NTC tiles.  A fragments are loaded two k-steps
+// ahead into registers, written to a double-buffered LDS tile, and read
+// back one row tile at a time with ds_read_b128; weights stream into a
+// register ring.  When the column blocks cannot fill the chip, K is split
+// over blockIdx.y and the slices are summed, in slice order, by
+// k_epi_wide.  Output: fp32 partial sums P[slice][row][col].
 template <int MTW, int NTC, int MG, int CG>
 __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
   // weight k-steps in flight per wave (even: the LDS buffer alternates)
@@ -446,26 +447,26 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
         const int k = it + u;                 // k-step s0 + k; LDS buffer and A set k & 1
         if (k < nsteps) {
           if (k + 2 < nsteps) load_a(u & 1, s0 + k + 2);
-          // A fragments come from LDS one term at a time, the next term's
-          // reads issued before the current term's MFMAs
+          // A fragments stream from LDS one row tile (three terms) at a
+          // time, the next tile's reads issued before this tile's MFMAs.
+          // Tiles past MT repeat the last tile (no branch in the MFMA
+          // stream); their rows are never stored.
           const bf16x8* abuf = lds_a + (u & 1) * NFRP + lane;
-          bf16x8 af[2][MTW];
+          bf16x8 af[2][3];
 #pragma unroll
-          for (int i = 0; i < MTW; ++i) af[0][i] = abuf[(min(mg * MTW + i, MT - 1) * 3) * 64];
+          for (int p = 0; p < 3; ++p) af[0][p] = abuf[(min(mg * MTW, MT - 1) * 3 + p) * 64];
 #pragma unroll
-          for (int p = 0; p < 3; ++p) {
-            if (p < 2) {
+          for (int i = 0; i < MTW; ++i) {
+            if (i + 1 < MTW) {
 #pragma unroll
-              for (int i = 0; i < MTW; ++i)
-                af[(p + 1) & 1][i] = abuf[(min(mg * MTW + i, MT - 1) * 3 + p + 1) * 64];
+              for (int p = 0; p < 3; ++p)
+                af[(i + 1) & 1][p] = abuf[(min(mg * MTW + i + 1, MT - 1) * 3 + p) * 64];
             }
-            // tiles past MT repeat the last tile (no branch in the MFMA
-            // stream); their rows are never stored
 #pragma unroll
-            for (int i = 0; i < MTW; ++i)
+            for (int p = 0; p < 3; ++p)
 #pragma unroll
               for (int t = 0; t < NTC; ++t)
-                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[p & 1][i], bq[u][t], acc[i][t], 0, 0, 0);
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i & 1][p], bq[u][t], acc[i][t], 0, 0, 0);
           }
           load_b(u, s0 + k + kWideRing);
           if (k + 1 < nsteps) store_a((u + 1) & 1, (u + 1) & 1);
@@ -691,10 +692,18 @@ GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack) {
 WidePlan plan_wide(int M, const Mat& m) {
   WidePlan p;
   p.MT = (M + 15) / 16;
-  p.mtw = p.MT <= 4 ? 4 : p.MT;      // one row group; wide_rows() keeps MT <= 7
-  p.mg = 1; p.ntc = 2; p.cg = 4;
+  if (p.MT <= 7) {
+    // one row group, 4 waves x 2 tiles = 8 column tiles
+    p.mtw = p.MT <= 4 ? 4 : p.MT;
+    p.mg = 1; p.ntc = 2; p.cg = 4;
+  } else {
+    // two row groups x 4 column groups of 4 tiles = 16 column tiles, 8 waves
+    p.mtw = p.MT <= 8 ? 4 : (p.MT + 1) / 2;
+    p.mg = 2; p.ntc = 4; p.cg = 4;
+  }
   const int tiles = m.Np / kSub;
-  p.colblocks = (tiles + kWideTiles - 1) / kWideTiles;
+  const int ntw = p.ntc * p.cg;
+  p.colblocks = (tiles + ntw - 1) / ntw;
   const int KS = m.Kp / kKStep;
   int S = 1;
   while (p.colblocks * S < SV_MIN_BLOCKS && S < 8 && KS / (2 * S) >= 16) S *= 2;
@@ -720,11 +729,20 @@ static void launch_wide_t(const WidePlan& p, const WideArgs& a, hipStream_t st, 
 
 hipError_t launch_wide(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
                        hipEvent_t e0, hipEvent_t e1) {
-  switch (p.mtw) {
-    case 4: launch_wide_t<4, 2, 1, 4>(p, a, st, e0, e1); break;
-    case 5: launch_wide_t<5, 2, 1, 4>(p, a, st, e0, e1); break;
-    case 6: launch_wide_t<6, 2, 1, 4>(p, a, st, e0, e1); break;
-    default: launch_wide_t<7, 2, 1, 4>(p, a, st, e0, e1); break;
+  if (p.mg == 1) {
+    switch (p.mtw) {
+      case 4: launch_wide_t<4, 2, 1, 4>(p, a, st, e0, e1); break;
+      case 5: launch_wide_t<5, 2, 1, 4>(p, a, st, e0, e1); break;
+      case 6: launch_wide_t<6, 2, 1, 4>(p, a, st, e0, e1); break;
+      default: launch_wide_t<7, 2, 1, 4>(p, a, st, e0, e1); break;
+    }
+  } else {
+    switch (p.mtw) {
+      case 4: launch_wide_t<4, 4, 2, 4>(p, a, st, e0, e1); break;
+      case 5: launch_wide_t<5, 4, 2, 4>(p, a, st, e0, e1); break;
+      case 6: launch_wide_t<6, 4, 2, 4>(p, a, st, e0, e1); break;
+      default: launch_wide_t<7, 4, 2, 4>(p, a, st, e0, e1); break;
+    }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -124,8 +124,8 @@ struct WideArgs {
   size_t slice_stride = 0;    // floats between slices
 };
 WidePlan plan_wide(int M, const Mat& m);
-// Row counts the wide GEMM serves: plain packing up to 7 row tiles.
-inline bool wide_rows(int M) { return !xs_stacked(M) && M <= 7 * 16; }
+// Row counts the wide GEMM serves: the plain packing up to one 224-row chunk.
+inline bool wide_rows(int M) { return !xs_stacked(M) && M <= 224; }
 // The GEMM (timed by e0 / e1 when given) and then its epilogue kernel.
 hipError_t launch_wide(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
                        hipEvent_t e0, hipEvent_t e1);

@@ -501,18 +501,21 @@ __global__ __launch_bounds__(kResThreads) void k_decide_chunks(SampleArgs a) {
   const int gamma = a.gamma, G1 = gamma + 1;
   if (tid == 0) { sh_bad = 0; sh_first = INT_MAX; }
   __syncthreads();
+  // statistics of local row r (p rows 0..gamma, then q rows)
+  auto ri_of = [&](int r) -> const float* {
+    return a.rowinfo + (r < G1 ? (size_t)b * G1 + r : (size_t)a.M + (size_t)b * gamma + (r - G1)) * kRowInfo;
+  };
   for (int i = tid; i < gamma; i += blockDim.x) {
     const int x = a.draft[(size_t)b * gamma + i];
     if (x < 0 || x >= a.V) { atomicOr(&sh_bad, 1); continue; }
     const size_t prow = (size_t)b * G1 + i;
     bool reject;
     if (a.tmode == 0) {
-      reject = x != __float_as_int(a.rowinfo[prow * kRowInfo + RI_M]);
+      reject = x != __float_as_int(ri_of(i)[RI_M]);
     } else {
       const size_t qrow = (size_t)b * gamma + i;
-      const float pp = p_prime(a.rowinfo + prow * kRowInfo, a.logits[prow * a.ldl + x], x, a.invT);
-      const float qq = q_prime(a.rowinfo + ((size_t)a.M + qrow) * kRowInfo, a.q[qrow * a.V + x], x,
-                               a.tmode, a.invT);
+      const float pp = p_prime(ri_of(i), a.logits[prow * a.ldl + x], x, a.invT);
+      const float qq = q_prime(ri_of(G1 + i), a.q[qrow * a.V + x], x, a.tmode, a.invT);
       float r, u;
       row_uniforms(a.seed, b, i, r, u);
       reject = !(r * qq < pp);
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(kResThreads) void k_decide_chunks(SampleArgs a) {
       int tok = -1;
       if (i < n) tok = a.draft[(size_t)b * gamma + i];
       else if (i == n && a.tmode == 0)
-        tok = __float_as_int(a.rowinfo[((size_t)b * G1 + n) * kRowInfo + RI_M]);
+        tok = __float_as_int(ri_of(n)[RI_M]);
       a.emitted[(size_t)b * G1 + i] = tok;
     }
     if (tid == 0) { a.n_acc[b] = n; a.dec[4 * b] = n; }
@@ -577,9 +580,29 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
   row_uniforms(a.seed, b, j, r, u);
   const double* cs = a.csum + 2 * (size_t)b * a.nch;
   if (tid == 0) { sh_c = INT_MAX; sh_cand = INT_MAX; sh_last = -1; sh_base = 0.0; sh_lastbase = 0.0; }
-  // total of the residual chunk sums; the p' sums when it is exactly zero
   int usep = 0;
-  double total = 0.0;
+  double total = 0.0, target = 0.0;
+  if (a.nch <= kResThreads) {
+    // one chunk sum per thread: one block scan picks the chunk
+    const bool in = tid < a.nch;
+    double xw = in ? cs[2 * tid] : 0.0, xp = in ? cs[2 * tid + 1] : 0.0;
+    double ex = block_excl_scan_f64(xw, lds_w, &total);
+    if (!(total > 0.0)) {               // zero residual: sample p' instead
+      usep = 1;
+      xw = xp;
+      ex = block_excl_scan_f64(xw, lds_w, &total);
+    }
+    target = (double)u * total;
+    if (in && ex + xw > target) atomicMin(&sh_c, tid);
+    if (in && xw > 0.0) atomicMax(&sh_last, tid);
+    __syncthreads();
+    const int pick = sh_c != INT_MAX ? sh_c : max(sh_last, 0);
+    if (tid == pick) sh_base = ex;
+    __syncthreads();
+    if (tid == 0) { sh_c = pick; sh_last = -1; }
+    __syncthreads();
+  } else {
+  // total of the residual chunk sums; the p' sums when it is exactly zero
   for (int pass = 0; pass < 2; ++pass) {
     total = 0.0;
     for (int c0 = 0; c0 < a.nch; c0 += kResThreads) {
@@ -591,7 +614,7 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
     usep = pass;
     if (total > 0.0) break;
   }
-  const double target = (double)u * total;
+  target = (double)u * total;
   // the first chunk whose inclusive prefix exceeds the target (the last
   // chunk when rounding leaves none)
   double run = 0.0;
@@ -610,8 +633,11 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
     run += t;
   }
   __syncthreads();
-  const int c = sh_c != INT_MAX ? sh_c : a.nch - 1;
-  const double base = sh_c != INT_MAX ? sh_base : sh_lastbase;
+  if (tid == 0 && sh_c == INT_MAX) { sh_c = a.nch - 1; sh_base = sh_lastbase; }
+  __syncthreads();
+  }
+  const int c = sh_c;
+  const double base = sh_base;
   const ResRow rr = make_row(a, b, j, usep != 0);
   float l[kResPer], qv[kResPer];
   load_chunk(a, rr, c, l, qv);
@@ -668,9 +694,10 @@ hipError_t launch_dump_probs(const SampleArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------- sequencing
 hipError_t launch_sampling(const SampleArgs& a, hipStream_t st) {
   const int qrows = a.B * a.gamma;
+  const bool topp = a.tmode != 0 && a.top_p < 1.0f;
+  // one work group per row combines the statistics, in parallel over rows
   hipLaunchKernelGGL(k_rowstats, dim3(a.tmode != 0 ? a.M + qrows : a.M), dim3(kRowThreads), 0, st, a);
-  if (a.tmode != 0 && a.top_p < 1.0f)
-    hipLaunchKernelGGL(k_topp, dim3(a.M + qrows), dim3(kToppThreads), 0, st, a);
+  if (topp) hipLaunchKernelGGL(k_topp, dim3(a.M + qrows), dim3(kToppThreads), 0, st, a);
   hipLaunchKernelGGL(k_decide_chunks, dim3(a.tmode != 0 ? a.nch : 1, a.B), dim3(kResThreads), 0, st, a);
   if (a.tmode != 0)
     hipLaunchKernelGGL(k_res_select, dim3(a.B), dim3(kResThreads), 0, st, a);

@@ -77,6 +77,8 @@ CASES = [
     ("bf16-mfma-k2-greedy", 4, 4, 320, 640, 777, 2, "bf16", 0.0, 1.0, True, {}),
     ("bf16-mfma-rows-topp", 8, 8, 256, 512, 2000, 1, "bf16", 0.7, 0.9, False, {}),
     ("bf16-mfma-chunked", 40, 6, 128, 256, 500, 1, "bf16", 1.3, 0.6, False, {}),
+    ("bf16-wide-two-row-groups", 20, 6, 192, 320, 900, 2, "bf16", 1.0, 1.0, True, {}),
+    ("bf16-wide-224-greedy", 32, 6, 160, 288, 700, 1, "bf16", 0.0, 1.0, False, {}),
     ("bf16-fma", 2, 4, 192, 448, 900, 2, "bf16", 1.0, 1.0, True,
      {"keep_rowmajor": True, "mfma_min_rows": 10 ** 6}),
     ("bf16-fma-many-rows", 12, 3, 136, 200, 333, 1, "bf16", 0.8, 1.0, False,
