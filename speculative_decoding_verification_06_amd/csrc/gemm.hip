@@ -372,8 +372,11 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 // k_epi_wide.  Output: fp32 partial sums P[slice][row][col].
 template <int MTW, int NTC, int MG, int CG>
 __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
-  // weight k-steps in flight per wave (even: the LDS buffer alternates)
-  constexpr int kWideRing = NTC >= 4 ? 2 : 4;
+  // weight k-steps in flight per wave (even: the LDS buffer alternates).
+  // The 16-tile variant keeps one A register set (A is an L2 hit, one
+  // k-step ahead suffices) so that its register budget holds the ring.
+  constexpr int kWideRing = 4;
+  constexpr int ASETS = NTC >= 4 ? 1 : 2;
   constexpr int NW = MG * CG, THREADS = 64 * NW;
   constexpr int CPT = (MTW * MG * 3 * 64 + THREADS - 1) / THREADS;   // A chunks per thread
   extern __shared__ bf16x8 lds_a[];                                   // [2][NFRP]
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
 #pragma unroll
     for (int t = 0; t < NTC; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 areg[2][CPT];
+  bf16x8 areg[ASETS][CPT];
   bf16x8 bq[kWideRing][NTC];
   // chunk c of a k-step: fragment (mt, p) = (c / 192, c / 64 % 3), lane
   // c % 64.  The LDS tile is padded to CPT * THREADS chunks so the copy has
@@ -439,14 +442,15 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
 #pragma unroll
     for (int u = 0; u < kWideRing; ++u) load_b(u, s0 + u);
     store_a(0, 0);
-    if (nsteps > 1) load_a(1, s0 + 1);
+    if (ASETS == 2 && nsteps > 1) load_a(ASETS - 1, s0 + 1);
     __syncthreads();
     for (int it = 0; it < nsteps; it += kWideRing) {
 #pragma unroll
       for (int u = 0; u < kWideRing; ++u) {
-        const int k = it + u;                 // k-step s0 + k; LDS buffer and A set k & 1
+        const int k = it + u;                 // k-step s0 + k; LDS buffer k & 1
         if (k < nsteps) {
-          if (k + 2 < nsteps) load_a(u & 1, s0 + k + 2);
+          // A for k-step k + ASETS into register set (k & 1) % ASETS
+          if (k + ASETS < nsteps) load_a((u & 1) % ASETS, s0 + k + ASETS);
           // A fragments stream from LDS one row tile (three terms) at a
           // time, the next tile's reads issued before this tile's MFMAs.
           // Tiles past MT repeat the last tile (no branch in the MFMA
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
                 acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i & 1][p], bq[u][t], acc[i][t], 0, 0, 0);
           }
           load_b(u, s0 + k + kWideRing);
-          if (k + 1 < nsteps) store_a((u + 1) & 1, (u + 1) & 1);
+          if (k + 1 < nsteps) store_a(((u + 1) & 1) % ASETS, (u + 1) & 1);
           __syncthreads();
         }
       }
