@@ -361,21 +361,22 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 // ---------------------------------------------------------------- wide MFMA GEMM
 // Many rows (plain packing, 11 to 224 rows): the split activations of a
 // k-step, MT row tiles x 3 terms, are staged once per work group in LDS and
-// shared by every column tile of the group (8 tiles = 128 columns up to 7
-// row tiles; 16 tiles with two row groups above), instead of being read
-// from L2 by every 16-column tile.  MG x CG waves: row groups of MTW tiles
-// times column groups of NTC tiles.  A fragments are loaded two k-steps
-// ahead into registers, written to a double-buffered LDS tile, and read
-// back one row tile at a time with ds_read_b128; weights stream into a
-// register ring.  When the column blocks cannot fill the chip, K is split
-// over blockIdx.y and the slices are summed, in slice order, by
-// k_epi_wide.  Output: fp32 partial sums P[slice][row][col].
+// shared by the group's 16 column tiles (256 columns), instead of being
+// read from L2 by every 16-column tile.  MG x CG waves: row groups of MTW
+// tiles times column groups of NTC tiles.  A fragments are loaded ahead
+// into registers, written to a double-buffered LDS tile, and read back one
+// row tile at a time with ds_read_b128; weights stream into a register
+// ring.  When the column blocks cannot fill the chip, K is split over
+// blockIdx.y and the slices are summed, in slice order, by k_epi_wide.
+// Output: fp32 partial sums P[slice][row][col].
 template <int MTW, int NTC, int MG, int CG>
 __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
-  // weight k-steps in flight per wave (even: the LDS buffer alternates).
-  // The 16-tile variant keeps one A register set (A is an L2 hit, one
-  // k-step ahead suffices) so that its register budget holds the ring.
-  constexpr int kWideRing = 4;
+  // weight k-steps in flight per wave (even: the LDS buffer alternates):
+  // the 8-tile variant does little MFMA work per k-step, so it needs more
+  // k-steps in flight to cover HBM latency.  The 16-tile variant keeps one
+  // A register set (A is an L2 hit, one k-step ahead suffices) so that its
+  // register budget holds its ring.
+  constexpr int kWideRing = NTC >= 4 ? 4 : 8;
   constexpr int ASETS = NTC >= 4 ? 1 : 2;
   constexpr int NW = MG * CG, THREADS = 64 * NW;
   constexpr int CPT = (MTW * MG * 3 * 64 + THREADS - 1) / THREADS;   // A chunks per thread
@@ -696,21 +697,16 @@ GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack) {
 WidePlan plan_wide(int M, const Mat& m) {
   WidePlan p;
   p.MT = (M + 15) / 16;
-  if (p.MT <= 7) {
-    // one row group, 4 waves x 2 tiles = 8 column tiles
-    p.mtw = p.MT <= 4 ? 4 : p.MT;
-    p.mg = 1; p.ntc = 2; p.cg = 4;
-  } else {
-    // two row groups x 4 column groups of 4 tiles = 16 column tiles, 8 waves
-    p.mtw = p.MT <= 8 ? 4 : (p.MT + 1) / 2;
-    p.mg = 2; p.ntc = 4; p.cg = 4;
-  }
+  // two row groups x 4 column groups of 4 tiles = 16 column tiles, 8 waves
+  p.mtw = (p.MT + 1) / 2;
+  p.mg = 2; p.ntc = 4; p.cg = 4;
   const int tiles = m.Np / kSub;
   const int ntw = p.ntc * p.cg;
   p.colblocks = (tiles + ntw - 1) / ntw;
   const int KS = m.Kp / kKStep;
+  // at least one 8-wave work group per CU
   int S = 1;
-  while (p.colblocks * S < SV_MIN_BLOCKS && S < 8 && KS / (2 * S) >= 16) S *= 2;
+  while (p.colblocks * S < SV_MIN_BLOCKS && S < 16 && KS / (2 * S) >= 8) S *= 2;
   p.ks_slice = (KS + S - 1) / S;
   p.S = (KS + p.ks_slice - 1) / p.ks_slice;
   const int threads = 64 * p.mg * p.cg;
@@ -733,20 +729,14 @@ static void launch_wide_t(const WidePlan& p, const WideArgs& a, hipStream_t st, 
 
 hipError_t launch_wide(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
                        hipEvent_t e0, hipEvent_t e1) {
-  if (p.mg == 1) {
-    switch (p.mtw) {
-      case 4: launch_wide_t<4, 2, 1, 4>(p, a, st, e0, e1); break;
-      case 5: launch_wide_t<5, 2, 1, 4>(p, a, st, e0, e1); break;
-      case 6: launch_wide_t<6, 2, 1, 4>(p, a, st, e0, e1); break;
-      default: launch_wide_t<7, 2, 1, 4>(p, a, st, e0, e1); break;
-    }
-  } else {
-    switch (p.mtw) {
-      case 4: launch_wide_t<4, 4, 2, 4>(p, a, st, e0, e1); break;
-      case 5: launch_wide_t<5, 4, 2, 4>(p, a, st, e0, e1); break;
-      case 6: launch_wide_t<6, 4, 2, 4>(p, a, st, e0, e1); break;
-      default: launch_wide_t<7, 4, 2, 4>(p, a, st, e0, e1); break;
-    }
+  switch (p.mtw) {
+    case 1: launch_wide_t<1, 4, 2, 4>(p, a, st, e0, e1); break;
+    case 2: launch_wide_t<2, 4, 2, 4>(p, a, st, e0, e1); break;
+    case 3: launch_wide_t<3, 4, 2, 4>(p, a, st, e0, e1); break;
+    case 4: launch_wide_t<4, 4, 2, 4>(p, a, st, e0, e1); break;
+    case 5: launch_wide_t<5, 4, 2, 4>(p, a, st, e0, e1); break;
+    case 6: launch_wide_t<6, 4, 2, 4>(p, a, st, e0, e1); break;
+    default: launch_wide_t<7, 4, 2, 4>(p, a, st, e0, e1); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
