@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kRowThreads) void k_rowstats(SampleArgs a) {
 // ---------------------------------------------------------------- top-p
 constexpr int kToppThreads = 1024;
 constexpr int kHistCopies = 8;
-constexpr int kToppBatch = 8;            // loads issued before their atomics
+constexpr int kToppBatch = 16;           // loads of one batch (the next batch is in flight meanwhile)
 constexpr int kTieCap = 64;              // tied keys ordered by one thread
 typedef unsigned long long u64;
 
@@ -254,6 +254,30 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
     return fixed_mass(p);
   };
 
+  // Visits this thread's tokens v = tid + k * kToppThreads in order, with
+  // the loads of the next batch in flight while a batch is processed.
+  auto for_each_token = [&](auto&& f) {
+    float cur[kToppBatch], nxt[kToppBatch];
+    const int stride = kToppBatch * kToppThreads;
+#pragma unroll
+    for (int u = 0; u < kToppBatch; ++u) {
+      const int v = tid + u * kToppThreads;
+      cur[u] = v < V ? src[v] : 0.f;
+    }
+    for (int v0 = tid; v0 < V; v0 += stride) {
+#pragma unroll
+      for (int u = 0; u < kToppBatch; ++u) {
+        const int v = v0 + stride + u * kToppThreads;
+        nxt[u] = v < V ? src[v] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kToppBatch; ++u)
+        if (v0 + u * kToppThreads < V) f(v0 + u * kToppThreads, cur[u]);
+#pragma unroll
+      for (int u = 0; u < kToppBatch; ++u) cur[u] = nxt[u];
+    }
+  };
+
   uint32_t prefix = 0, pmask = 0;
   u64 above = 0;
   double thr = 0.0;
@@ -262,21 +286,10 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
     for (int i = tid; i < kHistCopies * 256; i += kToppThreads) hist[i] = 0;
     __syncthreads();
     u64* myhist = hist + (lane % kHistCopies) * 256;
-    for (int v0 = tid; v0 < V; v0 += kToppBatch * kToppThreads) {
-      float xs[kToppBatch];
-#pragma unroll
-      for (int u = 0; u < kToppBatch; ++u) {
-        const int v = v0 + u * kToppThreads;
-        xs[u] = v < V ? src[v] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < kToppBatch; ++u) {
-        if (v0 + u * kToppThreads < V) {
-          const uint32_t k = key_of(xs[u]);
-          if ((k & pmask) == prefix) atomicAdd(&myhist[(k >> shift) & 255u], mass_of(xs[u]));
-        }
-      }
-    }
+    for_each_token([&](int v, float x) {
+      const uint32_t k = key_of(x);
+      if ((k & pmask) == prefix) atomicAdd(&myhist[(k >> shift) & 255u], mass_of(x));
+    });
     __syncthreads();
     if (wave == 0) {
       // lane L holds bins 4L..4L+3; masses of higher bins live in higher lanes
@@ -328,22 +341,12 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
   // per-thread id ranges.
   if (tid == 0) { sh_tie = INT_MAX; sh_nt = 0; }
   __syncthreads();
-  for (int v0 = tid; v0 < V; v0 += kToppBatch * kToppThreads) {
-    float xs[kToppBatch];
-#pragma unroll
-    for (int u = 0; u < kToppBatch; ++u) {
-      const int v = v0 + u * kToppThreads;
-      xs[u] = v < V ? src[v] : 0.f;
+  for_each_token([&](int v, float x) {
+    if (key_of(x) == prefix) {
+      const int slot = atomicAdd(&sh_nt, 1);
+      if (slot < kTieCap) { tie_id[slot] = v; tie_m[slot] = mass_of(x); }
     }
-#pragma unroll
-    for (int u = 0; u < kToppBatch; ++u) {
-      const int v = v0 + u * kToppThreads;
-      if (v < V && key_of(xs[u]) == prefix) {
-        const int slot = atomicAdd(&sh_nt, 1);
-        if (slot < kTieCap) { tie_id[slot] = v; tie_m[slot] = mass_of(xs[u]); }
-      }
-    }
-  }
+  });
   __syncthreads();
   const int nt = sh_nt;
   if (nt <= kTieCap) {
