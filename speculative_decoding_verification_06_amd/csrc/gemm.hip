@@ -371,13 +371,21 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 // Output: fp32 partial sums P[slice][row][col].
 template <int MTW, int NTC, int MG, int CG>
 __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
-  // weight k-steps in flight per wave (even: the LDS buffer alternates):
-  // the 8-tile variant does little MFMA work per k-step, so it needs more
-  // k-steps in flight to cover HBM latency.  The 16-tile variant keeps one
-  // A register set (A is an L2 hit, one k-step ahead suffices) so that its
-  // register budget holds its ring.
-  constexpr int kWideRing = NTC >= 4 ? 4 : 8;
-  constexpr int ASETS = NTC >= 4 ? 1 : 2;
+  // Load vmcnt completes in issue order, so waiting for the activations of
+  // the next k-step also waits for every weight load issued before them:
+  // the weight ring is effectively min(kWideRing, ASETS) k-steps deep.  A
+  // k-step's A is loaded ASETS steps ahead into one of ASETS register sets.
+  // Few row tiles per wave (short k-steps, HBM bound): 4 and 4.  Many (long
+  // k-steps, MFMA bound, registers taken by accumulators): 2 and 2.
+#ifndef SV_WRING
+#define SV_WRING (MTW >= 5 ? 2 : 4)
+#endif
+#ifndef SV_WASETS
+#define SV_WASETS (MTW >= 5 ? 2 : 4)
+#endif
+  constexpr int kWideRing = SV_WRING;
+  constexpr int ASETS = SV_WASETS;
+  static_assert(kWideRing % 2 == 0 && kWideRing % ASETS == 0, "ring slots must map to fixed A sets");
   constexpr int NW = MG * CG, THREADS = 64 * NW;
   constexpr int CPT = (MTW * MG * 3 * 64 + THREADS - 1) / THREADS;   // A chunks per thread
   extern __shared__ bf16x8 lds_a[];                                   // [2][NFRP]
@@ -432,51 +440,63 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) lds_a[buf * NFRP + tid + i * THREADS] = areg[set][i];
   };
-  auto load_b = [&](int slot, int s) {
-    const int ss = min(s, s1 - 1);
+  // k-step k of the slice: weights clamped to its last step, activations
+  // from the all-zero step KS past its end, so padded steps add exactly 0
+  auto load_b = [&](int slot, int k) {
+    const int ss = s0 + min(k, nsteps - 1);
 #pragma unroll
     for (int t = 0; t < NTC; ++t) bq[slot][t] = wp[t][(size_t)ss * wstep];
   };
+  auto a_step = [&](int k) { return k < nsteps ? s0 + k : KS; };
 
   if (nsteps > 0) {
-    load_a(0, s0);
+    // The loop body has no branches (the step count is padded to a whole
+    // ring), so every s_waitcnt in it counts exactly the loads issued since
+    // the one it needs and the weight ring stays kWideRing steps deep.  A
+    // branch around a step would let the compiler assume a path on which
+    // the refilled slot is the newest load and drain the ring every step.
+    const int npad = (nsteps + kWideRing - 1) / kWideRing * kWideRing;
+    load_a(0, a_step(0));
 #pragma unroll
-    for (int u = 0; u < kWideRing; ++u) load_b(u, s0 + u);
+    for (int u = 0; u < kWideRing; ++u) load_b(u, u);
     store_a(0, 0);
-    if (ASETS == 2 && nsteps > 1) load_a(ASETS - 1, s0 + 1);
+#pragma unroll
+    for (int j = 1; j < ASETS; ++j) load_a(j, a_step(j));
     __syncthreads();
-    for (int it = 0; it < nsteps; it += kWideRing) {
+    for (int it = 0; it < npad; it += kWideRing) {
 #pragma unroll
       for (int u = 0; u < kWideRing; ++u) {
-        const int k = it + u;                 // k-step s0 + k; LDS buffer k & 1
-        if (k < nsteps) {
-          // A for k-step k + ASETS into register set (k & 1) % ASETS
-          if (k + ASETS < nsteps) load_a((u & 1) % ASETS, s0 + k + ASETS);
-          // A fragments stream from LDS one row tile (three terms) at a
-          // time, the next tile's reads issued before this tile's MFMAs.
-          // Tiles past MT repeat the last tile (no branch in the MFMA
-          // stream); their rows are never stored.
-          const bf16x8* abuf = lds_a + (u & 1) * NFRP + lane;
-          bf16x8 af[2][3];
+        const int k = it + u;                 // LDS buffer k & 1 = u & 1
+        // A for k-step k + ASETS into set k % ASETS (free: it held A(k),
+        // stored at the end of the previous step), issued first
+        load_a(u % ASETS, a_step(k + ASETS));
+        __builtin_amdgcn_sched_barrier(0);
+        // A fragments stream from LDS one row tile (three terms) at a
+        // time, the next tile's reads issued before this tile's MFMAs.
+        // Tiles past MT repeat the last tile (no branch in the MFMA
+        // stream); their rows are never stored.
+        const bf16x8* abuf = lds_a + (u & 1) * NFRP + lane;
+        bf16x8 af[2][3];
 #pragma unroll
-          for (int p = 0; p < 3; ++p) af[0][p] = abuf[(min(mg * MTW, MT - 1) * 3 + p) * 64];
+        for (int p = 0; p < 3; ++p) af[0][p] = abuf[(min(mg * MTW, MT - 1) * 3 + p) * 64];
 #pragma unroll
-          for (int i = 0; i < MTW; ++i) {
-            if (i + 1 < MTW) {
-#pragma unroll
-              for (int p = 0; p < 3; ++p)
-                af[(i + 1) & 1][p] = abuf[(min(mg * MTW + i + 1, MT - 1) * 3 + p) * 64];
-            }
+        for (int i = 0; i < MTW; ++i) {
+          if (i + 1 < MTW) {
 #pragma unroll
             for (int p = 0; p < 3; ++p)
-#pragma unroll
-              for (int t = 0; t < NTC; ++t)
-                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i & 1][p], bq[u][t], acc[i][t], 0, 0, 0);
+              af[(i + 1) & 1][p] = abuf[(min(mg * MTW + i + 1, MT - 1) * 3 + p) * 64];
           }
-          load_b(u, s0 + k + kWideRing);
-          if (k + 1 < nsteps) store_a(((u + 1) & 1) % ASETS, (u + 1) & 1);
-          __syncthreads();
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+#pragma unroll
+            for (int t = 0; t < NTC; ++t)
+              acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i & 1][p], bq[u][t], acc[i][t], 0, 0, 0);
         }
+        load_b(u, k + kWideRing);
+        // A(k + 1) to the other LDS buffer, last, so its wait comes late
+        __builtin_amdgcn_sched_barrier(0);
+        store_a((u + 1) % ASETS, (u + 1) & 1);
+        __syncthreads();
       }
     }
   }
