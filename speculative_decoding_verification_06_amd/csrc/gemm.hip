@@ -358,6 +358,130 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
   run_epilogue(a.e, M, c0, NT, res, ldr, sh_inv, nwaves, pv);
 }
 
+// ---------------------------------------------------------------- LM epilogue from registers
+// In the 16x16 MFMA C layout, register j of the 16-lane group g holds row
+// 4 g + j of a tile, one column per lane.  Each tile is reduced over its
+// group and the four tiles of a unit are merged ((t0, t1), (t2, t3)) -- the
+// order lm_unit_stats uses -- so the statistics bits match the separate
+// epilogue's.
+// Statistics of one row's unit from its four tiles (one column per lane of
+// each tile's 16-lane group); the group's first lane writes when `live`.
+__device__ __forceinline__ void unit_stats_4(const EpiArgs& e, float l0, float l1, float l2, float l3,
+                                             float q0, float q1, float q2, float q3, int n0,
+                                             bool live, int grow, int unit) {
+  const float lv[4] = {l0, l1, l2, l3}, qa[4] = {q0, q1, q2, q3};
+  const bool writer = live && (threadIdx.x & 15) == 0;
+  const size_t ts = (size_t)grow * e.G + unit;
+  if (e.tmode == 0) {
+    float v = -INFINITY;
+    int idx = 0x7fffffff;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = n0 + t * kSub;
+      const bool valid = live && n < e.N;
+      float vt = valid ? lv[t] : -INFINITY;
+      int it = valid ? n : 0x7fffffff;
+      argmax16(vt, it);
+      if (vt > v || (vt == v && it < idx)) { v = vt; idx = it; }
+    }
+    if (writer) { e.pst[2 * ts] = v; e.pst[2 * ts + 1] = 0.f; e.pidx[ts] = idx; }
+    return;
+  }
+  float mx[4], se[4], ym[4], sq[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const bool valid = live && n0 + t * kSub < e.N;
+    mx[t] = max16(valid ? lv[t] : -INFINITY);
+    se[t] = sum16(valid ? expf((lv[t] - mx[t]) * e.invT) : 0.f);
+    const float q = valid ? qa[t] : 0.f;
+    ym[t] = 0.f;
+    if (e.tmode == 1) {
+      sq[t] = sum16(q);
+    } else {
+      const float y = q > 0.f ? logf(q) * e.invT : -INFINITY;
+      ym[t] = max16(y);
+      sq[t] = sum16(q > 0.f ? expf(y - ym[t]) : 0.f);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 4; h += 2) {         // (t0, t1) and (t2, t3), then both
+    lse_merge(mx[h], se[h], mx[h + 1], se[h + 1], e.invT);
+    if (e.tmode == 1) sq[h] = sq[h] + sq[h + 1];
+    else lse_merge(ym[h], sq[h], ym[h + 1], sq[h + 1], 1.0f);
+  }
+  lse_merge(mx[0], se[0], mx[2], se[2], e.invT);
+  if (e.tmode == 1) sq[0] = sq[0] + sq[2];
+  else lse_merge(ym[0], sq[0], ym[2], sq[2], 1.0f);
+  if (writer) { e.pst[2 * ts] = mx[0]; e.pst[2 * ts + 1] = se[0]; }
+  const int b = grow / e.G1, ip = grow - b * e.G1;
+  if (writer && ip < e.gamma) {
+    const size_t tq = ((size_t)b * e.gamma + ip) * e.G + unit;
+    e.qst[2 * tq] = ym[0];
+    e.qst[2 * tq + 1] = sq[0];
+  }
+}
+
+// Draft probabilities of row tile I's items (0 for bonus rows, columns
+// past N, greedy passes).
+template <int I, int MTW>
+__device__ __forceinline__ void wide_lm_q(const EpiArgs& e, float (&qv)[4][4], int M, int MT, int mt0,
+                                          int n0, bool unit_ok) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (mt0 + I) * 16 + 4 * g + j;
+    const bool live = unit_ok && mt0 + I < MT && row < M;
+    const int grow = e.row0 + row;
+    const int b = grow / e.G1, ip = grow - b * e.G1;
+    const bool qrow = live && e.tmode != 0 && ip < e.gamma;
+    const float* qp = e.q + ((size_t)b * e.gamma + (qrow ? ip : 0)) * e.V;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = n0 + t * kSub;
+      qv[t][j] = qrow && n < e.N ? qp[n] : 0.f;
+    }
+  }
+}
+
+// Logits and statistics of row tile I, then of the tiles after it: a
+// compile-time recursion (the accumulators stay in registers only when
+// every index is a constant, and the loop would be too large to unroll),
+// with the next tile's draft probabilities loaded before this tile's work.
+template <int I, int MTW>
+__device__ __forceinline__ void wide_lm_rows(const EpiArgs& e, const f32x4 (&acc)[MTW][4],
+                                             const float (&qv)[4][4], int M, int MT, int mt0,
+                                             int unit, int n0, bool unit_ok) {
+  float qn[4][4];
+  if constexpr (I + 1 < MTW) wide_lm_q<I + 1, MTW>(e, qn, M, MT, mt0, n0, unit_ok);
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (mt0 + I) * 16 + 4 * g + j;
+    const bool live = unit_ok && mt0 + I < MT && row < M;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = n0 + t * kSub;
+      if (live && n < e.N) e.out[(size_t)row * e.ldo + n] = acc[I][t][j];
+    }
+    unit_stats_4(e, acc[I][0][j], acc[I][1][j], acc[I][2][j], acc[I][3][j], qv[0][j], qv[1][j],
+                 qv[2][j], qv[3][j], n0, live, e.row0 + row, unit);
+  }
+  if constexpr (I + 1 < MTW) wide_lm_rows<I + 1, MTW>(e, acc, qn, M, MT, mt0, unit, n0, unit_ok);
+}
+
+// The LM head's epilogue straight from a wide-GEMM wave's accumulators,
+// when one work group sums all of K for its columns.  A wave's four column
+// tiles are one 64-column statistics unit.
+template <int MTW>
+__device__ __forceinline__ void wide_lm_epilogue(const EpiArgs& e, const f32x4 (&acc)[MTW][4], int M,
+                                                 int MT, int mt0, int unit, int tiles) {
+  const int n0 = unit * 4 * kSub + (threadIdx.x & 15);   // this lane's column in tile 0
+  const bool unit_ok = unit * 4 < tiles;
+  float q0[4][4];
+  wide_lm_q<0, MTW>(e, q0, M, MT, mt0, n0, unit_ok);
+  wide_lm_rows<0, MTW>(e, acc, q0, M, MT, mt0, unit, n0, unit_ok);
+}
+
 // ---------------------------------------------------------------- wide MFMA GEMM
 // Many rows (plain packing, 11 to 224 rows): the split activations of a
 // k-step, MT row tiles x 3 terms, are staged once per work group in LDS and
@@ -370,7 +494,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 // blockIdx.y and the slices are summed, in slice order, by k_epi_wide.
 // Output: fp32 partial sums P[slice][row][col].
 template <int MTW, int NTC, int MG, int CG>
-__global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
+__global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs e) {
   // Load vmcnt completes in issue order, so waiting for the activations of
   // the next k-step also waits for every weight load issued before them:
   // the weight ring is effectively min(kWideRing, ASETS) k-steps deep.  A
@@ -499,6 +623,12 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a) {
         __syncthreads();
       }
     }
+  }
+
+  if (a.fuse_lm) {
+    static_assert(NTC == 4, "a wave's tiles form one statistics unit");
+    wide_lm_epilogue<MTW>(e, acc, M, MT, mg * MTW, blockIdx.x * CG + cg, a.tiles);
+    return;
   }
 
   // partial sums to P[slice][row][col]; C layout: lane holds rows
@@ -736,30 +866,32 @@ WidePlan plan_wide(int M, const Mat& m) {
 }
 
 template <int MTW, int NTC, int MG, int CG>
-static void launch_wide_t(const WidePlan& p, const WideArgs& a, hipStream_t st, hipEvent_t e0,
-                          hipEvent_t e1) {
+static void launch_wide_t(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
+                          hipEvent_t e0, hipEvent_t e1) {
   // the double-buffered activation tile can exceed the default 64 KiB
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&k_gemm_wide<MTW, NTC, MG, CG>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
   (void)attr;
   hipExtLaunchKernelGGL((k_gemm_wide<MTW, NTC, MG, CG>), dim3(p.colblocks, p.S),
-                        dim3(64 * MG * CG), p.lds, st, e0, e1, 0, a);
+                        dim3(64 * MG * CG), p.lds, st, e0, e1, 0, a, e);
 }
 
-hipError_t launch_wide(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
+hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e, hipStream_t st,
                        hipEvent_t e0, hipEvent_t e1) {
+  WideArgs a = a_in;
+  a.fuse_lm = p.S == 1 && e.kind == EPI_LM;
   switch (p.mtw) {
-    case 1: launch_wide_t<1, 4, 2, 4>(p, a, st, e0, e1); break;
-    case 2: launch_wide_t<2, 4, 2, 4>(p, a, st, e0, e1); break;
-    case 3: launch_wide_t<3, 4, 2, 4>(p, a, st, e0, e1); break;
-    case 4: launch_wide_t<4, 4, 2, 4>(p, a, st, e0, e1); break;
-    case 5: launch_wide_t<5, 4, 2, 4>(p, a, st, e0, e1); break;
-    case 6: launch_wide_t<6, 4, 2, 4>(p, a, st, e0, e1); break;
-    default: launch_wide_t<7, 4, 2, 4>(p, a, st, e0, e1); break;
+    case 1: launch_wide_t<1, 4, 2, 4>(p, a, e, st, e0, e1); break;
+    case 2: launch_wide_t<2, 4, 2, 4>(p, a, e, st, e0, e1); break;
+    case 3: launch_wide_t<3, 4, 2, 4>(p, a, e, st, e0, e1); break;
+    case 4: launch_wide_t<4, 4, 2, 4>(p, a, e, st, e0, e1); break;
+    case 5: launch_wide_t<5, 4, 2, 4>(p, a, e, st, e0, e1); break;
+    case 6: launch_wide_t<6, 4, 2, 4>(p, a, e, st, e0, e1); break;
+    default: launch_wide_t<7, 4, 2, 4>(p, a, e, st, e0, e1); break;
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || a.fuse_lm) return err;
   hipLaunchKernelGGL(k_epi_wide, dim3(a.tiles / 4, (a.M + 15) / 16), dim3(kEpiThreads), 0, st, a, e);
   return hipGetLastError();
 }

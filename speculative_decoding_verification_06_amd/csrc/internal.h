@@ -122,11 +122,14 @@ struct WideArgs {
   float* P = nullptr;         // [S][M][ldp] fp32 partial sums
   int ldp = 0;
   size_t slice_stride = 0;    // floats between slices
+  bool fuse_lm = false;       // LM head in one slice: the GEMM writes the
+                              // logits and unit statistics, P is unused
 };
 WidePlan plan_wide(int M, const Mat& m);
 // Row counts the wide GEMM serves: the plain packing up to one 224-row chunk.
 inline bool wide_rows(int M) { return !xs_stacked(M) && M <= 224; }
-// The GEMM (timed by e0 / e1 when given) and then its epilogue kernel.
+// The GEMM (timed by e0 / e1 when given) and then its epilogue kernel; an
+// LM head in one K slice runs its epilogue inside the GEMM.
 hipError_t launch_wide(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
                        hipEvent_t e0, hipEvent_t e1);
 // e0 / e1: null, or events that take the launch's start and end timestamps.
