@@ -5,9 +5,10 @@
 //              per-unit sums of each draft row into
 //              q' = q^(1/T) / sum ("Speculative decoding" pigeon guide, When it
 //              breaks: the same temperature / top-p on p and q)
-//   topp     : nucleus of each row by an 8-bit-digit radix select on an
-//              order-preserving key, with masses in 2^-40 fixed point so the
-//              histogram sums are exact and order independent
+//   topp     : nucleus of each row by a radix select (11, 11, 10-bit
+//              digits) on an order-preserving key, with masses in 2^-40
+//              fixed point so the histogram sums are exact and order
+//              independent
 //   decide   : ratio test r * q'(x) < p'(x) per drafted position, first
 //              rejection per sequence, then the chunk sums of the resample
 //              row (lattice-ai-eng explainer, acceptance
@@ -196,16 +197,19 @@ __global__ __launch_bounds__(kRowThreads) void k_rowstats(SampleArgs a) {
 
 // ---------------------------------------------------------------- top-p
 constexpr int kToppThreads = 1024;
-constexpr int kHistCopies = 8;
+constexpr int kToppWaves = kToppThreads / kWave;
+constexpr int kHistCopies = 4;
+constexpr int kMaxBins = 2048;           // digits of 11, 11 and 10 bits
 constexpr int kToppBatch = 16;           // loads of one batch (the next batch is in flight meanwhile)
 constexpr int kTieCap = 64;              // tied keys ordered by one thread
+constexpr int kCandPerWave = 512;        // candidate slots of each wave
 typedef unsigned long long u64;
 
 __device__ __forceinline__ u64 fixed_mass(float p) { return (u64)(p * 0x1.0p40f); }
 
 // Exclusive prefix (thread order) of a u64 over the block; integer, so exact.
 __device__ u64 block_excl_scan_u64(u64 x, u64* lds_waves) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   u64 inc = x;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -216,90 +220,153 @@ __device__ u64 block_excl_scan_u64(u64 x, u64* lds_waves) {
   __syncthreads();
   u64 base = 0;
   for (int w = 0; w < wave; ++w) base += lds_waves[w];
-  (void)nw;
   __syncthreads();
   return base + inc - x;
 }
 
-__global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool isq = row >= a.M;
-  float* ri = a.rowinfo + (size_t)row * kRowInfo;
-  const float* src = isq ? a.q + (size_t)(row - a.M) * a.V : a.logits + (size_t)row * a.ldl;
-  const float m = ri[RI_M], invZ = ri[RI_INVZ], invT = a.invT;
-  const int tmode = a.tmode, V = a.V;
-
-  // kHistCopies copies of the 256-bin histogram, lane L adding to copy
+struct ToppShared {
+  // kHistCopies copies of the digit histogram, lane L adding to copy
   // L % kHistCopies, so lanes of a wave that share a digit collide at most
   // 64 / kHistCopies ways in the LDS atomic unit
-  __shared__ u64 hist[kHistCopies * 256];
-  __shared__ u64 sh_above, sh_total, sh_zn;
-  __shared__ uint32_t sh_prefix;
-  __shared__ int sh_found, sh_tie, sh_nt;
-  __shared__ int tie_id[kTieCap];
-  __shared__ u64 tie_m[kTieCap];
-  __shared__ u64 lds_waves[kToppThreads / 64];
+  u64 hist[kHistCopies * kMaxBins];
+  // The tokens of the first digit's crossing bucket (value bits, id), each
+  // wave appending to its own segment during the second pass: they are the
+  // only ones the last pass and the tie scan can match, so when they fit
+  // those read LDS instead of the row.  Sums are integers, so the order of
+  // the candidates changes no result.
+  uint2 cand[kCandPerWave * kToppWaves];
+  u64 tie_m[kTieCap];
+  u64 lds_waves[kToppWaves];
+  u64 above, total, zn;
+  int tie_id[kTieCap];
+  int ncw[kToppWaves];
+  uint32_t prefix;
+  int found, tie, nt, overflow;
+};
+
+// Nucleus of one row (p row, or draft row when ISQ): three radix passes
+// over an order-preserving 32-bit key, 11, 11 and 10 bits, the first
+// splitting each power-of-two range of values in four so that its
+// crossing bucket is a small part of even a flat distribution.
+template <bool ISQ>
+__device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* ri = a.rowinfo + (size_t)row * kRowInfo;
+  const float* src = ISQ ? a.q + (size_t)(row - a.M) * a.V : a.logits + (size_t)row * a.ldl;
+  const float m = ri[RI_M], invZ = ri[RI_INVZ], invT = a.invT;
+  const int tmode = a.tmode, V = a.V;
 
   // Masses only place the cut, so they use the hardware exp2 / log2: p rows
   // exp2((l - m) c) / Z with c = log2(e) / T; draft rows q / Z at T == 1,
   // else exp2(log2(q) / T - m log2(e)) / Z.
   constexpr float kLog2e = 1.4426950408889634f;
   const float c = invT * kLog2e, mq = m * kLog2e;
-  auto key_of = [&](float x) -> uint32_t { return isq ? q_key(x) : logit_key(x); };
+  auto key_of = [&](float x) -> uint32_t { return ISQ ? q_key(x) : logit_key(x); };
   auto mass_of = [&](float x) -> u64 {
     float p;
-    if (!isq) p = __builtin_amdgcn_exp2f((x - m) * c) * invZ;
+    if (!ISQ) p = __builtin_amdgcn_exp2f((x - m) * c) * invZ;
     else if (tmode == 1) p = x * invZ;
     else p = x > 0.f ? __builtin_amdgcn_exp2f(__builtin_amdgcn_logf(x) * invT - mq) * invZ : 0.f;
     return fixed_mass(p);
   };
 
   // Visits this thread's tokens v = tid + k * kToppThreads in order, with
-  // the loads of the next batch in flight while a batch is processed.
+  // the loads of the next batch in flight while a batch is processed; only
+  // the last batch checks v < V per token.
   auto for_each_token = [&](auto&& f) {
+    constexpr int stride = kToppBatch * kToppThreads;
+    const int nbt = (V + stride - 1) / stride, nfull = V / stride;
     float cur[kToppBatch], nxt[kToppBatch];
-    const int stride = kToppBatch * kToppThreads;
 #pragma unroll
     for (int u = 0; u < kToppBatch; ++u) {
       const int v = tid + u * kToppThreads;
       cur[u] = v < V ? src[v] : 0.f;
     }
-    for (int v0 = tid; v0 < V; v0 += stride) {
+    for (int bt = 0; bt < nbt; ++bt) {
+      const int v0 = tid + bt * stride;
+      if (bt + 1 < nbt) {
 #pragma unroll
-      for (int u = 0; u < kToppBatch; ++u) {
-        const int v = v0 + stride + u * kToppThreads;
-        nxt[u] = v < V ? src[v] : 0.f;
+        for (int u = 0; u < kToppBatch; ++u) {
+          const int v = v0 + stride + u * kToppThreads;
+          nxt[u] = v < V ? src[v] : 0.f;
+        }
       }
+      if (bt < nfull) {
 #pragma unroll
-      for (int u = 0; u < kToppBatch; ++u)
-        if (v0 + u * kToppThreads < V) f(v0 + u * kToppThreads, cur[u]);
+        for (int u = 0; u < kToppBatch; ++u) f(v0 + u * kToppThreads, cur[u]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kToppBatch; ++u)
+          if (v0 + u * kToppThreads < V) f(v0 + u * kToppThreads, cur[u]);
+      }
 #pragma unroll
       for (int u = 0; u < kToppBatch; ++u) cur[u] = nxt[u];
     }
   };
+  // Candidates of this wave: segment cand[wave * kCandPerWave ...].
+  uint2* wcand = sh.cand + wave * kCandPerWave;
 
   uint32_t prefix = 0, pmask = 0;
   u64 above = 0;
   double thr = 0.0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kHistCopies * 256; i += kToppThreads) hist[i] = 0;
+  bool compact = false;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int bits = pass < 2 ? 11 : 10;
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = 1 << bits;
+    for (int i = tid; i < kHistCopies * nb; i += kToppThreads) sh.hist[i] = 0;
+    if (tid == 0) sh.overflow = 0;
     __syncthreads();
-    u64* myhist = hist + (lane % kHistCopies) * 256;
-    for_each_token([&](int v, float x) {
-      const uint32_t k = key_of(x);
-      if ((k & pmask) == prefix) atomicAdd(&myhist[(k >> shift) & 255u], mass_of(x));
-    });
-    __syncthreads();
-    if (wave == 0) {
-      // lane L holds bins 4L..4L+3; masses of higher bins live in higher lanes
-      u64 h[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        h[j] = 0;
-        for (int c = 0; c < kHistCopies; ++c) h[j] += hist[c * 256 + 4 * lane + j];
+    u64* myhist = sh.hist + (lane % kHistCopies) * nb;
+    if (pass == 0) {
+      for_each_token([&](int, float x) { atomicAdd(&myhist[key_of(x) >> 21], mass_of(x)); });
+    } else if (pass == 1) {
+      // histogram of the second digit within the first digit's crossing
+      // bucket, whose tokens are appended to the wave's segment (a
+      // wave-uniform count, no atomics)
+      const uint32_t p0 = prefix >> 21;
+      int wn = 0;
+      for_each_token([&](int v, float x) {
+        const uint32_t k = key_of(x);
+        const bool hit = (k >> 21) == p0;
+        if (hit) atomicAdd(&myhist[(k >> 10) & 2047u], mass_of(x));
+        const u64 mask = __ballot(hit);
+        const int slot = wn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (hit && slot < kCandPerWave) wcand[slot] = make_uint2(__float_as_uint(x), (uint32_t)v);
+        wn += __popcll(mask);
+      });
+      if (lane == 0) {
+        sh.ncw[wave] = min(wn, kCandPerWave);
+        if (wn > kCandPerWave) sh.overflow = 1;
       }
-      const u64 S = h[0] + h[1] + h[2] + h[3];
+    } else if (compact) {
+      const int n = sh.ncw[wave];
+      for (int i = lane; i < n; i += kWave) {
+        const float x = __uint_as_float(wcand[i].x);
+        const uint32_t k = key_of(x);
+        if ((k & pmask) == prefix) atomicAdd(&myhist[k & 1023u], mass_of(x));
+      }
+    } else {
+      for_each_token([&](int, float x) {
+        const uint32_t k = key_of(x);
+        if ((k & pmask) == prefix) atomicAdd(&myhist[k & 1023u], mass_of(x));
+      });
+    }
+    __syncthreads();
+    if (pass == 1) compact = sh.overflow == 0;
+    if (wave == 0) {
+      // lane L holds bins [L bpl, (L + 1) bpl); masses of higher bins live in
+      // higher lanes
+      const int bpl = nb / kWave;
+      auto bin = [&](int b) {
+        u64 t = 0;
+#pragma unroll
+        for (int cc = 0; cc < kHistCopies; ++cc) t += sh.hist[cc * nb + b];
+        return t;
+      };
+      u64 S = 0;
+      for (int j = 0; j < bpl; ++j) S += bin(lane * bpl + j);
       u64 inc = S;   // inclusive suffix sum over lanes >= L
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -308,62 +375,67 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
       }
       if (pass == 0) {
         const u64 total = __shfl(inc, 0, kWave);
-        if (lane == 0) sh_total = total;
+        if (lane == 0) sh.total = total;
         thr = (double)a.top_p * (double)total;
       }
-      if (lane == 0) sh_found = 0;
+      if (lane == 0) sh.found = 0;
       u64 cum = above + (inc - S);
       if ((double)cum < thr && (double)(cum + S) >= thr) {
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-          if ((double)(cum + h[j]) >= thr) {
-            sh_prefix = prefix | ((uint32_t)(4 * lane + j) << shift);
-            sh_above = cum;
-            sh_found = 1;
+        for (int j = bpl - 1; j >= 0; --j) {
+          const u64 hj = bin(lane * bpl + j);
+          if ((double)(cum + hj) >= thr) {
+            sh.prefix = prefix | ((uint32_t)(lane * bpl + j) << shift);
+            sh.above = cum;
+            sh.found = 1;
             break;
           }
-          cum += h[j];
+          cum += hj;
         }
       }
     }
     __syncthreads();
-    if (pass == 0) thr = (double)a.top_p * (double)sh_total;
-    if (!sh_found) return;   // no crossing (degenerate row): keep every token
-    prefix = sh_prefix;
-    pmask |= 0xffu << shift;
-    above = sh_above;
+    if (pass == 0) thr = (double)a.top_p * (double)sh.total;
+    if (!sh.found) return;   // no crossing (degenerate row): keep every token
+    prefix = sh.prefix;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    above = sh.above;
     __syncthreads();
   }
 
   // Tokens whose key equals the threshold key join in ascending id order.
-  // They are gathered (id, mass) in one coalesced pass; up to kTieCap of
-  // them are ordered by one thread, more fall back to an ordered scan over
-  // per-thread id ranges.
-  if (tid == 0) { sh_tie = INT_MAX; sh_nt = 0; }
+  // They are gathered (id, mass); up to kTieCap of them are ordered by one
+  // thread, more fall back to an ordered scan over per-thread id ranges.
+  if (tid == 0) { sh.tie = INT_MAX; sh.nt = 0; }
   __syncthreads();
-  for_each_token([&](int v, float x) {
+  auto gather_tie = [&](int v, float x) {
     if (key_of(x) == prefix) {
-      const int slot = atomicAdd(&sh_nt, 1);
-      if (slot < kTieCap) { tie_id[slot] = v; tie_m[slot] = mass_of(x); }
+      const int slot = atomicAdd(&sh.nt, 1);
+      if (slot < kTieCap) { sh.tie_id[slot] = v; sh.tie_m[slot] = mass_of(x); }
     }
-  });
+  };
+  if (compact) {
+    const int n = sh.ncw[wave];
+    for (int i = lane; i < n; i += kWave) gather_tie((int)wcand[i].y, __uint_as_float(wcand[i].x));
+  } else {
+    for_each_token(gather_tie);
+  }
   __syncthreads();
-  const int nt = sh_nt;
+  const int nt = sh.nt;
   if (nt <= kTieCap) {
     if (tid == 0) {
       // insertion sort by id, then the running mass in id order
       for (int i = 1; i < nt; ++i) {
-        const int id = tie_id[i];
-        const u64 ms = tie_m[i];
+        const int id = sh.tie_id[i];
+        const u64 ms = sh.tie_m[i];
         int j = i - 1;
-        while (j >= 0 && tie_id[j] > id) { tie_id[j + 1] = tie_id[j]; tie_m[j + 1] = tie_m[j]; --j; }
-        tie_id[j + 1] = id;
-        tie_m[j + 1] = ms;
+        while (j >= 0 && sh.tie_id[j] > id) { sh.tie_id[j + 1] = sh.tie_id[j]; sh.tie_m[j + 1] = sh.tie_m[j]; --j; }
+        sh.tie_id[j + 1] = id;
+        sh.tie_m[j + 1] = ms;
       }
       u64 cum = above;
       for (int i = 0; i < nt; ++i) {
-        cum += tie_m[i];
-        if ((double)cum >= thr) { sh_tie = tie_id[i]; sh_zn = cum; break; }
+        cum += sh.tie_m[i];
+        if ((double)cum >= thr) { sh.tie = sh.tie_id[i]; sh.zn = cum; break; }
       }
     }
   } else {
@@ -374,30 +446,36 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
       const float x = src[v];
       if (key_of(x) == prefix) local += mass_of(x);
     }
-    const u64 excl = block_excl_scan_u64(local, lds_waves);
+    const u64 excl = block_excl_scan_u64(local, sh.lds_waves);
     u64 cum = above + excl;
     for (int v = v0; v < v1; ++v) {
       const float x = src[v];
       if (key_of(x) != prefix) continue;
       cum += mass_of(x);
       if ((double)cum >= thr) {
-        atomicMin(&sh_tie, v);
+        atomicMin(&sh.tie, v);
         break;
       }
     }
     __syncthreads();
     // the thread that owns the tie cut reports the nucleus mass
-    const int tie = sh_tie;
-    if (tie >= v0 && tie < v1 && tie != INT_MAX) sh_zn = cum;
+    const int tie = sh.tie;
+    if (tie >= v0 && tie < v1 && tie != INT_MAX) sh.zn = cum;
   }
   __syncthreads();
-  const int tie = sh_tie;
+  const int tie = sh.tie;
   if (tid == 0 && tie != INT_MAX) {
     ri[RI_THR] = __uint_as_float(prefix);
     ri[RI_TIE] = __int_as_float(tie);
-    ri[RI_INVZN] = (float)((double)sh_total / (double)sh_zn);
+    ri[RI_INVZN] = (float)((double)sh.total / (double)sh.zn);
     ri[RI_NUC] = __int_as_float(1);
   }
+}
+
+__global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
+  __shared__ ToppShared sh;
+  if ((int)blockIdx.x < a.M) topp_row<false>(a, blockIdx.x, sh);
+  else topp_row<true>(a, blockIdx.x, sh);
 }
 
 // ---------------------------------------------------------------- resample helpers

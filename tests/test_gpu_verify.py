@@ -167,6 +167,47 @@ def test_rule_from_logits_parity(case):
         assert_tokens_match(n.cpu().numpy(), e.cpu().numpy(), ref, what=f"rule {case} seed {seed}")
 
 
+TOPP_PATH_CASES = [
+    # name, B, gamma, V, T, top_p, logit grid (0: continuous)
+    # a flat 600k-token row: the first digit's crossing bucket overflows the
+    # LDS candidate list, so the last pass and the tie scan read the row
+    ("candidate-overflow", 1, 2, 600000, 0.8, 0.9, 0.0),
+    # logits on a 0.5 grid: thousands of tokens share the cut key, more than
+    # one thread orders, so the tie falls back to the ordered range scan
+    ("many-ties", 2, 3, 5000, 1.0, 0.6, 0.5),
+    ("many-ties-draft-T", 2, 3, 5000, 0.7, 0.75, 0.5),
+]
+
+
+@pytest.mark.parametrize("case", TOPP_PATH_CASES, ids=[c[0] for c in TOPP_PATH_CASES])
+def test_rule_topp_paths(case):
+    name, B, gamma, V, T, top_p, grid = case
+    key = (5600 + TOPP_PATH_CASES.index(case),)
+    print(f"[case] topp path {name} B={B} gamma={gamma} V={V} T={T} top_p={top_p}", flush=True)
+    gen = synth.generator(*key, synth.T_MISC)
+    ell = gen.standard_normal((B, gamma + 1, V), dtype=np.float32) * 2.0
+    if grid > 0:
+        ell = (np.round(ell / grid) * grid).astype(np.float32)
+    q = draft_q(ell.astype(np.float64), synth.noise_np(key, B, gamma, V, 0.7))
+    if grid > 0:
+        q = (np.round(q * 2.0 ** 12) / 2.0 ** 12).astype(np.float32)   # tied draft probabilities too
+        q = (q / q.sum(-1, keepdims=True)).astype(np.float32)
+    draft = sample_drafts(q, T, top_p, key)
+    for seed in (3, 4):
+        n, e = sv.verify_from_logits(dev(ell), dev(draft), dev(q), T, top_p, seed)
+        n, e = n.cpu().numpy(), e.cpu().numpy()
+        ref = oracle.spec_verify_from_logits(ell, draft, q, T, top_p, seed)
+        if grid > 0:
+            # exact fp32 inputs and ties broken by ascending id on both sides:
+            # the oracle's near-tie band (which covers a whole tie group and
+            # would flag most ratio tests here) is no uncertainty, so every
+            # row must agree
+            assert np.array_equal(n, ref.n_accepted), f"topp {name} seed {seed}: {n} vs {ref.n_accepted}"
+            assert np.array_equal(e, ref.emitted), f"topp {name} seed {seed}"
+        else:
+            assert_tokens_match(n, e, ref, what=f"topp {name} seed {seed}")
+
+
 def test_rule_edge_cases():
     """Bad token ids, a draft outside q's support (q' = 0), and a zero
     residual (p' = q' = one-hot after top-p) that falls back to p'."""
