@@ -115,26 +115,40 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
   const int c = lane & 15;
   if (e.kind == EPI_UP) {
     // 1 / rms per row from its per-16-column sums of squares: one wave per
-    // row, each lane summing a fixed strided subset (8 independent loads in
-    // flight), then a butterfly; the order is fixed, so the bits are too
-    for (int r = wave; r < M; r += nwaves) {
-      const float* ps = e.ss_in + (size_t)r * e.ss_ld;
-      float part[8];
+    // row, each lane summing a fixed strided subset (8 independent loads),
+    // then a butterfly; the order is fixed, so the bits are too.  The
+    // wave's first row was prefetched; its next three rows are loaded
+    // together, so they cost one round trip, not three.
+    for (int r0 = wave; r0 < M; r0 += 4 * nwaves) {
+      float part[4][8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = j * kWave + lane;
-        part[j] = r == wave ? pv[j] : (t < e.ss_n ? ps[t] : 0.f);
-      }
-      for (int t0 = 8 * kWave; t0 < e.ss_n; t0 += 8 * kWave) {
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + q * nwaves;
+        const float* ps = e.ss_in + (size_t)min(r, M - 1) * e.ss_ld;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int t = t0 + j * kWave + lane;
-          part[j] += t < e.ss_n ? ps[t] : 0.f;
+          const int t = j * kWave + lane;
+          part[q][j] = (q == 0 && r == wave) ? pv[j] : (r < M && t < e.ss_n ? ps[t] : 0.f);
         }
       }
-      float s = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-      s = wave_sum(s);
-      if (lane == 0) sh_inv[r] = 1.0f / sqrtf(s * e.inv_d + e.eps);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + q * nwaves;
+        if (r < M) {
+          const float* ps = e.ss_in + (size_t)r * e.ss_ld;
+          for (int t0 = 8 * kWave; t0 < e.ss_n; t0 += 8 * kWave) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int t = t0 + j * kWave + lane;
+              part[q][j] += t < e.ss_n ? ps[t] : 0.f;
+            }
+          }
+          float s = ((part[q][0] + part[q][1]) + (part[q][2] + part[q][3])) +
+                    ((part[q][4] + part[q][5]) + (part[q][6] + part[q][7]));
+          s = wave_sum(s);
+          if (lane == 0) sh_inv[r] = 1.0f / sqrtf(s * e.inv_d + e.eps);
+        }
+      }
     }
     __syncthreads();
   }
@@ -854,9 +868,24 @@ WidePlan plan_wide(int M, const Mat& m) {
   const int ntw = p.ntc * p.cg;
   p.colblocks = (tiles + ntw - 1) / ntw;
   const int KS = m.Kp / kKStep;
-  // at least one 8-wave work group per CU
+  // K slices: one 8-wave work group fits a CU at a time, so the launch
+  // runs in rounds of SV_MIN_BLOCKS groups, and every slice adds an M x N
+  // fp32 partial sum written and read back.  Take the fewest slices (each
+  // at least 8 k-steps, dividing K evenly) whose rounds are at least 85%
+  // full, else the fullest.  Past 112 rows the MFMA work outweighs the
+  // weight stream and an idle CU is lost time, so there the launch must
+  // also fill one round (finishing groups then free CUs for the rest).
+  const bool mfma_bound = M > 112;
   int S = 1;
-  while (p.colblocks * S < SV_MIN_BLOCKS && S < 16 && KS / (2 * S) >= 8) S *= 2;
+  double best = 0.0;
+  for (int s = 1; s <= 16 && KS / s >= 8; ++s) {
+    if (KS % s != 0 && s > 1) continue;
+    const int w = p.colblocks * s;
+    const int rounds = (w + SV_MIN_BLOCKS - 1) / SV_MIN_BLOCKS;
+    const double eff = (double)w / ((double)rounds * SV_MIN_BLOCKS);
+    if (eff > best + 1e-9) { best = eff; S = s; }
+    if (eff >= 0.85 && (!mfma_bound || w >= SV_MIN_BLOCKS)) { S = s; break; }
+  }
   p.ks_slice = (KS + S - 1) / S;
   p.S = (KS + p.ks_slice - 1) / p.ks_slice;
   const int threads = 64 * p.mg * p.cg;
