@@ -200,7 +200,8 @@ constexpr int kToppThreads = 1024;
 constexpr int kToppWaves = kToppThreads / kWave;
 constexpr int kHistCopies = 4;
 constexpr int kMaxBins = 2048;           // digits of 11, 11 and 10 bits
-constexpr int kToppBatch = 16;           // loads of one batch (the next batch is in flight meanwhile)
+constexpr int kToppBatch4 = 4;           // 16-byte loads of one batch (the next batch is in flight meanwhile)
+constexpr int kToppBatch1 = 8;           // 4-byte loads of one batch, rows that are not 16-byte aligned
 constexpr int kTieCap = 64;              // tied keys ordered by one thread
 constexpr int kCandPerWave = 512;        // candidate slots of each wave
 typedef unsigned long long u64;
@@ -270,15 +271,51 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
     return fixed_mass(p);
   };
 
-  // Visits this thread's tokens v = tid + k * kToppThreads in order, with
-  // the loads of the next batch in flight while a batch is processed; only
-  // the last batch checks v < V per token.
+  // Visits every token once, with the loads of the next batch in flight
+  // while a batch is processed; only the last batch checks bounds.  Rows
+  // that allow it are read 16 bytes per lane (tokens 4 i .. 4 i + 3 of
+  // float4 i), else 4 bytes per lane.
+  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (V & 3) == 0;
   auto for_each_token = [&](auto&& f) {
-    constexpr int stride = kToppBatch * kToppThreads;
-    const int nbt = (V + stride - 1) / stride, nfull = V / stride;
-    float cur[kToppBatch], nxt[kToppBatch];
+    if (vec) {
+      constexpr int B4 = kToppBatch4;
+      constexpr int stride = B4 * kToppThreads;
+      const float4* s4 = reinterpret_cast<const float4*>(src);
+      const int V4 = V >> 2;
+      const int nbt = (V4 + stride - 1) / stride, nfull = V4 / stride;
+      float4 cur[B4], nxt[B4];
 #pragma unroll
-    for (int u = 0; u < kToppBatch; ++u) {
+      for (int u = 0; u < B4; ++u) {
+        const int i = tid + u * kToppThreads;
+        cur[u] = i < V4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      for (int bt = 0; bt < nbt; ++bt) {
+        const int i0 = tid + bt * stride;
+        if (bt + 1 < nbt) {
+#pragma unroll
+          for (int u = 0; u < B4; ++u) {
+            const int i = i0 + stride + u * kToppThreads;
+            nxt[u] = i < V4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+        const bool full = bt < nfull;
+#pragma unroll
+        for (int u = 0; u < B4; ++u) {
+          const int i = i0 + u * kToppThreads;
+          if (full || i < V4) {
+            f(4 * i, cur[u].x); f(4 * i + 1, cur[u].y); f(4 * i + 2, cur[u].z); f(4 * i + 3, cur[u].w);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < B4; ++u) cur[u] = nxt[u];
+      }
+      return;
+    }
+    constexpr int stride = kToppBatch1 * kToppThreads;
+    const int nbt = (V + stride - 1) / stride, nfull = V / stride;
+    float cur[kToppBatch1], nxt[kToppBatch1];
+#pragma unroll
+    for (int u = 0; u < kToppBatch1; ++u) {
       const int v = tid + u * kToppThreads;
       cur[u] = v < V ? src[v] : 0.f;
     }
@@ -286,21 +323,21 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
       const int v0 = tid + bt * stride;
       if (bt + 1 < nbt) {
 #pragma unroll
-        for (int u = 0; u < kToppBatch; ++u) {
+        for (int u = 0; u < kToppBatch1; ++u) {
           const int v = v0 + stride + u * kToppThreads;
           nxt[u] = v < V ? src[v] : 0.f;
         }
       }
       if (bt < nfull) {
 #pragma unroll
-        for (int u = 0; u < kToppBatch; ++u) f(v0 + u * kToppThreads, cur[u]);
+        for (int u = 0; u < kToppBatch1; ++u) f(v0 + u * kToppThreads, cur[u]);
       } else {
 #pragma unroll
-        for (int u = 0; u < kToppBatch; ++u)
+        for (int u = 0; u < kToppBatch1; ++u)
           if (v0 + u * kToppThreads < V) f(v0 + u * kToppThreads, cur[u]);
       }
 #pragma unroll
-      for (int u = 0; u < kToppBatch; ++u) cur[u] = nxt[u];
+      for (int u = 0; u < kToppBatch1; ++u) cur[u] = nxt[u];
     }
   };
   // Candidates of this wave: segment cand[wave * kCandPerWave ...].
