@@ -41,7 +41,7 @@ struct Layout {
   int M = 0, ldd = 0, ldf = 0, Vs = 0, G = 0, Gu = 0, nch = 0;
   int ksd = 0, ksf = 0;       // k-steps of the d- and ffn-wide split inputs
   size_t h = 0, xg = 0, ss = 0, act = 0, logits = 0, pst = 0, pidx = 0, qst = 0, rowinfo = 0,
-         dec = 0, csum = 0, xsd = 0, xsf = 0, part = 0, total = 0;
+         dec = 0, csum = 0, xsd = 0, xsf = 0, part = 0, rms = 0, total = 0;
 };
 
 int gemm_path(const spec_weights* w, int M) {
@@ -113,6 +113,7 @@ Layout make_layout(const spec_weights* w, int B, int gamma) {
     L.xsd = off; off = align256(off + xs_bytes(L.M, L.ksd));
     L.xsf = off; off = align256(off + xs_bytes(L.M, L.ksf));
     L.part = off; off = align256(off + wide_part_bytes(w, L.M));
+    L.rms = off; off = align256(off + sizeof(float) * M);
   }
   layout_sampling(L, B, gamma, w->V, lm_units(w, L.M), off);
   L.total = off;
@@ -268,6 +269,8 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
   float* act = at<float>(ws, L.act);
   float* logits = at<float>(ws, L.logits);
   float* part = L.part ? at<float>(ws, L.part) : nullptr;
+  // per-row 1 / rms for the wide GEMM's UP epilogue (computed once per pass)
+  float* rms = path == PATH_MFMA && wide_rows(M) ? at<float>(ws, L.rms) : nullptr;
   const int ss_ld = L.ldd / kSub;
   const int tmode = tmode_of(T);
   // split activations, for the MFMA path only
@@ -282,6 +285,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
     up.out = act; up.ldo = L.ldf; up.N = w->ffn;
     up.ss_in = ss; up.ss_ld = ss_ld; up.ss_n = ss_ld;
     up.inv_d = 1.0f / (float)w->d; up.eps = w->eps;
+    up.rms = rms;
     up.xs = xsf; up.xs_ks = L.ksf;
     err = run_gemm(w, path, w->up[l], xg, xsd, L.ldd, M, up, part, st);
     if (err != hipSuccess) break;

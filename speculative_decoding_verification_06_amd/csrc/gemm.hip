@@ -81,12 +81,34 @@ __device__ __forceinline__ float lm_item_q(const EpiArgs& e, const EpiItem& x) {
   return i < e.gamma ? e.q[((size_t)b * e.gamma + i) * e.V + x.n] : 0.f;
 }
 
+// 1 / rms of row r from its per-16-column sums of squares (one wave; the
+// result in every lane): each lane sums a fixed strided subset, then a
+// butterfly, in the order run_epilogue uses, so the bits match.
+__device__ __forceinline__ float row_inv_rms(const EpiArgs& e, int r) {
+  const int lane = threadIdx.x & 63;
+  const float* ps = e.ss_in + (size_t)r * e.ss_ld;
+  float part[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) part[j] = 0.f;
+  for (int t0 = 0; t0 < e.ss_n; t0 += 8 * kWave) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t0 + j * kWave + lane;
+      part[j] += t < e.ss_n ? ps[t] : 0.f;
+    }
+  }
+  float s = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+  s = wave_sum(s);
+  return 1.0f / sqrtf(s * e.inv_d + e.eps);
+}
+
 __device__ __forceinline__ void epi_prefetch(const EpiArgs& e, int M, int c0, int nt, int nwaves,
                                              float (&pv)[8]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < 8; ++j) pv[j] = 0.f;
   if (e.kind == EPI_UP) {
+    if (e.rms) return;
     if (wave < M) {
       const float* ps = e.ss_in + (size_t)wave * e.ss_ld;
 #pragma unroll
@@ -113,7 +135,11 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
                              float* sh_inv, int nwaves, const float (&pv)[8]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15;
-  if (e.kind == EPI_UP) {
+  if (e.kind == EPI_UP && e.rms) {
+    for (int r = wave; r < M; r += nwaves)
+      if (lane == 0) sh_inv[r] = e.rms[e.row0 + r];
+    __syncthreads();
+  } else if (e.kind == EPI_UP) {
     // 1 / rms per row from its per-16-column sums of squares: one wave per
     // row, each lane summing a fixed strided subset (8 independent loads),
     // then a butterfly; the order is fixed, so the bits are too.  The
@@ -537,6 +563,15 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs 
   const int nfr = MT * 3 * 64;
   const bf16x8* XS = reinterpret_cast<const bf16x8*>(a.XS);
   const bf16x8* W = reinterpret_cast<const bf16x8*>(a.W);
+  // UP: 1 / rms of every row once per pass, for k_epi_wide (slice 0's work
+  // groups take 16-row blocks in turn), instead of once per epilogue group
+  if (e.kind == EPI_UP && e.rms && blockIdx.y == 0) {
+    for (int rb = blockIdx.x; rb * 16 < M; rb += gridDim.x)
+      for (int r = rb * 16 + wave; r < min(M, rb * 16 + 16); r += NW) {
+        const float v = row_inv_rms(e, r);
+        if (lane == 0) e.rms[r] = v;
+      }
+  }
 
   // weight fragments of this wave's tiles: tile t of layout block b = t / nt
   const bf16x8* wp[NTC];

@@ -46,6 +46,8 @@ struct EpiArgs {
   const float* ss_in = nullptr;
   int ss_ld = 0, ss_n = 0;
   float inv_d = 0.f, eps = 0.f;
+  float* rms = nullptr;       // UP, wide path: 1 / rms of every row of the pass,
+                              // written by the GEMM, read by its epilogue
   // DOWN: next block's normalised input and its sums of squares
   float* xg = nullptr;
   const float* gain_next = nullptr;   // null: last block
