@@ -522,6 +522,143 @@ __device__ __forceinline__ void wide_lm_epilogue(const EpiArgs& e, const f32x4 (
   wide_lm_rows<0, MTW>(e, acc, q0, M, MT, mt0, unit, n0, unit_ok);
 }
 
+// Two-tile variant (NTC = 2: a 64-column unit spans the tiles of waves
+// 2u and 2u + 1).  Each wave reduces its two tiles of a row and merges
+// them (t0, t1) or (t2, t3); the halves meet in LDS and are merged last,
+// the order lm_unit_stats uses.
+struct HalfStats { float mx, se, ym, sq; };   // greedy: mx = max logit, se = argmax id bits
+
+__device__ __forceinline__ HalfStats half_stats_2(const EpiArgs& e, float l0, float l1, float q0,
+                                                  float q1, int n0, bool live) {
+  const float lv[2] = {l0, l1}, qa[2] = {q0, q1};
+  HalfStats h;
+  if (e.tmode == 0) {
+    float v = -INFINITY;
+    int idx = 0x7fffffff;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int n = n0 + t * kSub;
+      const bool valid = live && n < e.N;
+      float vt = valid ? lv[t] : -INFINITY;
+      int it = valid ? n : 0x7fffffff;
+      argmax16(vt, it);
+      if (vt > v || (vt == v && it < idx)) { v = vt; idx = it; }
+    }
+    h.mx = v; h.se = __int_as_float(idx); h.ym = 0.f; h.sq = 0.f;
+    return h;
+  }
+  float mx[2], se[2], ym[2], sq[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const bool valid = live && n0 + t * kSub < e.N;
+    mx[t] = max16(valid ? lv[t] : -INFINITY);
+    se[t] = sum16(valid ? expf((lv[t] - mx[t]) * e.invT) : 0.f);
+    const float q = valid ? qa[t] : 0.f;
+    ym[t] = 0.f;
+    if (e.tmode == 1) {
+      sq[t] = sum16(q);
+    } else {
+      const float y = q > 0.f ? logf(q) * e.invT : -INFINITY;
+      ym[t] = max16(y);
+      sq[t] = sum16(q > 0.f ? expf(y - ym[t]) : 0.f);
+    }
+  }
+  lse_merge(mx[0], se[0], mx[1], se[1], e.invT);
+  if (e.tmode == 1) sq[0] = sq[0] + sq[1];
+  else lse_merge(ym[0], sq[0], ym[1], sq[1], 1.0f);
+  h.mx = mx[0]; h.se = se[0]; h.ym = ym[0]; h.sq = sq[0];
+  return h;
+}
+
+// Draft probabilities of row tile I's items, two tiles.
+template <int I, int MTW>
+__device__ __forceinline__ void wide_lm_q2(const EpiArgs& e, float (&qv)[2][4], int M, int MT, int mt0,
+                                           int n0, bool unit_ok) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (mt0 + I) * 16 + 4 * g + j;
+    const bool live = unit_ok && mt0 + I < MT && row < M;
+    const int grow = e.row0 + row;
+    const int b = grow / e.G1, ip = grow - b * e.G1;
+    const bool qrow = live && e.tmode != 0 && ip < e.gamma;
+    const float* qp = e.q + ((size_t)b * e.gamma + (qrow ? ip : 0)) * e.V;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int n = n0 + t * kSub;
+      qv[t][j] = qrow && n < e.N ? qp[n] : 0.f;
+    }
+  }
+}
+
+// Logits and half-unit statistics (to LDS half[row]) of row tile I, then
+// of the tiles after it; the next tile's draft probabilities load first.
+template <int I, int MTW>
+__device__ __forceinline__ void wide_lm_rows2(const EpiArgs& e, const f32x4 (&acc)[MTW][2],
+                                              const float (&qv)[2][4], int M, int MT, int mt0,
+                                              int n0, bool unit_ok, float4* half) {
+  float qn[2][4];
+  if constexpr (I + 1 < MTW) wide_lm_q2<I + 1, MTW>(e, qn, M, MT, mt0, n0, unit_ok);
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (mt0 + I) * 16 + 4 * g + j;
+    const bool live = unit_ok && mt0 + I < MT && row < M;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int n = n0 + t * kSub;
+      if (live && n < e.N) e.out[(size_t)row * e.ldo + n] = acc[I][t][j];
+    }
+    const HalfStats h = half_stats_2(e, acc[I][0][j], acc[I][1][j], qv[0][j], qv[1][j], n0, live);
+    if ((threadIdx.x & 15) == 0 && mt0 + I < MT) half[row] = make_float4(h.mx, h.se, h.ym, h.sq);
+  }
+  if constexpr (I + 1 < MTW)
+    wide_lm_rows2<I + 1, MTW>(e, acc, qn, M, MT, mt0, n0, unit_ok, half);
+}
+
+// LM epilogue of the two-tile wide GEMM: CG waves, CG / 2 units per work
+// group, rows of all MG row groups; hbuf is LDS for CG * R float4 (R rows).
+template <int MTW, int CG>
+__device__ __forceinline__ void wide_lm_epilogue2(const EpiArgs& e, const f32x4 (&acc)[MTW][2], int M,
+                                                  int MT, int mt0, int cg, int tiles, float4* hbuf,
+                                                  int R) {
+  const int unit = blockIdx.x * (CG / 2) + cg / 2;
+  const int n0 = (unit * 4 + 2 * (cg & 1)) * kSub + (threadIdx.x & 15);
+  const bool unit_ok = unit * 4 < tiles;
+  float q0[2][4];
+  wide_lm_q2<0, MTW>(e, q0, M, MT, mt0, n0, unit_ok);
+  wide_lm_rows2<0, MTW>(e, acc, q0, M, MT, mt0, n0, unit_ok, hbuf + cg * R);
+  __syncthreads();
+  for (int k = threadIdx.x; k < (CG / 2) * M; k += blockDim.x) {
+    const int u = k / M, row = k - u * M;
+    const int ug = blockIdx.x * (CG / 2) + u;
+    if (ug * 4 >= tiles) continue;
+    float4 lo = hbuf[(2 * u) * R + row];
+    const float4 hi = hbuf[(2 * u + 1) * R + row];
+    const int grow = e.row0 + row;
+    const size_t ts = (size_t)grow * e.G + ug;
+    if (e.tmode == 0) {
+      const int li = __float_as_int(lo.y), hi_i = __float_as_int(hi.y);
+      if (hi.x > lo.x || (hi.x == lo.x && hi_i < li)) { lo.x = hi.x; lo.y = hi.y; }
+      e.pst[2 * ts] = lo.x;
+      e.pst[2 * ts + 1] = 0.f;
+      e.pidx[ts] = __float_as_int(lo.y);
+      continue;
+    }
+    lse_merge(lo.x, lo.y, hi.x, hi.y, e.invT);
+    if (e.tmode == 1) lo.w = lo.w + hi.w;
+    else lse_merge(lo.z, lo.w, hi.z, hi.w, 1.0f);
+    e.pst[2 * ts] = lo.x;
+    e.pst[2 * ts + 1] = lo.y;
+    const int b = grow / e.G1, ip = grow - b * e.G1;
+    if (ip < e.gamma) {
+      const size_t tq = ((size_t)b * e.gamma + ip) * e.G + ug;
+      e.qst[2 * tq] = lo.z;
+      e.qst[2 * tq + 1] = lo.w;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- wide MFMA GEMM
 // Many rows (plain packing, 11 to 224 rows): the split activations of a
 // k-step, MT row tiles x 3 terms, are staged once per work group in LDS and
@@ -675,8 +812,16 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs 
   }
 
   if (a.fuse_lm) {
-    static_assert(NTC == 4, "a wave's tiles form one statistics unit");
-    wide_lm_epilogue<MTW>(e, acc, M, MT, mg * MTW, blockIdx.x * CG + cg, a.tiles);
+    static_assert(NTC == 4 || (NTC == 2 && CG % 2 == 0), "units of four tiles per wave or wave pair");
+    if constexpr (NTC == 4) {
+      wide_lm_epilogue<MTW>(e, acc, M, MT, mg * MTW, blockIdx.x * CG + cg, a.tiles);
+    } else {
+      // the A buffers hold the half-unit statistics (free after the k-loop)
+      constexpr int R = MG * MTW * 16;
+      static_assert(CG * R * 16 <= 2 * NFRP * 16, "LDS for the half-unit statistics");
+      wide_lm_epilogue2<MTW, CG>(e, acc, M, MT, mg * MTW, cg, a.tiles,
+                                 reinterpret_cast<float4*>(lds_a), R);
+    }
     return;
   }
 
@@ -899,6 +1044,11 @@ WidePlan plan_wide(int M, const Mat& m) {
   // two row groups x 4 column groups of 4 tiles = 16 column tiles, 8 waves
   p.mtw = (p.MT + 1) / 2;
   p.mg = 2; p.ntc = 4; p.cg = 4;
+  if (p.MT <= 5) {
+    // up to 80 rows: one row group of MT tiles (no padding tile), 8 column
+    // groups of 2 tiles, so no two waves load the same weight tile
+    p.mtw = p.MT; p.mg = 1; p.ntc = 2; p.cg = 8;
+  }
   const int tiles = m.Np / kSub;
   const int ntw = p.ntc * p.cg;
   p.colblocks = (tiles + ntw - 1) / ntw;
@@ -945,14 +1095,22 @@ hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e
                        hipEvent_t e0, hipEvent_t e1) {
   WideArgs a = a_in;
   a.fuse_lm = p.S == 1 && e.kind == EPI_LM;
-  switch (p.mtw) {
-    case 1: launch_wide_t<1, 4, 2, 4>(p, a, e, st, e0, e1); break;
-    case 2: launch_wide_t<2, 4, 2, 4>(p, a, e, st, e0, e1); break;
+  if (p.mg == 1) {
+    switch (p.mtw) {
+      case 1: launch_wide_t<1, 2, 1, 8>(p, a, e, st, e0, e1); break;
+      case 2: launch_wide_t<2, 2, 1, 8>(p, a, e, st, e0, e1); break;
+      case 3: launch_wide_t<3, 2, 1, 8>(p, a, e, st, e0, e1); break;
+      case 4: launch_wide_t<4, 2, 1, 8>(p, a, e, st, e0, e1); break;
+      default: launch_wide_t<5, 2, 1, 8>(p, a, e, st, e0, e1); break;
+    }
+  } else {
+    switch (p.mtw) {   // 6 to 14 row tiles: mtw = 3 .. 7
     case 3: launch_wide_t<3, 4, 2, 4>(p, a, e, st, e0, e1); break;
     case 4: launch_wide_t<4, 4, 2, 4>(p, a, e, st, e0, e1); break;
     case 5: launch_wide_t<5, 4, 2, 4>(p, a, e, st, e0, e1); break;
     case 6: launch_wide_t<6, 4, 2, 4>(p, a, e, st, e0, e1); break;
     default: launch_wide_t<7, 4, 2, 4>(p, a, e, st, e0, e1); break;
+    }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.fuse_lm) return err;
