@@ -686,6 +686,12 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs 
 #endif
   constexpr int kWideRing = SV_WRING;
   constexpr int ASETS = SV_WASETS;
+  // Long k-steps (two row groups): with A loaded two or more steps ahead,
+  // the next step's A goes to LDS after the first row tile, so the wait for
+  // its writes is not at the barrier, where both waves of a SIMD would idle
+  // the MFMA pipe.  (Measured: +2% greedy; the short one-row-group k-steps
+  // of 72 rows lose 1%, so they store last.)
+  constexpr bool kEarlyStore = ASETS >= 2 && MG == 2;
   static_assert(kWideRing % 2 == 0 && kWideRing % ASETS == 0, "ring slots must map to fixed A sets");
   constexpr int NW = MG * CG, THREADS = 64 * NW;
   constexpr int CPT = (MTW * MG * 3 * 64 + THREADS - 1) / THREADS;   // A chunks per thread
@@ -801,11 +807,20 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs 
 #pragma unroll
             for (int t = 0; t < NTC; ++t)
               acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i & 1][p], bq[u][t], acc[i][t], 0, 0, 0);
+          if (kEarlyStore && i == 0) {
+            // A(k + 1), loaded a step ago, to the other LDS buffer early:
+            // its writes have landed long before the barrier
+            __builtin_amdgcn_sched_barrier(0);
+            store_a((u + 1) % ASETS, (u + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         load_b(u, k + kWideRing);
-        // A(k + 1) to the other LDS buffer, last, so its wait comes late
-        __builtin_amdgcn_sched_barrier(0);
-        store_a((u + 1) % ASETS, (u + 1) & 1);
+        if (!kEarlyStore) {
+          // A(k + 1) to the other LDS buffer, last, so its wait comes late
+          __builtin_amdgcn_sched_barrier(0);
+          store_a((u + 1) % ASETS, (u + 1) & 1);
+        }
         __syncthreads();
       }
     }
