@@ -78,6 +78,11 @@ CASES = [
     ("bf16-mfma-rows-topp", 8, 8, 256, 512, 2000, 1, "bf16", 0.7, 0.9, False, {}),
     ("bf16-mfma-chunked", 40, 6, 128, 256, 500, 1, "bf16", 1.3, 0.6, False, {}),
     ("bf16-wide-two-row-groups", 20, 6, 192, 320, 900, 2, "bf16", 1.0, 1.0, True, {}),
+    # wide GEMM shapes: one row group of 1 row tile (12 rows), two row groups
+    # of 3 and of 4 row tiles (90 and 120 rows)
+    ("bf16-wide-one-tile", 4, 2, 160, 224, 650, 1, "bf16", 0.8, 0.9, True, {}),
+    ("bf16-wide-90-rows", 10, 8, 128, 256, 600, 1, "bf16", 1.0, 1.0, False, {}),
+    ("bf16-wide-120-rows-greedy", 15, 7, 128, 192, 520, 2, "bf16", 0.0, 1.0, True, {}),
     ("bf16-wide-224-greedy", 32, 6, 160, 288, 700, 1, "bf16", 0.0, 1.0, False, {}),
     ("bf16-fma", 2, 4, 192, 448, 900, 2, "bf16", 1.0, 1.0, True,
      {"keep_rowmajor": True, "mfma_min_rows": 10 ** 6}),
