@@ -1070,21 +1070,31 @@ WidePlan plan_wide(int M, const Mat& m) {
   const int KS = m.Kp / kKStep;
   // K slices: one 8-wave work group fits a CU at a time, so the launch
   // runs in rounds of SV_MIN_BLOCKS groups, and every slice adds an M x N
-  // fp32 partial sum written and read back.  Take the fewest slices (each
-  // at least 8 k-steps, dividing K evenly) whose rounds are at least 85%
-  // full, else the fullest.  Past 112 rows the MFMA work outweighs the
-  // weight stream and an idle CU is lost time, so there the launch must
-  // also fill one round (finishing groups then free CUs for the rest).
+  // fp32 partial sum written and read back.  Each slice is at least 8
+  // k-steps and divides K evenly.  Up to 112 rows the weight stream bounds
+  // the launch: take the fewest slices whose rounds are at least 85% full,
+  // else the fullest.  Past 112 rows the MFMA work bounds it and every CU
+  // runs at its own rate: minimise a cost in k-steps, rounds x (slice
+  // length + 2 for a group's start and its partial-sum stores) plus N/6000
+  // per slice for the partial's round trip through HBM (a k-step and the
+  // partial both scale with M, so M drops out).  Measured at 224 rows, two
+  // slices of 128 k-steps in 224 groups beat four of 64 in 448 groups by
+  // 3% of the pass, and sixteen slices lose 10%.
   const bool mfma_bound = M > 112;
   int S = 1;
-  double best = 0.0;
+  double best = 0.0, best_cost = -1.0;
   for (int s = 1; s <= 16 && KS / s >= 8; ++s) {
     if (KS % s != 0 && s > 1) continue;
     const int w = p.colblocks * s;
     const int rounds = (w + SV_MIN_BLOCKS - 1) / SV_MIN_BLOCKS;
+    if (mfma_bound) {
+      const double cost = rounds * (double)((KS + s - 1) / s + 2) + s * (double)m.Np / 6000.0;
+      if (best_cost < 0.0 || cost < best_cost - 1e-9) { best_cost = cost; S = s; }
+      continue;
+    }
     const double eff = (double)w / ((double)rounds * SV_MIN_BLOCKS);
     if (eff > best + 1e-9) { best = eff; S = s; }
-    if (eff >= 0.85 && (!mfma_bound || w >= SV_MIN_BLOCKS)) { S = s; break; }
+    if (eff >= 0.85) { S = s; break; }
   }
   p.ks_slice = (KS + S - 1) / S;
   p.S = (KS + p.ks_slice - 1) / p.ks_slice;
