@@ -670,22 +670,16 @@ __device__ __forceinline__ void wide_lm_epilogue2(const EpiArgs& e, const f32x4 
 // ring.  When the column blocks cannot fill the chip, K is split over
 // blockIdx.y and the slices are summed, in slice order, by k_epi_wide.
 // Output: fp32 partial sums P[slice][row][col].
-template <int MTW, int NTC, int MG, int CG>
+template <int MTW, int NTC, int MG, int CG, int RING>
 __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs e) {
   // Load vmcnt completes in issue order, so waiting for the activations of
   // the next k-step also waits for every weight load issued before them:
-  // the weight ring is effectively min(kWideRing, ASETS) k-steps deep.  A
-  // k-step's A is loaded ASETS steps ahead into one of ASETS register sets.
-  // Few row tiles per wave (short k-steps, HBM bound): 4 and 4.  Many (long
-  // k-steps, MFMA bound, registers taken by accumulators): 2 and 2.
-#ifndef SV_WRING
-#define SV_WRING (MTW >= 5 ? 2 : 4)
-#endif
-#ifndef SV_WASETS
-#define SV_WASETS (MTW >= 5 ? 2 : 4)
-#endif
-  constexpr int kWideRing = SV_WRING;
-  constexpr int ASETS = SV_WASETS;
+  // a weight ring deeper than the A register sets would gain nothing, so
+  // both are RING deep: a k-step's A is loaded RING steps ahead into one
+  // of RING register sets.  4 where the registers allow it, 2 where the
+  // accumulators take them or two groups must share a CU.
+  constexpr int kWideRing = RING;
+  constexpr int ASETS = RING;
   // Long k-steps (two row groups): with A loaded two or more steps ahead,
   // the next step's A goes to LDS after the first row tile, so the wait for
   // its writes is not at the barrier, where both waves of a SIMD would idle
@@ -1104,15 +1098,15 @@ WidePlan plan_wide(int M, const Mat& m) {
   return p;
 }
 
-template <int MTW, int NTC, int MG, int CG>
+template <int MTW, int NTC, int MG, int CG, int RING = (MTW >= 5 ? 2 : 4)>
 static void launch_wide_t(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
                           hipEvent_t e0, hipEvent_t e1) {
   // the double-buffered activation tile can exceed the default 64 KiB
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm_wide<MTW, NTC, MG, CG>),
+      reinterpret_cast<const void*>(&k_gemm_wide<MTW, NTC, MG, CG, RING>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
   (void)attr;
-  hipExtLaunchKernelGGL((k_gemm_wide<MTW, NTC, MG, CG>), dim3(p.colblocks, p.S),
+  hipExtLaunchKernelGGL((k_gemm_wide<MTW, NTC, MG, CG, RING>), dim3(p.colblocks, p.S),
                         dim3(64 * MG * CG), p.lds, st, e0, e1, 0, a, e);
 }
 
@@ -1126,7 +1120,13 @@ hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e
       case 2: launch_wide_t<2, 2, 1, 8>(p, a, e, st, e0, e1); break;
       case 3: launch_wide_t<3, 2, 1, 8>(p, a, e, st, e0, e1); break;
       case 4: launch_wide_t<4, 2, 1, 8>(p, a, e, st, e0, e1); break;
-      default: launch_wide_t<5, 2, 1, 8>(p, a, e, st, e0, e1); break;
+      default:
+        // a 4-deep ring takes 137 registers: one group per CU.  Where
+        // more groups than CUs are launched (the LM head), two groups per
+        // CU with a 2-deep ring stream faster.
+        if (p.colblocks * p.S > SV_MIN_BLOCKS) launch_wide_t<5, 2, 1, 8, 2>(p, a, e, st, e0, e1);
+        else launch_wide_t<5, 2, 1, 8, 4>(p, a, e, st, e0, e1);
+        break;
     }
   } else {
     switch (p.mtw) {   // 6 to 14 row tiles: mtw = 3 .. 7
