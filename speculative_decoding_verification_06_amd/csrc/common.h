@@ -157,23 +157,47 @@ __device__ __forceinline__ uint32_t logit_key(float x) {
 }
 
 // ---- 16-lane group reductions (one MFMA column tile = 16 lanes) ----------
+// A 16-lane group is one DPP row, so the butterfly runs on row rotations
+// (VALU operands, no trip through the LDS crossbar as ds_bpermute takes).
+// Rotating by 8 pairs lane i with lane i ^ 8.  Each step combines a lane's
+// value with its partner's by a commutative rule, so afterwards lanes i and
+// i ^ 8 hold the same value: the data has period 8, and rotating by 4 then
+// reads, in lane i, the value lane i ^ 4 holds; likewise for 2 and 1.  The
+// result is therefore bit for bit the xor butterfly's (for NaN-free data,
+// where the argmax rule is commutative).
+template <int N>
+__device__ __forceinline__ int row_ror_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x120 + N, 0xF, 0xF, false);   // DPP row_ror:N
+}
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(row_ror_i<N>(__float_as_int(v)));
+}
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
   return v;
 }
 __device__ __forceinline__ float max16(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  v = fmaxf(v, row_ror<1>(v));
   return v;
 }
+template <int N>
+__device__ __forceinline__ void argmax_step(float& v, int& idx) {
+  const float ov = row_ror<N>(v);
+  const int oi = row_ror_i<N>(idx);
+  if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+}
 __device__ __forceinline__ void argmax16(float& v, int& idx) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, kWave);
-    const int oi = __shfl_xor(idx, o, kWave);
-    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
-  }
+  argmax_step<8>(v, idx);
+  argmax_step<4>(v, idx);
+  argmax_step<2>(v, idx);
+  argmax_step<1>(v, idx);
 }
 
 // Softmax / argmax statistics of one unit of U adjacent 16-column logits

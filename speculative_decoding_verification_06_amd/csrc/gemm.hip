@@ -971,7 +971,7 @@ __global__ __launch_bounds__(kFmaThreads) void k_gemm_fma(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float v = acc[m][j];
-        v += __shfl_xor(v, 8, kWave);
+        v += row_ror<8>(v);                 // lane i ^ 8 of the 16-lane row
         v += __shfl_xor(v, 16, kWave);
         v += __shfl_xor(v, 32, kWave);
         acc[m][j] = v;
