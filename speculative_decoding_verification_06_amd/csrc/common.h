@@ -103,60 +103,7 @@ __device__ __forceinline__ void row_uniforms(uint64_t seed, int b, int i, float&
   u = (float)(uint32_t)(c[1] >> 40) * 0x1.0p-24f;
 }
 
-// ---- wave reductions (butterfly, identical result in every lane) ---------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-// Max with the lowest index among equal maxima.
-__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, kWave);
-    const int oi = __shfl_xor(idx, o, kWave);
-    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
-  }
-}
-__device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-// Online-softmax merge of (max, sum of exp((x - max) * invT)) pairs.
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2, float invT) {
-  if (s2 == 0.0f) return;
-  if (s == 0.0f) { m = m2; s = s2; return; }
-  if (m2 > m) { s = s * expf((m - m2) * invT) + s2; m = m2; }
-  else { s = s + s2 * expf((m2 - m) * invT); }
-}
-__device__ __forceinline__ void wave_lse(float& m, float& s, float invT) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, kWave);
-    const float s2 = __shfl_xor(s, o, kWave);
-    // merge in a lane-independent order so every lane gets the same bits
-    float am = m, as = s, bm = m2, bs = s2;
-    const bool swap = (threadIdx.x & o) != 0;
-    if (swap) { am = m2; as = s2; bm = m; bs = s; }
-    lse_merge(am, as, bm, bs, invT);
-    m = am; s = as;
-  }
-}
-
-// Order-preserving map of an fp32 logit to uint32 (larger value, larger key).
-__device__ __forceinline__ uint32_t logit_key(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// ---- 16-lane group reductions (one MFMA column tile = 16 lanes) ----------
+// ---- cross-lane steps ------------------------------------------------------
 // A 16-lane group is one DPP row, so the butterfly runs on row rotations
 // (VALU operands, no trip through the LDS crossbar as ds_bpermute takes).
 // Rotating by 8 pairs lane i with lane i ^ 8.  Each step combines a lane's
@@ -173,6 +120,7 @@ template <int N>
 __device__ __forceinline__ float row_ror(float v) {
   return __int_as_float(row_ror_i<N>(__float_as_int(v)));
 }
+// ---- 16-lane group reductions (one MFMA column tile = 16 lanes) ----------
 __device__ __forceinline__ float sum16(float v) {
   v += row_ror<8>(v);
   v += row_ror<4>(v);
@@ -199,6 +147,72 @@ __device__ __forceinline__ void argmax16(float& v, int& idx) {
   argmax_step<2>(v, idx);
   argmax_step<1>(v, idx);
 }
+
+// ---- wave reductions (butterfly, identical result in every lane) ---------
+// Offsets 32 and 16 cross DPP rows (ds_bpermute); 8, 4, 2 and 1 run on row
+// rotations in the same order, which gives the same bits (see above).
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __shfl_xor(v, 32, kWave);
+  v += __shfl_xor(v, 16, kWave);
+  return sum16(v);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  return max16(v);
+}
+// Max with the lowest index among equal maxima.
+__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 8; o >>= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(idx, o, kWave);
+    if (ov > v || (ov == v && oi < idx)) { v = ov; idx = oi; }
+  }
+  argmax16(v, idx);
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+  v = min(v, __shfl_xor(v, 32, kWave));
+  v = min(v, __shfl_xor(v, 16, kWave));
+  v = min(v, row_ror_i<8>(v));
+  v = min(v, row_ror_i<4>(v));
+  v = min(v, row_ror_i<2>(v));
+  v = min(v, row_ror_i<1>(v));
+  return v;
+}
+
+// Online-softmax merge of (max, sum of exp((x - max) * invT)) pairs.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2, float invT) {
+  if (s2 == 0.0f) return;
+  if (s == 0.0f) { m = m2; s = s2; return; }
+  if (m2 > m) { s = s * expf((m - m2) * invT) + s2; m = m2; }
+  else { s = s + s2 * expf((m2 - m) * invT); }
+}
+// One butterfly step of wave_lse: partner values m2, s2 from lane i ^ O.
+template <int O>
+__device__ __forceinline__ void lse_step(float& m, float& s, float m2, float s2, float invT) {
+  // merge in a lane-independent order so every lane gets the same bits
+  float am = m, as = s, bm = m2, bs = s2;
+  const bool swap = (threadIdx.x & O) != 0;
+  if (swap) { am = m2; as = s2; bm = m; bs = s; }
+  lse_merge(am, as, bm, bs, invT);
+  m = am; s = as;
+}
+__device__ __forceinline__ void wave_lse(float& m, float& s, float invT) {
+  lse_step<32>(m, s, __shfl_xor(m, 32, kWave), __shfl_xor(s, 32, kWave), invT);
+  lse_step<16>(m, s, __shfl_xor(m, 16, kWave), __shfl_xor(s, 16, kWave), invT);
+  lse_step<8>(m, s, row_ror<8>(m), row_ror<8>(s), invT);
+  lse_step<4>(m, s, row_ror<4>(m), row_ror<4>(s), invT);
+  lse_step<2>(m, s, row_ror<2>(m), row_ror<2>(s), invT);
+  lse_step<1>(m, s, row_ror<1>(m), row_ror<1>(s), invT);
+}
+
+// Order-preserving map of an fp32 logit to uint32 (larger value, larger key).
+__device__ __forceinline__ uint32_t logit_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 
 // Softmax / argmax statistics of one unit of U adjacent 16-column logits
 // tiles of a row (U = 1, 2 or 4), one column per lane; the U tiles sit in

@@ -559,16 +559,20 @@ __device__ __forceinline__ float res_weight_lq(const ResRow& rr, int v, float l,
   return fmaxf(pv - qq, 0.f);
 }
 
-__device__ __forceinline__ ResRow make_row(const SampleArgs& a, int b, int j, bool use_p) {
+// ri_seq: the sequence's row statistics in LDS (local rows: p rows 0..gamma,
+// then the gamma q rows), else null for the global table.
+__device__ __forceinline__ ResRow make_row(const SampleArgs& a, int b, int j, bool use_p,
+                                           const float* ri_seq = nullptr) {
   const int G1 = a.gamma + 1;
   const size_t prow = (size_t)b * G1 + j;
   ResRow rr;
   rr.l = a.logits + prow * a.ldl;
-  rr.rip = a.rowinfo + prow * kRowInfo;
+  rr.rip = ri_seq ? ri_seq + j * kRowInfo : a.rowinfo + prow * kRowInfo;
   rr.hasq = j < a.gamma;
   const size_t qrow = (size_t)b * a.gamma + (rr.hasq ? j : 0);
   rr.q = a.q + qrow * a.V;
-  rr.riq = a.rowinfo + ((size_t)a.M + qrow) * kRowInfo;
+  rr.riq = ri_seq ? ri_seq + (G1 + (rr.hasq ? j : 0)) * kRowInfo
+                  : a.rowinfo + ((size_t)a.M + qrow) * kRowInfo;
   rr.use_p = use_p;
   rr.tmode = a.tmode;
   rr.invT = a.invT;
@@ -604,6 +608,85 @@ __device__ __forceinline__ void load_chunk(const SampleArgs& a, const ResRow& rr
 }
 
 // ---------------------------------------------------------------- decide + chunk sums
+// Row statistics inside the decide kernel (no top-p, few short rows): every
+// work group of sequence b merges the unit statistics of the sequence's
+// 2 gamma + 1 rows itself, a wave per row, the same way in every group, so
+// all groups hold the same bits; chunk 0 also writes them to the row table
+// for the resample and the debug dumps.  This saves a launch and a memory
+// round trip where the rows are short.
+constexpr int kFuseRowsPerWave = 3;
+constexpr int kFuseUnitsPerLane = 8;
+
+bool fuse_rowstats(const SampleArgs& a, int threads) {
+  return a.tmode != 0 && !(a.top_p < 1.0f) &&
+         2 * a.gamma + 1 <= kFuseRowsPerWave * (threads / kWave) &&
+         a.Gu <= kFuseUnitsPerLane * kWave;
+}
+
+// (max, 1 / Z) of the local rows of sequence b taken by this wave (rows
+// wave, wave + nw, ...), as k_rowstats defines them, into ri_seq.  Two
+// plain reductions per row instead of an online merge: the row max M over
+// the units' maxima, then Z = sum over units of s * exp((m - M) / T).  The
+// rows of a wave are reduced side by side.
+__device__ void seq_rowstats(const SampleArgs& a, int b, float* ri_seq, bool publish) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int G1 = a.gamma + 1, nrows = 2 * a.gamma + 1;
+  float2 v[kFuseRowsPerWave][kFuseUnitsPerLane];
+  // every load first: one memory round trip for all of the wave's rows
+#pragma unroll
+  for (int k = 0; k < kFuseRowsPerWave; ++k) {
+    const int r = min(wave + k * nw, nrows - 1);
+    const bool isq = r >= G1;
+    const size_t srow = isq ? (size_t)b * a.gamma + (r - G1) : (size_t)b * G1 + r;
+    const float2* st = reinterpret_cast<const float2*>(isq ? a.qst : a.pst) + srow * a.G;
+#pragma unroll
+    for (int u = 0; u < kFuseUnitsPerLane; ++u) {
+      const int t = lane + u * kWave;
+      v[k][u] = t < a.Gu ? st[t] : make_float2(-INFINITY, 0.f);
+    }
+  }
+  float mx[kFuseRowsPerWave], z[kFuseRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kFuseRowsPerWave; ++k) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kFuseUnitsPerLane; ++u)
+      if (v[k][u].y > 0.f) m = fmaxf(m, v[k][u].x);
+    mx[k] = wave_max(m);
+  }
+#pragma unroll
+  for (int k = 0; k < kFuseRowsPerWave; ++k) {
+    const int r = min(wave + k * nw, nrows - 1);
+    const bool isq = r >= G1;
+    const bool plain_sum = isq && a.tmode == 1;
+    const float it = isq ? 1.f : a.invT;
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < kFuseUnitsPerLane; ++u) {
+      const float su = v[k][u].y;
+      if (plain_sum) sum += su;
+      else if (su > 0.f) sum += su * expf((v[k][u].x - mx[k]) * it);
+    }
+    z[k] = wave_sum(sum);
+    if (plain_sum) mx[k] = 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < kFuseRowsPerWave; ++k) {
+    const int r = wave + k * nw;
+    if (r < nrows && lane < kRowInfo) {
+      float x = 0.f;
+      if (lane == RI_M) x = mx[k];
+      else if (lane == RI_INVZ) x = 1.0f / z[k];
+      else if (lane == RI_INVZN) x = 1.0f;
+      ri_seq[r * kRowInfo + lane] = x;
+      if (publish) {
+        const size_t grow = r >= G1 ? (size_t)a.M + (size_t)b * a.gamma + (r - G1) : (size_t)b * G1 + r;
+        a.rowinfo[grow * kRowInfo + lane] = x;
+      }
+    }
+  }
+}
+
 // Grid (chunks, B).  Every work group of sequence b takes the same decision
 // (ratio test r * q'(x) < p'(x) per drafted position, first rejection;
 // lattice-ai-eng explainer, acceptance rule; pigeon guide, How it works,
@@ -612,19 +695,33 @@ __device__ __forceinline__ void load_chunk(const SampleArgs& a, const ResRow& rr
 // the resample row: the residual max(0, p' - q') at the first rejection,
 // p' for the bonus slot, plus p' itself for a zero residual (pigeon guide,
 // steps 4-5; scalablesystem article, The Accept/Reject Mechanism).
-__global__ __launch_bounds__(kResThreads) void k_decide_chunks(SampleArgs a) {
+__global__ __launch_bounds__(kResThreads) void k_decide_chunks(SampleArgs a, bool fuse) {
   __shared__ int sh_bad, sh_first;
   __shared__ double lds_w[kResThreads / kWave], lds_p[kResThreads / kWave];
+  __shared__ float sh_ri[kFuseRowsPerWave * (kResThreads / kWave) * kRowInfo];
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int gamma = a.gamma, G1 = gamma + 1;
   if (tid == 0) { sh_bad = 0; sh_first = INT_MAX; }
+  // this thread's draft token and the target / draft values at it, loaded
+  // before the statistics (they need none)
+  int x0 = -1;
+  float l0 = 0.f, q0 = 0.f;
+  if (tid < gamma) {
+    x0 = a.draft[(size_t)b * gamma + tid];
+    if (a.tmode != 0 && x0 >= 0 && x0 < a.V) {
+      l0 = a.logits[((size_t)b * G1 + tid) * a.ldl + x0];
+      q0 = a.q[((size_t)b * gamma + tid) * a.V + x0];
+    }
+  }
+  if (fuse) seq_rowstats(a, b, sh_ri, c == 0);
   __syncthreads();
   // statistics of local row r (p rows 0..gamma, then q rows)
   auto ri_of = [&](int r) -> const float* {
+    if (fuse) return sh_ri + r * kRowInfo;
     return a.rowinfo + (r < G1 ? (size_t)b * G1 + r : (size_t)a.M + (size_t)b * gamma + (r - G1)) * kRowInfo;
   };
   for (int i = tid; i < gamma; i += blockDim.x) {
-    const int x = a.draft[(size_t)b * gamma + i];
+    const int x = i == tid ? x0 : a.draft[(size_t)b * gamma + i];
     if (x < 0 || x >= a.V) { atomicOr(&sh_bad, 1); continue; }
     const size_t prow = (size_t)b * G1 + i;
     bool reject;
@@ -632,8 +729,10 @@ __global__ __launch_bounds__(kResThreads) void k_decide_chunks(SampleArgs a) {
       reject = x != __float_as_int(ri_of(i)[RI_M]);
     } else {
       const size_t qrow = (size_t)b * gamma + i;
-      const float pp = p_prime(ri_of(i), a.logits[prow * a.ldl + x], x, a.invT);
-      const float qq = q_prime(ri_of(G1 + i), a.q[qrow * a.V + x], x, a.tmode, a.invT);
+      const float lx = i == tid ? l0 : a.logits[prow * a.ldl + x];
+      const float qx = i == tid ? q0 : a.q[qrow * a.V + x];
+      const float pp = p_prime(ri_of(i), lx, x, a.invT);
+      const float qq = q_prime(ri_of(G1 + i), qx, x, a.tmode, a.invT);
       float r, u;
       row_uniforms(a.seed, b, i, r, u);
       reject = !(r * qq < pp);
@@ -660,7 +759,7 @@ __global__ __launch_bounds__(kResThreads) void k_decide_chunks(SampleArgs a) {
     if (tid == 0) { a.n_acc[b] = n; a.dec[4 * b] = n; }
   }
   if (a.tmode == 0) return;
-  const ResRow rr = make_row(a, b, n, false);
+  const ResRow rr = make_row(a, b, n, false, fuse ? sh_ri : nullptr);
   float l[kResPer], qv[kResPer];
   load_chunk(a, rr, c, l, qv);
   const int v0 = c * kResampleChunk + tid * kResPer;
@@ -813,10 +912,13 @@ hipError_t launch_dump_probs(const SampleArgs& a, hipStream_t st) {
 hipError_t launch_sampling(const SampleArgs& a, hipStream_t st) {
   const int qrows = a.B * a.gamma;
   const bool topp = a.tmode != 0 && a.top_p < 1.0f;
+  const bool fuse = fuse_rowstats(a, kResThreads);
   // one work group per row combines the statistics, in parallel over rows
-  hipLaunchKernelGGL(k_rowstats, dim3(a.tmode != 0 ? a.M + qrows : a.M), dim3(kRowThreads), 0, st, a);
+  if (!fuse)
+    hipLaunchKernelGGL(k_rowstats, dim3(a.tmode != 0 ? a.M + qrows : a.M), dim3(kRowThreads), 0, st, a);
   if (topp) hipLaunchKernelGGL(k_topp, dim3(a.M + qrows), dim3(kToppThreads), 0, st, a);
-  hipLaunchKernelGGL(k_decide_chunks, dim3(a.tmode != 0 ? a.nch : 1, a.B), dim3(kResThreads), 0, st, a);
+  hipLaunchKernelGGL(k_decide_chunks, dim3(a.tmode != 0 ? a.nch : 1, a.B), dim3(kResThreads), 0, st, a,
+                     fuse);
   if (a.tmode != 0)
     hipLaunchKernelGGL(k_res_select, dim3(a.B), dim3(kResThreads), 0, st, a);
   return hipGetLastError();
