@@ -524,14 +524,30 @@ constexpr int kResPer = kResampleChunk / kResThreads;   // contiguous ids per th
 
 // Exclusive prefix over the block in thread order (wave scan, then waves in
 // order); *total receives the block sum.
-__device__ double block_excl_scan_f64(double x, double* lds_waves, double* total = nullptr) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+// Inclusive scan over the wave in lane order.
+__device__ __forceinline__ double wave_incl_scan_f64(double x) {
+  const int lane = threadIdx.x & 63;
   double inc = x;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const double y = __shfl_up(inc, o, kWave);
     if (lane >= o) inc += y;
   }
+  return inc;
+}
+
+// Exclusive scan over the wave in lane order; *total receives the wave sum.
+__device__ __forceinline__ double wave_excl_scan_f64(double x, double* total) {
+  const int lane = threadIdx.x & 63;
+  const double inc = wave_incl_scan_f64(x);
+  const double prev = __shfl_up(inc, 1, kWave);
+  *total = __shfl(inc, 63, kWave);
+  return lane == 0 ? 0.0 : prev;
+}
+
+__device__ double block_excl_scan_f64(double x, double* lds_waves, double* total = nullptr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const double inc = wave_incl_scan_f64(x);
   const double prev = __shfl_up(inc, 1, kWave);
   const double excl_lane = lane == 0 ? 0.0 : prev;
   if (lane == 63) lds_waves[wave] = inc;
@@ -790,16 +806,37 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
   __shared__ double lds_w[kResThreads / kWave];
   __shared__ int sh_c, sh_cand, sh_last;
   __shared__ double sh_base, sh_lastbase;
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const double* cs = a.csum + 2 * (size_t)b * a.nch;
+  // Up to 64 chunks: every wave scans the chunk sums itself (the same bits
+  // as the block scan, whose other waves would only add zeros), with no
+  // LDS round trip or barrier; the sums are loaded with the decision.
+  const bool one_wave = a.nch <= kWave;
+  double xw = 0.0, xp = 0.0;
+  if (one_wave && lane < a.nch) { xw = cs[2 * lane]; xp = cs[2 * lane + 1]; }
   const int j = a.dec[4 * b];
   if (j < 0) return;
   float r, u;
   row_uniforms(a.seed, b, j, r, u);
-  const double* cs = a.csum + 2 * (size_t)b * a.nch;
   if (tid == 0) { sh_c = INT_MAX; sh_cand = INT_MAX; sh_last = -1; sh_base = 0.0; sh_lastbase = 0.0; }
   int usep = 0;
   double total = 0.0, target = 0.0;
-  if (a.nch <= kResThreads) {
+  int c = 0;
+  double base = 0.0;
+  if (one_wave) {
+    const bool in = lane < a.nch;
+    double ex = wave_excl_scan_f64(xw, &total);
+    if (!(total > 0.0)) {               // zero residual: sample p' instead
+      usep = 1;
+      xw = xp;
+      ex = wave_excl_scan_f64(xw, &total);
+    }
+    target = (double)u * total;
+    const uint64_t over = __ballot(in && ex + xw > target);
+    const uint64_t pos = __ballot(in && xw > 0.0);
+    c = over ? __ffsll((unsigned long long)over) - 1 : (pos ? 63 - __clzll((unsigned long long)pos) : 0);
+    base = __shfl(ex, c, kWave);
+  } else if (a.nch <= kResThreads) {
     // one chunk sum per thread: one block scan picks the chunk
     const bool in = tid < a.nch;
     double xw = in ? cs[2 * tid] : 0.0, xp = in ? cs[2 * tid + 1] : 0.0;
@@ -818,6 +855,8 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
     __syncthreads();
     if (tid == 0) { sh_c = pick; sh_last = -1; }
     __syncthreads();
+    c = sh_c;
+    base = sh_base;
   } else {
   // total of the residual chunk sums; the p' sums when it is exactly zero
   for (int pass = 0; pass < 2; ++pass) {
@@ -852,9 +891,9 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
   __syncthreads();
   if (tid == 0 && sh_c == INT_MAX) { sh_c = a.nch - 1; sh_base = sh_lastbase; }
   __syncthreads();
+  c = sh_c;
+  base = sh_base;
   }
-  const int c = sh_c;
-  const double base = sh_base;
   const ResRow rr = make_row(a, b, j, usep != 0);
   float l[kResPer], qv[kResPer];
   load_chunk(a, rr, c, l, qv);
