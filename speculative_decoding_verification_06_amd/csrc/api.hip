@@ -204,7 +204,7 @@ hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, con
     a.Np = W.Np;
     a.KS = W.Kp / kKStep;
     a.e = e;
-    a.e.out = e.out + (size_t)m0 * e.ldo;
+    a.e.out = e.out ? e.out + (size_t)m0 * e.ldo : nullptr;
     if (e.kind == EPI_UP) a.e.ss_in = e.ss_in + (size_t)m0 * e.ss_ld;
     if (e.kind == EPI_DOWN) {
       a.e.xg = e.xg + (size_t)m0 * e.ldo;
@@ -300,7 +300,8 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
   if (err == hipSuccess) {
     EpiArgs lm;
     lm.kind = EPI_LM;
-    lm.out = logits; lm.ldo = L.Vs; lm.N = w->V;
+    // greedy passes read only the argmax statistics: no logits unless asked for
+    lm.out = tmode == 0 && !logits_out ? nullptr : logits; lm.ldo = L.Vs; lm.N = w->V;
     lm.pst = at<float>(ws, L.pst); lm.pidx = at<int>(ws, L.pidx); lm.qst = at<float>(ws, L.qst);
     lm.q = q; lm.G = L.G; lm.G1 = gamma + 1; lm.gamma = gamma; lm.V = w->V;
     lm.tmode = tmode; lm.invT = tmode ? 1.0f / T : 1.0f;
