@@ -74,6 +74,11 @@ def test_full_size_parity(name):
                                           torch.from_numpy(q).to(DEV), T, top_p, seed)
     torch.cuda.synchronize()
     n, e, logits = n.cpu().numpy(), e.cpu().numpy(), logits.cpu().numpy()
+    # the plain call, as the benchmark makes it, decides exactly as the debug call
+    n2, e2 = sv.verify(w, hidden, torch.from_numpy(draft).to(DEV),
+                       torch.from_numpy(q).to(DEV) if T > 0 else None, T, top_p, seed)
+    torch.cuda.synchronize()
+    assert np.array_equal(n2.cpu().numpy(), n) and np.array_equal(e2.cpu().numpy(), e)
     err = logits_rel_err(logits[rows], ell)
     print(f"{name}: logits rel err max {err.max():.2e} median {np.median(err):.2e}")
     log_measurement({"what": f"full {name} logits", "rel_err_max": float(err.max()),

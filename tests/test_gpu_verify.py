@@ -59,6 +59,10 @@ def run_gpu(w, hidden, draft, q, T, top_p, seed):
 
 def check(m, hidden, ell, q, draft, T, top_p, seed, w, what):
     n, e, logits, p, qq = run_gpu(w, hidden, draft, q, T, top_p, seed)
+    # the plain call (what the benchmark times) decides exactly as the debug call
+    n2, e2 = sv.verify(w, dev(hidden), dev(draft), dev(q) if T > 0 else None, T, top_p, seed)
+    torch.cuda.synchronize()
+    assert np.array_equal(n2.cpu().numpy(), n) and np.array_equal(e2.cpu().numpy(), e), what
     err = logits_rel_err(logits, ell)
     log_measurement({"what": f"{what} logits", "rel_err_max": float(err.max())})
     assert err.max() <= 1e-3, f"{what}: logits rel err {err.max():.2e}"
