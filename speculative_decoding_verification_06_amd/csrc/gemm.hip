@@ -1003,9 +1003,12 @@ __global__ __launch_bounds__(kFmaThreads) void k_gemm_fma(GemmArgs a) {
 // ---------------------------------------------------------------- host side
 
 int mfma_block_tiles(int Np) {
+  // the widest column block (up to 4 tiles) that still gives 7/8 of the CUs
+  // a block: 896 tiles take 224 blocks of 4 (one per CU, 8 waves each)
+  // rather than 448 of 2 (measured 25.7 -> 24.6 us per 117 MB launch)
   const int tiles = Np / kSub;
   int nt = 4;
-  while (nt > 1 && tiles / nt < SV_MIN_BLOCKS) nt /= 2;
+  while (nt > 1 && tiles / nt < SV_MIN_BLOCKS * 7 / 8) nt /= 2;
   return nt;
 }
 
