@@ -522,8 +522,6 @@ __global__ __launch_bounds__(kToppThreads) void k_topp(SampleArgs a) {
 constexpr int kResThreads = 256;
 constexpr int kResPer = kResampleChunk / kResThreads;   // contiguous ids per thread
 
-// Exclusive prefix over the block in thread order (wave scan, then waves in
-// order); *total receives the block sum.
 // Inclusive scan over the wave in lane order.
 __device__ __forceinline__ double wave_incl_scan_f64(double x) {
   const int lane = threadIdx.x & 63;
@@ -545,6 +543,8 @@ __device__ __forceinline__ double wave_excl_scan_f64(double x, double* total) {
   return lane == 0 ? 0.0 : prev;
 }
 
+// Exclusive prefix over the block in thread order (wave scan, then waves in
+// order); *total receives the block sum.
 __device__ double block_excl_scan_f64(double x, double* lds_waves, double* total = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const double inc = wave_incl_scan_f64(x);
