@@ -404,15 +404,20 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 // group and the four tiles of a unit are merged ((t0, t1), (t2, t3)) -- the
 // order lm_unit_stats uses -- so the statistics bits match the separate
 // epilogue's.
+// The statistics mode TM (0 greedy, 1 T = 1, 2 other T) is a template
+// parameter: each epilogue loop below then holds one variant, and the code a
+// wave runs after its k-loop stays small enough for the instruction cache
+// (fully unrolled over every row with the mode decided per row, the LM
+// epilogue was 78 to 226 KB of straight-line code and took 43 us).
+//
 // Statistics of one row's unit from its four tiles (one column per lane of
 // each tile's 16-lane group); the group's first lane writes when `live`.
-__device__ __forceinline__ void unit_stats_4(const EpiArgs& e, float l0, float l1, float l2, float l3,
-                                             float q0, float q1, float q2, float q3, int n0,
-                                             bool live, int grow, int unit) {
-  const float lv[4] = {l0, l1, l2, l3}, qa[4] = {q0, q1, q2, q3};
+template <int TM>
+__device__ __forceinline__ void unit_stats_4(const EpiArgs& e, const float (&lv)[4], const float (&qa)[4],
+                                             int n0, bool live, int grow, int unit) {
   const bool writer = live && (threadIdx.x & 15) == 0;
   const size_t ts = (size_t)grow * e.G + unit;
-  if (e.tmode == 0) {
+  if constexpr (TM == 0) {
     float v = -INFINITY;
     int idx = 0x7fffffff;
 #pragma unroll
@@ -426,100 +431,40 @@ __device__ __forceinline__ void unit_stats_4(const EpiArgs& e, float l0, float l
     }
     if (writer) { e.pst[2 * ts] = v; e.pst[2 * ts + 1] = 0.f; e.pidx[ts] = idx; }
     return;
-  }
-  float mx[4], se[4], ym[4], sq[4];
+  } else {
+    float mx[4], se[4], ym[4], sq[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const bool valid = live && n0 + t * kSub < e.N;
-    mx[t] = max16(valid ? lv[t] : -INFINITY);
-    se[t] = sum16(valid ? expf((lv[t] - mx[t]) * e.invT) : 0.f);
-    const float q = valid ? qa[t] : 0.f;
-    ym[t] = 0.f;
-    if (e.tmode == 1) {
-      sq[t] = sum16(q);
-    } else {
-      const float y = q > 0.f ? logf(q) * e.invT : -INFINITY;
-      ym[t] = max16(y);
-      sq[t] = sum16(q > 0.f ? expf(y - ym[t]) : 0.f);
+    for (int t = 0; t < 4; ++t) {
+      const bool valid = live && n0 + t * kSub < e.N;
+      mx[t] = max16(valid ? lv[t] : -INFINITY);
+      se[t] = sum16(valid ? expf((lv[t] - mx[t]) * e.invT) : 0.f);
+      const float q = valid ? qa[t] : 0.f;
+      ym[t] = 0.f;
+      if constexpr (TM == 1) {
+        sq[t] = sum16(q);
+      } else {
+        const float y = q > 0.f ? logf(q) * e.invT : -INFINITY;
+        ym[t] = max16(y);
+        sq[t] = sum16(q > 0.f ? expf(y - ym[t]) : 0.f);
+      }
     }
-  }
 #pragma unroll
-  for (int h = 0; h < 4; h += 2) {         // (t0, t1) and (t2, t3), then both
-    lse_merge(mx[h], se[h], mx[h + 1], se[h + 1], e.invT);
-    if (e.tmode == 1) sq[h] = sq[h] + sq[h + 1];
-    else lse_merge(ym[h], sq[h], ym[h + 1], sq[h + 1], 1.0f);
-  }
-  lse_merge(mx[0], se[0], mx[2], se[2], e.invT);
-  if (e.tmode == 1) sq[0] = sq[0] + sq[2];
-  else lse_merge(ym[0], sq[0], ym[2], sq[2], 1.0f);
-  if (writer) { e.pst[2 * ts] = mx[0]; e.pst[2 * ts + 1] = se[0]; }
-  const int b = grow / e.G1, ip = grow - b * e.G1;
-  if (writer && ip < e.gamma) {
-    const size_t tq = ((size_t)b * e.gamma + ip) * e.G + unit;
-    e.qst[2 * tq] = ym[0];
-    e.qst[2 * tq + 1] = sq[0];
-  }
-}
-
-// Draft probabilities of row tile I's items (0 for bonus rows, columns
-// past N, greedy passes).
-template <int I, int MTW>
-__device__ __forceinline__ void wide_lm_q(const EpiArgs& e, float (&qv)[4][4], int M, int MT, int mt0,
-                                          int n0, bool unit_ok) {
-  const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (mt0 + I) * 16 + 4 * g + j;
-    const bool live = unit_ok && mt0 + I < MT && row < M;
-    const int grow = e.row0 + row;
+    for (int h = 0; h < 4; h += 2) {         // (t0, t1) and (t2, t3), then both
+      lse_merge(mx[h], se[h], mx[h + 1], se[h + 1], e.invT);
+      if constexpr (TM == 1) sq[h] = sq[h] + sq[h + 1];
+      else lse_merge(ym[h], sq[h], ym[h + 1], sq[h + 1], 1.0f);
+    }
+    lse_merge(mx[0], se[0], mx[2], se[2], e.invT);
+    if constexpr (TM == 1) sq[0] = sq[0] + sq[2];
+    else lse_merge(ym[0], sq[0], ym[2], sq[2], 1.0f);
+    if (writer) { e.pst[2 * ts] = mx[0]; e.pst[2 * ts + 1] = se[0]; }
     const int b = grow / e.G1, ip = grow - b * e.G1;
-    const bool qrow = live && e.tmode != 0 && ip < e.gamma;
-    const float* qp = e.q + ((size_t)b * e.gamma + (qrow ? ip : 0)) * e.V;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = n0 + t * kSub;
-      qv[t][j] = qrow && n < e.N ? qp[n] : 0.f;
+    if (writer && ip < e.gamma) {
+      const size_t tq = ((size_t)b * e.gamma + ip) * e.G + unit;
+      e.qst[2 * tq] = ym[0];
+      e.qst[2 * tq + 1] = sq[0];
     }
   }
-}
-
-// Logits and statistics of row tile I, then of the tiles after it: a
-// compile-time recursion (the accumulators stay in registers only when
-// every index is a constant, and the loop would be too large to unroll),
-// with the next tile's draft probabilities loaded before this tile's work.
-template <int I, int MTW>
-__device__ __forceinline__ void wide_lm_rows(const EpiArgs& e, const f32x4 (&acc)[MTW][4],
-                                             const float (&qv)[4][4], int M, int MT, int mt0,
-                                             int unit, int n0, bool unit_ok) {
-  float qn[4][4];
-  if constexpr (I + 1 < MTW) wide_lm_q<I + 1, MTW>(e, qn, M, MT, mt0, n0, unit_ok);
-  const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (mt0 + I) * 16 + 4 * g + j;
-    const bool live = unit_ok && mt0 + I < MT && row < M;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = n0 + t * kSub;
-      if (live && n < e.N && e.out) e.out[(size_t)row * e.ldo + n] = acc[I][t][j];
-    }
-    unit_stats_4(e, acc[I][0][j], acc[I][1][j], acc[I][2][j], acc[I][3][j], qv[0][j], qv[1][j],
-                 qv[2][j], qv[3][j], n0, live, e.row0 + row, unit);
-  }
-  if constexpr (I + 1 < MTW) wide_lm_rows<I + 1, MTW>(e, acc, qn, M, MT, mt0, unit, n0, unit_ok);
-}
-
-// The LM head's epilogue straight from a wide-GEMM wave's accumulators,
-// when one work group sums all of K for its columns.  A wave's four column
-// tiles are one 64-column statistics unit.
-template <int MTW>
-__device__ __forceinline__ void wide_lm_epilogue(const EpiArgs& e, const f32x4 (&acc)[MTW][4], int M,
-                                                 int MT, int mt0, int unit, int tiles) {
-  const int n0 = unit * 4 * kSub + (threadIdx.x & 15);   // this lane's column in tile 0
-  const bool unit_ok = unit * 4 < tiles;
-  float q0[4][4];
-  wide_lm_q<0, MTW>(e, q0, M, MT, mt0, n0, unit_ok);
-  wide_lm_rows<0, MTW>(e, acc, q0, M, MT, mt0, unit, n0, unit_ok);
 }
 
 // Two-tile variant (NTC = 2: a 64-column unit spans the tiles of waves
@@ -528,11 +473,11 @@ __device__ __forceinline__ void wide_lm_epilogue(const EpiArgs& e, const f32x4 (
 // the order lm_unit_stats uses.
 struct HalfStats { float mx, se, ym, sq; };   // greedy: mx = max logit, se = argmax id bits
 
-__device__ __forceinline__ HalfStats half_stats_2(const EpiArgs& e, float l0, float l1, float q0,
-                                                  float q1, int n0, bool live) {
-  const float lv[2] = {l0, l1}, qa[2] = {q0, q1};
+template <int TM>
+__device__ __forceinline__ HalfStats half_stats_2(const EpiArgs& e, const float (&lv)[2],
+                                                  const float (&qa)[2], int n0, bool live) {
   HalfStats h;
-  if (e.tmode == 0) {
+  if constexpr (TM == 0) {
     float v = -INFINITY;
     int idx = 0x7fffffff;
 #pragma unroll
@@ -546,74 +491,156 @@ __device__ __forceinline__ HalfStats half_stats_2(const EpiArgs& e, float l0, fl
     }
     h.mx = v; h.se = __int_as_float(idx); h.ym = 0.f; h.sq = 0.f;
     return h;
-  }
-  float mx[2], se[2], ym[2], sq[2];
+  } else {
+    float mx[2], se[2], ym[2], sq[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const bool valid = live && n0 + t * kSub < e.N;
-    mx[t] = max16(valid ? lv[t] : -INFINITY);
-    se[t] = sum16(valid ? expf((lv[t] - mx[t]) * e.invT) : 0.f);
-    const float q = valid ? qa[t] : 0.f;
-    ym[t] = 0.f;
-    if (e.tmode == 1) {
-      sq[t] = sum16(q);
-    } else {
-      const float y = q > 0.f ? logf(q) * e.invT : -INFINITY;
-      ym[t] = max16(y);
-      sq[t] = sum16(q > 0.f ? expf(y - ym[t]) : 0.f);
+    for (int t = 0; t < 2; ++t) {
+      const bool valid = live && n0 + t * kSub < e.N;
+      mx[t] = max16(valid ? lv[t] : -INFINITY);
+      se[t] = sum16(valid ? expf((lv[t] - mx[t]) * e.invT) : 0.f);
+      const float q = valid ? qa[t] : 0.f;
+      ym[t] = 0.f;
+      if constexpr (TM == 1) {
+        sq[t] = sum16(q);
+      } else {
+        const float y = q > 0.f ? logf(q) * e.invT : -INFINITY;
+        ym[t] = max16(y);
+        sq[t] = sum16(q > 0.f ? expf(y - ym[t]) : 0.f);
+      }
     }
+    lse_merge(mx[0], se[0], mx[1], se[1], e.invT);
+    if constexpr (TM == 1) sq[0] = sq[0] + sq[1];
+    else lse_merge(ym[0], sq[0], ym[1], sq[1], 1.0f);
+    h.mx = mx[0]; h.se = se[0]; h.ym = ym[0]; h.sq = sq[0];
+    return h;
   }
-  lse_merge(mx[0], se[0], mx[1], se[1], e.invT);
-  if (e.tmode == 1) sq[0] = sq[0] + sq[1];
-  else lse_merge(ym[0], sq[0], ym[1], sq[1], 1.0f);
-  h.mx = mx[0]; h.se = se[0]; h.ym = ym[0]; h.sq = sq[0];
-  return h;
 }
 
-// Draft probabilities of row tile I's items, two tiles.
-template <int I, int MTW>
-__device__ __forceinline__ void wide_lm_q2(const EpiArgs& e, float (&qv)[2][4], int M, int MT, int mt0,
-                                           int n0, bool unit_ok) {
+// Draft probabilities of row tile mt's items for NTC column tiles (0 for
+// bonus rows, columns past N, greedy passes).
+template <int NTC>
+__device__ __forceinline__ void wide_lm_q(const EpiArgs& e, float (&qv)[NTC][4], int M, int MT, int mt,
+                                          int n0, bool unit_ok) {
   const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = (mt0 + I) * 16 + 4 * g + j;
-    const bool live = unit_ok && mt0 + I < MT && row < M;
+    const int row = mt * 16 + 4 * g + j;
+    const bool live = unit_ok && mt < MT && row < M;
     const int grow = e.row0 + row;
     const int b = grow / e.G1, ip = grow - b * e.G1;
     const bool qrow = live && e.tmode != 0 && ip < e.gamma;
     const float* qp = e.q + ((size_t)b * e.gamma + (qrow ? ip : 0)) * e.V;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NTC; ++t) {
       const int n = n0 + t * kSub;
       qv[t][j] = qrow && n < e.N ? qp[n] : 0.f;
     }
   }
 }
 
-// Logits and half-unit statistics (to LDS half[row]) of row tile I, then
-// of the tiles after it; the next tile's draft probabilities load first.
-template <int I, int MTW>
-__device__ __forceinline__ void wide_lm_rows2(const EpiArgs& e, const f32x4 (&acc)[MTW][2],
-                                              const float (&qv)[2][4], int M, int MT, int mt0,
-                                              int n0, bool unit_ok, float4* half) {
-  float qn[2][4];
-  if constexpr (I + 1 < MTW) wide_lm_q2<I + 1, MTW>(e, qn, M, MT, mt0, n0, unit_ok);
+// Logits and half-unit statistics (to LDS half[row]) of the wave's row
+// tiles, two column tiles each (one row group, few accumulators), one tile
+// per iteration of a loop that is not unrolled: tile I's accumulators are
+// picked out with constant indices, so they stay in registers.
+template <int MTW, int NTC, int TM>
+__device__ __forceinline__ void wide_lm_tiles(const EpiArgs& e, const f32x4 (&acc)[MTW][NTC], int M, int MT,
+                                              int mt0, int unit, int n0, bool unit_ok, float4* half) {
+  static_assert(NTC == 2, "two column tiles per wave");
+  (void)unit;
+  const int g = (threadIdx.x & 63) >> 4;
+  // draft probabilities two tiles ahead of the work that uses them (their
+  // loads queue behind the other group's weight stream on the CU)
+  float qv[NTC][4], qn[NTC][4];
+  wide_lm_q<NTC>(e, qv, M, MT, mt0, n0, unit_ok);
+  wide_lm_q<NTC>(e, qn, M, MT, MTW > 1 ? mt0 + 1 : MT, n0, unit_ok);
+#pragma unroll 1
+  for (int I = 0; I < MTW; ++I) {
+    f32x4 at[NTC];
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) at[t] = acc[0][t];
+#pragma unroll
+    for (int i = 1; i < MTW; ++i)
+      if (i == I) {
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) at[t] = acc[i][t];
+      }
+    float qnn[NTC][4];
+    wide_lm_q<NTC>(e, qnn, M, MT, I + 2 < MTW ? mt0 + I + 2 : MT, n0, unit_ok);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = (mt0 + I) * 16 + 4 * g + j;
+      const bool live = unit_ok && mt0 + I < MT && row < M;
+      float lv[NTC], qj[NTC];
+#pragma unroll
+      for (int t = 0; t < NTC; ++t) {
+        lv[t] = at[t][j];
+        qj[t] = qv[t][j];
+        const int n = n0 + t * kSub;
+        if (live && n < e.N && e.out) e.out[(size_t)row * e.ldo + n] = lv[t];
+      }
+      const HalfStats h = half_stats_2<TM>(e, lv, qj, n0, live);
+      if ((threadIdx.x & 15) == 0 && mt0 + I < MT) half[row] = make_float4(h.mx, h.se, h.ym, h.sq);
+    }
+#pragma unroll
+    for (int t = 0; t < NTC; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { qv[t][j] = qn[t][j]; qn[t][j] = qnn[t][j]; }
+  }
+}
+
+template <int I, int MTW, int TM>
+__device__ __forceinline__ void wide_lm_rows4(const EpiArgs& e, const f32x4 (&acc)[MTW][4],
+                                              const float (&qv)[4][4], int M, int MT, int mt0,
+                                              int unit, int n0, bool unit_ok) {
+  float qn[4][4];
+  if constexpr (I + 1 < MTW) wide_lm_q<4>(e, qn, M, MT, mt0 + I + 1, n0, unit_ok);
   const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = (mt0 + I) * 16 + 4 * g + j;
     const bool live = unit_ok && mt0 + I < MT && row < M;
+    float lv[4], qj[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 4; ++t) {
+      lv[t] = acc[I][t][j];
+      qj[t] = qv[t][j];
       const int n = n0 + t * kSub;
-      if (live && n < e.N && e.out) e.out[(size_t)row * e.ldo + n] = acc[I][t][j];
+      if (live && n < e.N && e.out) e.out[(size_t)row * e.ldo + n] = lv[t];
     }
-    const HalfStats h = half_stats_2(e, acc[I][0][j], acc[I][1][j], qv[0][j], qv[1][j], n0, live);
-    if ((threadIdx.x & 15) == 0 && mt0 + I < MT) half[row] = make_float4(h.mx, h.se, h.ym, h.sq);
+    unit_stats_4<TM>(e, lv, qj, n0, live, e.row0 + row, unit);
   }
-  if constexpr (I + 1 < MTW)
-    wide_lm_rows2<I + 1, MTW>(e, acc, qn, M, MT, mt0, n0, unit_ok, half);
+  if constexpr (I + 1 < MTW) wide_lm_rows4<I + 1, MTW, TM>(e, acc, qn, M, MT, mt0, unit, n0, unit_ok);
+}
+
+template <int MTW, int NTC, int TM>
+__device__ __forceinline__ void wide_lm_mode(const EpiArgs& e, const f32x4 (&acc)[MTW][NTC], int M, int MT,
+                                             int mt0, int unit, int n0, bool unit_ok, float4* half) {
+  if constexpr (NTC == 4) {
+    float q0[4][4];
+    wide_lm_q<4>(e, q0, M, MT, mt0, n0, unit_ok);
+    wide_lm_rows4<0, MTW, TM>(e, acc, q0, M, MT, mt0, unit, n0, unit_ok);
+  } else {
+    wide_lm_tiles<MTW, NTC, TM>(e, acc, M, MT, mt0, unit, n0, unit_ok, half);
+  }
+}
+
+template <int MTW, int NTC>
+__device__ __forceinline__ void wide_lm_tiles_tm(const EpiArgs& e, const f32x4 (&acc)[MTW][NTC], int M,
+                                                 int MT, int mt0, int unit, int n0, bool unit_ok,
+                                                 float4* half) {
+  if (e.tmode == 0) wide_lm_mode<MTW, NTC, 0>(e, acc, M, MT, mt0, unit, n0, unit_ok, half);
+  else if (e.tmode == 1) wide_lm_mode<MTW, NTC, 1>(e, acc, M, MT, mt0, unit, n0, unit_ok, half);
+  else wide_lm_mode<MTW, NTC, 2>(e, acc, M, MT, mt0, unit, n0, unit_ok, half);
+}
+
+// The LM head's epilogue straight from a wide-GEMM wave's accumulators,
+// when one work group sums all of K for its columns.  A wave's four column
+// tiles are one 64-column statistics unit.
+template <int MTW>
+__device__ __forceinline__ void wide_lm_epilogue(const EpiArgs& e, const f32x4 (&acc)[MTW][4], int M,
+                                                 int MT, int mt0, int unit, int tiles) {
+  const int n0 = unit * 4 * kSub + (threadIdx.x & 15);   // this lane's column in tile 0
+  wide_lm_tiles_tm<MTW, 4>(e, acc, M, MT, mt0, unit, n0, unit * 4 < tiles, nullptr);
 }
 
 // LM epilogue of the two-tile wide GEMM: CG waves, CG / 2 units per work
@@ -624,10 +651,7 @@ __device__ __forceinline__ void wide_lm_epilogue2(const EpiArgs& e, const f32x4 
                                                   int R) {
   const int unit = blockIdx.x * (CG / 2) + cg / 2;
   const int n0 = (unit * 4 + 2 * (cg & 1)) * kSub + (threadIdx.x & 15);
-  const bool unit_ok = unit * 4 < tiles;
-  float q0[2][4];
-  wide_lm_q2<0, MTW>(e, q0, M, MT, mt0, n0, unit_ok);
-  wide_lm_rows2<0, MTW>(e, acc, q0, M, MT, mt0, n0, unit_ok, hbuf + cg * R);
+  wide_lm_tiles_tm<MTW, 2>(e, acc, M, MT, mt0, unit, n0, unit * 4 < tiles, hbuf + cg * R);
   __syncthreads();
   for (int k = threadIdx.x; k < (CG / 2) * M; k += blockDim.x) {
     const int u = k / M, row = k - u * M;
