@@ -418,17 +418,16 @@ __device__ __forceinline__ void unit_stats_4(const EpiArgs& e, const float (&lv)
   const bool writer = live && (threadIdx.x & 15) == 0;
   const size_t ts = (size_t)grow * e.G + unit;
   if constexpr (TM == 0) {
+    // the lane's four columns first, then one 16-lane butterfly: the
+    // largest value with the lowest id is the same in any order
     float v = -INFINITY;
     int idx = 0x7fffffff;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int n = n0 + t * kSub;
-      const bool valid = live && n < e.N;
-      float vt = valid ? lv[t] : -INFINITY;
-      int it = valid ? n : 0x7fffffff;
-      argmax16(vt, it);
-      if (vt > v || (vt == v && it < idx)) { v = vt; idx = it; }
+      if (live && n < e.N && (lv[t] > v || idx == 0x7fffffff)) { v = lv[t]; idx = n; }
     }
+    argmax16(v, idx);
     if (writer) { e.pst[2 * ts] = v; e.pst[2 * ts + 1] = 0.f; e.pidx[ts] = idx; }
     return;
   } else {
@@ -483,12 +482,9 @@ __device__ __forceinline__ HalfStats half_stats_2(const EpiArgs& e, const float 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int n = n0 + t * kSub;
-      const bool valid = live && n < e.N;
-      float vt = valid ? lv[t] : -INFINITY;
-      int it = valid ? n : 0x7fffffff;
-      argmax16(vt, it);
-      if (vt > v || (vt == v && it < idx)) { v = vt; idx = it; }
+      if (live && n < e.N && (lv[t] > v || idx == 0x7fffffff)) { v = lv[t]; idx = n; }
     }
+    argmax16(v, idx);
     h.mx = v; h.se = __int_as_float(idx); h.ym = 0.f; h.sq = 0.f;
     return h;
   } else {
