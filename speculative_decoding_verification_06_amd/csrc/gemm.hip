@@ -400,15 +400,15 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 
 // ---------------------------------------------------------------- LM epilogue from registers
 // In the 16x16 MFMA C layout, register j of the 16-lane group g holds row
-// 4 g + j of a tile, one column per lane.  Each tile is reduced over its
-// group and the four tiles of a unit are merged ((t0, t1), (t2, t3)) -- the
-// order lm_unit_stats uses -- so the statistics bits match the separate
-// epilogue's.
+// 4 g + j of a tile, one column per lane.  A row's unit statistics reduce
+// each lane's columns first and then the 16-lane group, one butterfly per
+// statistic: the row max (or argmax), then the sum of exp((l - max) / T).
+// They are the separate epilogue's quantities, not its bits (that one
+// reduces tile by tile and merges).
 // The statistics mode TM (0 greedy, 1 T = 1, 2 other T) is a template
-// parameter: each epilogue loop below then holds one variant, and the code a
-// wave runs after its k-loop stays small enough for the instruction cache
-// (fully unrolled over every row with the mode decided per row, the LM
-// epilogue was 78 to 226 KB of straight-line code and took 43 us).
+// parameter, so the code a wave runs after its k-loop holds one variant
+// (deciding the mode per row, fully unrolled, the 72-row LM head kernel was
+// 78 KB of code; now 31 KB).
 //
 // Statistics of one row's unit from its four tiles (one column per lane of
 // each tile's 16-lane group); the group's first lane writes when `live`.
@@ -431,37 +431,42 @@ __device__ __forceinline__ void unit_stats_4(const EpiArgs& e, const float (&lv)
     if (writer) { e.pst[2 * ts] = v; e.pst[2 * ts + 1] = 0.f; e.pidx[ts] = idx; }
     return;
   } else {
-    float mx[4], se[4], ym[4], sq[4];
+    // max over the lane's columns, then over the group; then the sum of
+    // exp((l - max) / T) the same way (one butterfly per statistic instead
+    // of one per tile and a merge)
+    float m = -INFINITY, ymax = -INFINITY;
+    float y[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const bool valid = live && n0 + t * kSub < e.N;
-      mx[t] = max16(valid ? lv[t] : -INFINITY);
-      se[t] = sum16(valid ? expf((lv[t] - mx[t]) * e.invT) : 0.f);
-      const float q = valid ? qa[t] : 0.f;
-      ym[t] = 0.f;
-      if constexpr (TM == 1) {
-        sq[t] = sum16(q);
-      } else {
-        const float y = q > 0.f ? logf(q) * e.invT : -INFINITY;
-        ym[t] = max16(y);
-        sq[t] = sum16(q > 0.f ? expf(y - ym[t]) : 0.f);
+      if (valid) m = fmaxf(m, lv[t]);
+      y[t] = -INFINITY;
+      if constexpr (TM == 2) {
+        if (valid && qa[t] > 0.f) y[t] = logf(qa[t]) * e.invT;
+        ymax = fmaxf(ymax, y[t]);
       }
     }
+    const float mx = max16(m);
+    float se = 0.f, sq = 0.f;
+    if constexpr (TM == 2) ymax = max16(ymax);
 #pragma unroll
-    for (int h = 0; h < 4; h += 2) {         // (t0, t1) and (t2, t3), then both
-      lse_merge(mx[h], se[h], mx[h + 1], se[h + 1], e.invT);
-      if constexpr (TM == 1) sq[h] = sq[h] + sq[h + 1];
-      else lse_merge(ym[h], sq[h], ym[h + 1], sq[h + 1], 1.0f);
+    for (int t = 0; t < 4; ++t) {
+      const bool valid = live && n0 + t * kSub < e.N;
+      if (valid) se += expf((lv[t] - mx) * e.invT);
+      if constexpr (TM == 1) {
+        if (valid) sq += qa[t];
+      } else {
+        if (y[t] > -INFINITY) sq += expf(y[t] - ymax);
+      }
     }
-    lse_merge(mx[0], se[0], mx[2], se[2], e.invT);
-    if constexpr (TM == 1) sq[0] = sq[0] + sq[2];
-    else lse_merge(ym[0], sq[0], ym[2], sq[2], 1.0f);
-    if (writer) { e.pst[2 * ts] = mx[0]; e.pst[2 * ts + 1] = se[0]; }
+    se = sum16(se);
+    sq = sum16(sq);
+    if (writer) { e.pst[2 * ts] = mx; e.pst[2 * ts + 1] = se; }
     const int b = grow / e.G1, ip = grow - b * e.G1;
     if (writer && ip < e.gamma) {
       const size_t tq = ((size_t)b * e.gamma + ip) * e.G + unit;
-      e.qst[2 * tq] = ym[0];
-      e.qst[2 * tq + 1] = sq[0];
+      e.qst[2 * tq] = TM == 1 ? 0.f : ymax;
+      e.qst[2 * tq + 1] = sq;
     }
   }
 }
@@ -488,26 +493,32 @@ __device__ __forceinline__ HalfStats half_stats_2(const EpiArgs& e, const float 
     h.mx = v; h.se = __int_as_float(idx); h.ym = 0.f; h.sq = 0.f;
     return h;
   } else {
-    float mx[2], se[2], ym[2], sq[2];
+    float m = -INFINITY, ymax = -INFINITY;
+    float y[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const bool valid = live && n0 + t * kSub < e.N;
-      mx[t] = max16(valid ? lv[t] : -INFINITY);
-      se[t] = sum16(valid ? expf((lv[t] - mx[t]) * e.invT) : 0.f);
-      const float q = valid ? qa[t] : 0.f;
-      ym[t] = 0.f;
-      if constexpr (TM == 1) {
-        sq[t] = sum16(q);
-      } else {
-        const float y = q > 0.f ? logf(q) * e.invT : -INFINITY;
-        ym[t] = max16(y);
-        sq[t] = sum16(q > 0.f ? expf(y - ym[t]) : 0.f);
+      if (valid) m = fmaxf(m, lv[t]);
+      y[t] = -INFINITY;
+      if constexpr (TM == 2) {
+        if (valid && qa[t] > 0.f) y[t] = logf(qa[t]) * e.invT;
+        ymax = fmaxf(ymax, y[t]);
       }
     }
-    lse_merge(mx[0], se[0], mx[1], se[1], e.invT);
-    if constexpr (TM == 1) sq[0] = sq[0] + sq[1];
-    else lse_merge(ym[0], sq[0], ym[1], sq[1], 1.0f);
-    h.mx = mx[0]; h.se = se[0]; h.ym = ym[0]; h.sq = sq[0];
+    const float mx = max16(m);
+    float se = 0.f, sq = 0.f;
+    if constexpr (TM == 2) ymax = max16(ymax);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bool valid = live && n0 + t * kSub < e.N;
+      if (valid) se += expf((lv[t] - mx) * e.invT);
+      if constexpr (TM == 1) {
+        if (valid) sq += qa[t];
+      } else {
+        if (y[t] > -INFINITY) sq += expf(y[t] - ymax);
+      }
+    }
+    h.mx = mx; h.se = sum16(se); h.ym = TM == 1 ? 0.f : ymax; h.sq = sum16(sq);
     return h;
   }
 }
