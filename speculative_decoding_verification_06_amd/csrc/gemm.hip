@@ -108,7 +108,15 @@ __device__ __forceinline__ void epi_prefetch(const EpiArgs& e, int M, int c0, in
 #pragma unroll
   for (int j = 0; j < 8; ++j) pv[j] = 0.f;
   if (e.kind == EPI_UP) {
-    if (e.rms) return;
+    if (e.rms) {
+      // 1 / rms of rows wave, wave + nwaves, ... (at most 8 per wave)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = wave + j * nwaves;
+        pv[j] = r < M ? e.rms[e.row0 + r] : 0.f;
+      }
+      return;
+    }
     if (wave < M) {
       const float* ps = e.ss_in + (size_t)wave * e.ss_ld;
 #pragma unroll
@@ -136,8 +144,15 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15;
   if (e.kind == EPI_UP && e.rms) {
-    for (int r = wave; r < M; r += nwaves)
-      if (lane == 0) sh_inv[r] = e.rms[e.row0 + r];
+    // prefetched by epi_prefetch for the first 8 rows of each wave
+    for (int r = wave, j = 0; r < M; r += nwaves, ++j) {
+      float v = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (jj == j) v = pv[jj];
+      if (j >= 8) v = e.rms[e.row0 + r];
+      if (lane == 0) sh_inv[r] = v;
+    }
     __syncthreads();
   } else if (e.kind == EPI_UP) {
     // 1 / rms per row from its per-16-column sums of squares: one wave per
