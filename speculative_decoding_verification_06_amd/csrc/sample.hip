@@ -543,6 +543,20 @@ __device__ __forceinline__ double wave_excl_scan_f64(double x, double* total) {
   return lane == 0 ? 0.0 : prev;
 }
 
+// Block totals of x and y, each summed exactly as block_excl_scan_f64 sums
+// its total (wave inclusive scans, then the waves in order), with one
+// barrier for both.
+__device__ void block_sum2_f64(double x, double y, double* lx, double* ly, double& tx, double& ty) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const double ix = wave_incl_scan_f64(x), iy = wave_incl_scan_f64(y);
+  if (lane == 63) { lx[wave] = ix; ly[wave] = iy; }
+  __syncthreads();
+  double sx = 0.0, sy = 0.0;
+  for (int w = 0; w < nw; ++w) { sx += lx[w]; sy += ly[w]; }
+  tx = sx;
+  ty = sy;
+}
+
 // Exclusive prefix over the block in thread order (wave scan, then waves in
 // order); *total receives the block sum.
 __device__ double block_excl_scan_f64(double x, double* lds_waves, double* total = nullptr) {
@@ -789,8 +803,7 @@ __global__ __launch_bounds__(kResThreads) void k_decide_chunks(SampleArgs a, boo
     }
   }
   double tw, tp;
-  (void)block_excl_scan_f64(sw, lds_w, &tw);
-  (void)block_excl_scan_f64(sp, lds_p, &tp);
+  block_sum2_f64(sw, sp, lds_w, lds_p, tw, tp);
   if (tid == 0) {
     a.csum[2 * ((size_t)b * a.nch + c)] = tw;
     a.csum[2 * ((size_t)b * a.nch + c) + 1] = tp;
