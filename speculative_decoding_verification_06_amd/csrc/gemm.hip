@@ -1107,12 +1107,18 @@ WidePlan plan_wide(int M, const Mat& m) {
   // two row groups x 4 column groups of 4 tiles = 16 column tiles, 8 waves
   p.mtw = (p.MT + 1) / 2;
   p.mg = 2; p.ntc = 4; p.cg = 4;
+  const int tiles = m.Np / kSub;
   if (p.MT <= 5) {
     // up to 80 rows: one row group of MT tiles (no padding tile), 8 column
-    // groups of 2 tiles, so no two waves load the same weight tile
-    p.mtw = p.MT; p.mg = 1; p.ntc = 2; p.cg = 8;
+    // groups of 2 tiles, so no two waves load the same weight tile.  When
+    // more 16-tile blocks than CUs would run two per CU (the LM head), 16
+    // column groups of 1024 threads instead: one group per CU whose waves
+    // keep step at the k-step barrier.  Two groups on a CU do not: the
+    // older one is served first and finishes its k-loop in about half the
+    // time, and the younger one then streams alone, latency bound.
+    p.mtw = p.MT; p.mg = 1; p.ntc = 2;
+    p.cg = tiles / 16 > SV_MIN_BLOCKS ? 16 : 8;
   }
-  const int tiles = m.Np / kSub;
   const int ntw = p.ntc * p.cg;
   p.colblocks = (tiles + ntw - 1) / ntw;
   const int KS = m.Kp / kKStep;
@@ -1168,7 +1174,15 @@ hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e
                        hipEvent_t e0, hipEvent_t e1) {
   WideArgs a = a_in;
   a.fuse_lm = p.S == 1 && e.kind == EPI_LM;
-  if (p.mg == 1) {
+  if (p.mg == 1 && p.cg == 16) {
+    switch (p.mtw) {
+      case 1: launch_wide_t<1, 2, 1, 16>(p, a, e, st, e0, e1); break;
+      case 2: launch_wide_t<2, 2, 1, 16>(p, a, e, st, e0, e1); break;
+      case 3: launch_wide_t<3, 2, 1, 16>(p, a, e, st, e0, e1); break;
+      case 4: launch_wide_t<4, 2, 1, 16>(p, a, e, st, e0, e1); break;
+      default: launch_wide_t<5, 2, 1, 16, 2>(p, a, e, st, e0, e1); break;
+    }
+  } else if (p.mg == 1) {
     switch (p.mtw) {
       case 1: launch_wide_t<1, 2, 1, 8>(p, a, e, st, e0, e1); break;
       case 2: launch_wide_t<2, 2, 1, 8>(p, a, e, st, e0, e1); break;
