@@ -200,6 +200,10 @@ constexpr int kToppThreads = 1024;
 constexpr int kToppWaves = kToppThreads / kWave;
 constexpr int kHistCopies = 4;
 constexpr int kMaxBins = 2048;           // digits of 11, 11 and 10 bits
+// Histogram copies sit nb + 4 u64 apart (nb bins), so one bin of the four
+// copies falls in four different LDS banks (a stride of nb alone is a
+// multiple of the bank count, and the copies' lanes would conflict).
+constexpr int kHistPad = 4;
 constexpr int kToppBatch4 = 4;           // 16-byte loads of one batch (the next batch is in flight meanwhile)
 constexpr int kToppBatch1 = 8;           // 4-byte loads of one batch, rows that are not 16-byte aligned
 constexpr int kTieCap = 64;              // tied keys ordered by one thread
@@ -229,7 +233,7 @@ struct ToppShared {
   // kHistCopies copies of the digit histogram, lane L adding to copy
   // L % kHistCopies, so lanes of a wave that share a digit collide at most
   // 64 / kHistCopies ways in the LDS atomic unit
-  u64 hist[kHistCopies * kMaxBins];
+  u64 hist[kHistCopies * (kMaxBins + kHistPad)];
   // The tokens of the first digit's crossing bucket (value bits, id), each
   // wave appending to its own segment during the second pass: they are the
   // only ones the last pass and the tie scan can match, so when they fit
@@ -351,10 +355,11 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
     const int bits = pass < 2 ? 11 : 10;
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = 1 << bits;
-    for (int i = tid; i < kHistCopies * nb; i += kToppThreads) sh.hist[i] = 0;
+    const int hs = nb + kHistPad;            // copy stride
+    for (int i = tid; i < kHistCopies * hs; i += kToppThreads) sh.hist[i] = 0;
     if (tid == 0) sh.overflow = 0;
     __syncthreads();
-    u64* myhist = sh.hist + (lane % kHistCopies) * nb;
+    u64* myhist = sh.hist + (lane % kHistCopies) * hs;
     if (pass == 0) {
       for_each_token([&](int, float x) { atomicAdd(&myhist[key_of(x) >> 21], mass_of(x)); });
     } else if (pass == 1) {
@@ -399,11 +404,13 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
       auto bin = [&](int b) {
         u64 t = 0;
 #pragma unroll
-        for (int cc = 0; cc < kHistCopies; ++cc) t += sh.hist[cc * nb + b];
+        for (int cc = 0; cc < kHistCopies; ++cc) t += sh.hist[cc * hs + b];
         return t;
       };
+      // each lane's bins in a lane-rotated order, so that the lanes of a
+      // step read different banks (integer sums: the order changes nothing)
       u64 S = 0;
-      for (int j = 0; j < bpl; ++j) S += bin(lane * bpl + j);
+      for (int j = 0; j < bpl; ++j) S += bin(lane * bpl + ((j + lane) & (bpl - 1)));
       u64 inc = S;   // inclusive suffix sum over lanes >= L
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
