@@ -828,12 +828,14 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
   __shared__ double sh_base, sh_lastbase;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const double* cs = a.csum + 2 * (size_t)b * a.nch;
-  // Up to 64 chunks: every wave scans the chunk sums itself (the same bits
-  // as the block scan, whose other waves would only add zeros), with no
-  // LDS round trip or barrier; the sums are loaded with the decision.
+  // The chunk sums do not depend on the decision: up to one per thread,
+  // they load along with it.  Up to 64 chunks, every wave then scans them
+  // itself (the same bits as the block scan, whose other waves would only
+  // add zeros), with no LDS round trip or barrier.
   const bool one_wave = a.nch <= kWave;
+  const int ci = one_wave ? lane : tid;
   double xw = 0.0, xp = 0.0;
-  if (one_wave && lane < a.nch) { xw = cs[2 * lane]; xp = cs[2 * lane + 1]; }
+  if (a.nch <= kResThreads && ci < a.nch) { xw = cs[2 * ci]; xp = cs[2 * ci + 1]; }
   const int j = a.dec[4 * b];
   if (j < 0) return;
   float r, u;
@@ -859,7 +861,6 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
   } else if (a.nch <= kResThreads) {
     // one chunk sum per thread: one block scan picks the chunk
     const bool in = tid < a.nch;
-    double xw = in ? cs[2 * tid] : 0.0, xp = in ? cs[2 * tid + 1] : 0.0;
     double ex = block_excl_scan_f64(xw, lds_w, &total);
     if (!(total > 0.0)) {               // zero residual: sample p' instead
       usep = 1;
