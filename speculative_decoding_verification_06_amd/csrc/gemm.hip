@@ -1190,8 +1190,9 @@ hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e
       case 4: launch_wide_t<4, 2, 1, 8>(p, a, e, st, e0, e1); break;
       default:
         // a 4-deep ring takes 137 registers: one group per CU.  Where
-        // more groups than CUs are launched (the LM head), two groups per
-        // CU with a 2-deep ring stream faster.
+        // more groups than CUs are launched, two groups per CU with a
+        // 2-deep ring stream faster (measured on a 501-group LM head, now
+        // launched in the 1024-thread shape above).
         if (p.colblocks * p.S > SV_MIN_BLOCKS) launch_wide_t<5, 2, 1, 8, 2>(p, a, e, st, e0, e1);
         else launch_wide_t<5, 2, 1, 8, 4>(p, a, e, st, e0, e1);
         break;
