@@ -88,6 +88,10 @@ CASES = [
     ("bf16-wide-90-rows", 10, 8, 128, 256, 600, 1, "bf16", 1.0, 1.0, False, {}),
     ("bf16-wide-120-rows-greedy", 15, 7, 128, 192, 520, 2, "bf16", 0.0, 1.0, True, {}),
     ("bf16-wide-224-greedy", 32, 6, 160, 288, 700, 1, "bf16", 0.0, 1.0, False, {}),
+    # LM heads of more than 4096 tiles at up to 80 rows: the 1024-thread
+    # one-row-group shape (18 rows, sampling with top-p; 16 rows, greedy)
+    ("bf16-wide-lm-1024", 3, 5, 128, 192, 70000, 1, "bf16", 0.9, 0.95, False, {}),
+    ("bf16-wide-lm-1024-greedy", 4, 3, 96, 160, 66000, 1, "bf16", 0.0, 1.0, True, {}),
     ("bf16-fma", 2, 4, 192, 448, 900, 2, "bf16", 1.0, 1.0, True,
      {"keep_rowmajor": True, "mfma_min_rows": 10 ** 6}),
     ("bf16-fma-many-rows", 12, 3, 136, 200, 333, 1, "bf16", 0.8, 1.0, False,
