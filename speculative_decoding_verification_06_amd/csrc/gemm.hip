@@ -420,6 +420,10 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 // statistic: the row max (or argmax), then the sum of exp((l - max) / T).
 // They are the separate epilogue's quantities, not its bits (that one
 // reduces tile by tile and merges).
+// The sums use the hardware exp2 / log2 (__expf, __logf): a relative error
+// of about |x| 2^-24 per term, below 2e-6 for every term that is not
+// negligible, so 1/Z and the probabilities built on it stay far inside
+// their 1e-5 bound; the max is exact.
 // The statistics mode TM (0 greedy, 1 T = 1, 2 other T) is a template
 // parameter, so the code a wave runs after its k-loop holds one variant
 // (deciding the mode per row, fully unrolled, the 72-row LM head kernel was
@@ -457,7 +461,7 @@ __device__ __forceinline__ void unit_stats_4(const EpiArgs& e, const float (&lv)
       if (valid) m = fmaxf(m, lv[t]);
       y[t] = -INFINITY;
       if constexpr (TM == 2) {
-        if (valid && qa[t] > 0.f) y[t] = logf(qa[t]) * e.invT;
+        if (valid && qa[t] > 0.f) y[t] = __logf(qa[t]) * e.invT;
         ymax = fmaxf(ymax, y[t]);
       }
     }
@@ -467,11 +471,11 @@ __device__ __forceinline__ void unit_stats_4(const EpiArgs& e, const float (&lv)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const bool valid = live && n0 + t * kSub < e.N;
-      if (valid) se += expf((lv[t] - mx) * e.invT);
+      if (valid) se += __expf((lv[t] - mx) * e.invT);
       if constexpr (TM == 1) {
         if (valid) sq += qa[t];
       } else {
-        if (y[t] > -INFINITY) sq += expf(y[t] - ymax);
+        if (y[t] > -INFINITY) sq += __expf(y[t] - ymax);
       }
     }
     se = sum16(se);
@@ -516,7 +520,7 @@ __device__ __forceinline__ HalfStats half_stats_2(const EpiArgs& e, const float 
       if (valid) m = fmaxf(m, lv[t]);
       y[t] = -INFINITY;
       if constexpr (TM == 2) {
-        if (valid && qa[t] > 0.f) y[t] = logf(qa[t]) * e.invT;
+        if (valid && qa[t] > 0.f) y[t] = __logf(qa[t]) * e.invT;
         ymax = fmaxf(ymax, y[t]);
       }
     }
@@ -526,11 +530,11 @@ __device__ __forceinline__ HalfStats half_stats_2(const EpiArgs& e, const float 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const bool valid = live && n0 + t * kSub < e.N;
-      if (valid) se += expf((lv[t] - mx) * e.invT);
+      if (valid) se += __expf((lv[t] - mx) * e.invT);
       if constexpr (TM == 1) {
         if (valid) sq += qa[t];
       } else {
-        if (y[t] > -INFINITY) sq += expf(y[t] - ymax);
+        if (y[t] > -INFINITY) sq += __expf(y[t] - ymax);
       }
     }
     h.mx = mx; h.se = sum16(se); h.ym = TM == 1 ? 0.f : ymax; h.sq = sum16(sq);
