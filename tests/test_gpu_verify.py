@@ -162,6 +162,10 @@ RULE_CASES = [
     (16, 2, 130, 1.3, 0.6), (6, 0, 300, 1.0, 1.0), (5, 3, 64, 1.0, 0.5), (7, 3, 1, 1.0, 1.0),
     (2, 5, 70000, 0.9, 0.95), (1, 4, 32000, 1.0, 1.0), (1, 5, 128256, 1.0, 1.0),
     (2, 3, 128256, 0.7, 0.9), (1, 2, 600000, 1.0, 1.0), (3, 4, 129, 0.0, 1.0),
+    # extremes: a nucleus of about one token, near-greedy and near-flat
+    # temperatures, top-p with V = 1
+    (4, 4, 3000, 1.0, 0.01), (4, 4, 3000, 0.05, 0.9), (3, 3, 3000, 8.0, 0.5),
+    (2, 3, 1, 0.7, 0.9),
 ]
 
 
