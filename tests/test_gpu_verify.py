@@ -92,6 +92,10 @@ CASES = [
     # one-row-group shape (18 rows, sampling with top-p; 16 rows, greedy)
     ("bf16-wide-lm-1024", 3, 5, 128, 192, 70000, 1, "bf16", 0.9, 0.95, False, {}),
     ("bf16-wide-lm-1024-greedy", 4, 3, 96, 160, 66000, 1, "bf16", 0.0, 1.0, True, {}),
+    # up projections of 14336 columns at up to 80 rows (one K pass per work
+    # group when 64-column blocks fill the chip): K of 2 and 8 k-steps
+    ("bf16-wide-14336-up", 3, 5, 64, 14336, 500, 1, "bf16", 1.0, 1.0, True, {}),
+    ("bf16-wide-14336-up-72", 8, 8, 256, 14336, 700, 1, "bf16", 0.7, 0.9, False, {}),
     ("bf16-fma", 2, 4, 192, 448, 900, 2, "bf16", 1.0, 1.0, True,
      {"keep_rowmajor": True, "mfma_min_rows": 10 ** 6}),
     ("bf16-fma-many-rows", 12, 3, 136, 200, 333, 1, "bf16", 0.8, 1.0, False,
