@@ -253,12 +253,62 @@ struct ToppShared {
 // over an order-preserving 32-bit key, 11, 11 and 10 bits, the first
 // splitting each power-of-two range of values in four so that its
 // crossing bucket is a small part of even a flat distribution.
+// The row's (max, 1 / Z) from its unit statistics, as k_rowstats defines
+// them (two block reductions: the max over the units' maxima, then the sum
+// of s exp((m - max) / T); draft rows at T == 1 a plain sum), written to
+// the row table with the no-nucleus defaults that a cut overwrites.  The
+// top-p kernel does this for its row itself, one launch fewer.
+template <bool ISQ>
+__device__ __forceinline__ void topp_row_stats(const SampleArgs& a, int row, ToppShared& sh, float* ri,
+                                               float& m_out, float& invz_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t srow = ISQ ? (size_t)(row - a.M) : (size_t)row;
+  const float2* st = reinterpret_cast<const float2*>(ISQ ? a.qst : a.pst) + srow * a.G;
+  const bool plain_sum = ISQ && a.tmode == 1;
+  const float it = ISQ ? 1.f : a.invT;
+  float* red = reinterpret_cast<float*>(sh.hist);   // scratch before the histograms
+  float mx = -INFINITY;
+  for (int t = tid; t < a.Gu; t += kToppThreads) {
+    const float2 v = st[t];
+    if (v.y > 0.f) mx = fmaxf(mx, v.x);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int w = 0; w < kToppWaves; ++w) M = fmaxf(M, red[w]);
+  float sum = 0.f;
+  for (int t = tid; t < a.Gu; t += kToppThreads) {
+    const float2 v = st[t];
+    if (plain_sum) sum += v.y;
+    else if (v.y > 0.f) sum += v.y * expf((v.x - M) * it);
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) red[kToppWaves + wave] = sum;
+  __syncthreads();
+  float S = 0.f;
+  for (int w = 0; w < kToppWaves; ++w) S += red[kToppWaves + w];
+  m_out = plain_sum ? 0.f : M;
+  invz_out = 1.0f / S;
+  if (tid == 0) {
+    ri[RI_M] = m_out;
+    ri[RI_INVZ] = invz_out;
+    ri[RI_THR] = 0.f;
+    ri[RI_TIE] = 0.f;
+    ri[RI_INVZN] = 1.0f;
+    ri[RI_NUC] = 0.f;
+  }
+  __syncthreads();   // the scratch becomes histograms
+}
+
 template <bool ISQ>
 __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* ri = a.rowinfo + (size_t)row * kRowInfo;
   const float* src = ISQ ? a.q + (size_t)(row - a.M) * a.V : a.logits + (size_t)row * a.ldl;
-  const float m = ri[RI_M], invZ = ri[RI_INVZ], invT = a.invT;
+  float m, invZ;
+  topp_row_stats<ISQ>(a, row, sh, ri, m, invZ);
+  const float invT = a.invT;
   const int tmode = a.tmode, V = a.V;
 
   // Masses only place the cut, so they use the hardware exp2 / log2: p rows
@@ -974,7 +1024,8 @@ hipError_t launch_sampling(const SampleArgs& a, hipStream_t st) {
   const bool topp = a.tmode != 0 && a.top_p < 1.0f;
   const bool fuse = fuse_rowstats(a, kResThreads);
   // one work group per row combines the statistics, in parallel over rows
-  if (!fuse)
+  // with top-p, the top-p kernel merges each row's statistics itself
+  if (!fuse && !topp)
     hipLaunchKernelGGL(k_rowstats, dim3(a.tmode != 0 ? a.M + qrows : a.M), dim3(kRowThreads), 0, st, a);
   if (topp) hipLaunchKernelGGL(k_topp, dim3(a.M + qrows), dim3(kToppThreads), 0, st, a);
   hipLaunchKernelGGL(k_decide_chunks, dim3(a.tmode != 0 ? a.nch : 1, a.B), dim3(kResThreads), 0, st, a,
