@@ -139,8 +139,36 @@ __device__ __forceinline__ void epi_prefetch(const EpiArgs& e, int M, int c0, in
   }
 }
 
+// 1 / rms of row `wave` (when < M) from the sums of squares that
+// epi_prefetch loaded, into sh_inv.  The MFMA GEMM runs it right after
+// issuing its first weight loads, so the butterfly and the square root
+// overlap the weight latency instead of lengthening the epilogue; the
+// order of the sums is run_epilogue's, so the bits are too.
+__device__ __forceinline__ void early_inv_rms(const EpiArgs& e, int M, float* sh_inv,
+                                              const float (&pv)[8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave >= M) return;
+  float part[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) part[j] = pv[j];
+  const float* ps = e.ss_in + (size_t)wave * e.ss_ld;
+  for (int t0 = 8 * kWave; t0 < e.ss_n; t0 += 8 * kWave) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t0 + j * kWave + lane;
+      part[j] += t < e.ss_n ? ps[t] : 0.f;
+    }
+  }
+  float s = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+  s = wave_sum(s);
+  if (lane == 0) sh_inv[wave] = 1.0f / sqrtf(s * e.inv_d + e.eps);
+}
+
+// rms_early: the UP rows below nwaves already hold 1 / rms in sh_inv
+// (early_inv_rms), behind a barrier the caller has passed since.
 __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const float* res, int ldr,
-                             float* sh_inv, int nwaves, const float (&pv)[8]) {
+                             float* sh_inv, int nwaves, const float (&pv)[8],
+                             bool rms_early = false) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15;
   if (e.kind == EPI_UP && e.rms) {
@@ -160,7 +188,7 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
     // then a butterfly; the order is fixed, so the bits are too.  The
     // wave's first row was prefetched; its next three rows are loaded
     // together, so they cost one round trip, not three.
-    for (int r0 = wave; r0 < M; r0 += 4 * nwaves) {
+    for (int r0 = wave + (rms_early ? nwaves : 0); r0 < M; r0 += 4 * nwaves) {
       float part[4][8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -191,7 +219,7 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
         }
       }
     }
-    __syncthreads();
+    if (!rms_early || M > nwaves) __syncthreads();
   }
   const int items = M * nt;
   int k = 0;
@@ -337,6 +365,10 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
   // weights (a cache hit) with the all-zero activation step, so its MFMAs
   // add nothing, every path issues the same loads and each wait covers only
   // the oldest stage.  sched_barrier keeps the issue order of the stages.
+  // An UP epilogue that sums squares itself takes each wave's first row's
+  // 1 / rms while the first k-steps load (the barrier after the partial
+  // tiles orders it before its readers).
+  const bool rms_early = a.e.kind == EPI_UP && !a.e.rms;
   int k = kg;
   if (wave_live && k < KS) {
     const int n = (KS - k + KG - 1) / KG;            // k-steps of this wave
@@ -347,6 +379,8 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
       SV_LOAD(u, min(kk, klast), kk <= klast ? kk : KS);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (rms_early) early_inv_rms(a.e, M, sh_inv, pv);
+    __builtin_amdgcn_sched_barrier(0);
     for (int it = 0; it < n; it += PIPE) {
 #pragma unroll
       for (int u = 0; u < PIPE; ++u) {
@@ -357,6 +391,8 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  } else if (rms_early) {
+    early_inv_rms(a.e, M, sh_inv, pv);
   }
 #undef SV_LOAD
 #undef SV_COMPUTE
@@ -410,7 +446,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
     }
     __syncthreads();
   }
-  run_epilogue(a.e, M, c0, NT, res, ldr, sh_inv, nwaves, pv);
+  run_epilogue(a.e, M, c0, NT, res, ldr, sh_inv, nwaves, pv, rms_early);
 }
 
 // ---------------------------------------------------------------- LM epilogue from registers
