@@ -32,7 +32,7 @@ Modules:
   model   -- the synthetic target: RMSNorm / up / SiLU / down / residual MLP
              blocks, then the LM head
   rule    -- temperature, top-p, the ratio test, residual resampling, bonus,
-             greedy branch, and the margin of every decision
+             greedy branch, and the margin, slack and token band of every decision
   verify  -- spec_verify / spec_verify_from_logits over a batch
 
 Parity status of each part (what pins it) is listed in the module docstrings.
@@ -41,13 +41,14 @@ Parity status of each part (what pins it) is listed in the module docstrings.
 from .philox import philox4x64_10, row_uniforms, PURPOSE_VERIFY, PURPOSE_DRAFT
 from .model import bf16_to_f64, as_f64, rmsnorm, silu, forward
 from .rule import (warp_logits, warp_probs, nucleus_mask, accept_test,
-                   inverse_cdf, verify_row, verify_row_greedy, MARGIN, TopP)
+                   inverse_cdf, cdf_band, verify_row, verify_row_greedy, MARGIN, TopP,
+                   Decision)
 from .verify import spec_verify, spec_verify_from_logits, VerifyResult
 
 __all__ = [
     "philox4x64_10", "row_uniforms", "PURPOSE_VERIFY", "PURPOSE_DRAFT",
     "bf16_to_f64", "as_f64", "rmsnorm", "silu", "forward",
     "warp_logits", "warp_probs", "nucleus_mask", "accept_test", "inverse_cdf",
-    "verify_row", "verify_row_greedy", "MARGIN", "TopP",
+    "cdf_band", "verify_row", "verify_row_greedy", "MARGIN", "TopP", "Decision",
     "spec_verify", "spec_verify_from_logits", "VerifyResult",
 ]

@@ -21,9 +21,13 @@ generator; numpy advances its counter by one before it produces a block).
 Uniform layout (a convention shared with the HIP library, fixed here):
     key     = (seed, 0)
     counter = (i, b, purpose, 0)        i = position, b = batch row
-    r_{b,i} = (word0 >> 40) * 2**-24    acceptance draw
-    u_{b,i} = (word1 >> 40) * 2**-24    inverse-CDF draw at row i
-Both lie in [0, 1) and are exact in float32 and float64.  purpose 0 is the
+    r_{b,i} = (word0 >> 40) * 2**-24    acceptance draw (exact in float32,
+                                        where the ratio test runs)
+    u_{b,i} = (word1 >> 11) * 2**-53    inverse-CDF draw at row i (exact in
+                                        float64, where u * R is formed, so
+                                        the sampled law is not rounded to
+                                        steps of 2**-24)
+Both lie in [0, 1).  purpose 0 is the
 verify step; purpose 1 is reserved for a harness that draws draft tokens, so
 the two never share numbers.  The layout itself is pinned only by GPU/CPU
 agreement (parity), since it is a convention rather than a fact of the pages.
@@ -65,7 +69,12 @@ def words_to_unit(word):
     return (int(word) >> 40) * (2.0 ** -24)
 
 
+def words_to_unit53(word):
+    """Top 53 bits of a 64-bit word as a float in [0, 1)."""
+    return (int(word) >> 11) * (2.0 ** -53)
+
+
 def row_uniforms(seed, b, i, purpose=PURPOSE_VERIFY):
     """(r, u) for batch row b, position i: acceptance draw and resample draw."""
     w = philox4x64_10((i, b, purpose, 0), (seed, 0))
-    return words_to_unit(w[0]), words_to_unit(w[1])
+    return words_to_unit(w[0]), words_to_unit53(w[1])

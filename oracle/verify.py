@@ -21,16 +21,17 @@ import numpy as np
 
 from .model import as_f64, forward
 from .philox import row_uniforms
-from .rule import MARGIN, verify_row, verify_row_greedy, warp_logits, warp_probs
+from .rule import verify_row, verify_row_greedy, warp_logits, warp_probs
 
 
 @dataclass
 class VerifyResult:
     n_accepted: np.ndarray
     emitted: np.ndarray
-    margins: list = field(default_factory=list)   # per row: [(kind, pos, value)]
+    decisions: list = field(default_factory=list)  # per row: [rule.Decision]
     logits: np.ndarray = None
     cuts: list = field(default_factory=list)      # per row: (p TopPs, q TopPs) at T > 0
+    drafts: np.ndarray = None                     # the draft tokens the rule read
 
     def nucleus_uncertain(self, b):
         """(p rows, q rows) of row b whose top-p membership is uncertain."""
@@ -40,19 +41,15 @@ class VerifyResult:
         return ({i for i, c in enumerate(pc) if c.uncertain},
                 {i for i, c in enumerate(qc) if c.uncertain})
 
-    def row_min_margin(self, b):
-        vals = [m[2] for m in self.margins[b]]
-        return min(vals) if vals else np.inf
-
-    def flagged_rows(self, threshold=MARGIN):
-        return [b for b in range(len(self.margins))
-                if self.row_min_margin(b) < threshold]
+    def row_flagged(self, b):
+        """Whether any decision of row b could flip on the other side."""
+        return any(d.flagged for d in self.decisions[b])
 
     def n_decisions(self):
-        return sum(len(m) for m in self.margins)
+        return sum(len(d) for d in self.decisions)
 
-    def n_flagged_decisions(self, threshold=MARGIN):
-        return sum(1 for row in self.margins for m in row if m[2] < threshold)
+    def n_flagged_decisions(self):
+        return sum(1 for row in self.decisions for d in row if d.flagged)
 
 
 def _check_scalars(temperature, top_p):
@@ -63,13 +60,15 @@ def _check_scalars(temperature, top_p):
 
 
 def spec_verify_from_logits(logits, draft_tokens, q, temperature, top_p, seed,
-                            batch_ids=None):
+                            batch_ids=None, logit_tol=0.0):
     """Acceptance rule for a batch given target logits [B, gamma+1, V].
 
     q is [B, gamma, V] (the draft's T = 1 probabilities); it is not read and
     may be None when temperature == 0.  batch_ids gives the batch index b of
     each row for its uniforms (default 0..B-1), so a few sequences of a larger
-    batch can be checked on their own.
+    batch can be checked on their own.  logit_tol only shapes the decision
+    records: the other implementation's logits of a row may differ from these
+    by up to logit_tol * max |logit| of the row (0: it reads the same logits).
     """
     _check_scalars(temperature, top_p)
     ell = as_f64(logits)
@@ -93,18 +92,19 @@ def spec_verify_from_logits(logits, draft_tokens, q, temperature, top_p, seed,
         raise ValueError("batch_ids must have one entry per row")
     n_acc = np.full(B, -1, dtype=np.int32)
     emitted = np.full((B, G1), -1, dtype=np.int32)
-    margins, cuts = [], []
+    decisions, cuts = [], []
     for b in range(B):
         xs = draft[b]
         if np.any(xs < 0) or np.any(xs >= V):
-            margins.append([])
+            decisions.append([])
             cuts.append(None)
             continue
+        lerr = logit_tol * np.abs(ell[b]).max(axis=-1)
         if greedy:
-            j, tok, mg = verify_row_greedy(ell[b], xs)
+            j, tok, mg = verify_row_greedy(ell[b], xs, lerr)
             cuts.append(None)
         else:
-            p_rows, p_mg = zip(*[warp_logits(ell[b, i], temperature, top_p)
+            p_rows, p_mg = zip(*[warp_logits(ell[b, i], temperature, top_p, lerr[i])
                                  for i in range(G1)])
             q_rows, q_mg = zip(*[warp_probs(qq[b, i], temperature, top_p)
                                  for i in range(gamma)]) if gamma else ((), ())
@@ -114,8 +114,8 @@ def spec_verify_from_logits(logits, draft_tokens, q, temperature, top_p, seed,
         n_acc[b] = j
         emitted[b, :j] = xs[:j]
         emitted[b, j] = tok
-        margins.append(mg)
-    return VerifyResult(n_acc, emitted, margins, ell, cuts)
+        decisions.append(mg)
+    return VerifyResult(n_acc, emitted, decisions, ell, cuts, draft)
 
 
 def spec_verify(hidden, weights, draft_tokens, q, temperature, top_p, seed):

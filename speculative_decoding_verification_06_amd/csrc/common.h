@@ -54,10 +54,11 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid
 //             so a single MFMA covers every term of five rows and the
 //             terms are summed after the k-loop
 // xs_index returns the bf16 index of term 0 of (row, col); term p sits at
-// +p * xs_term_step(stacked).
+// +p * xs_term_step(stacked).  Both are host functions too, so the host-side
+// access check evaluates the very formulas the kernels use.
 constexpr int kStackRows = 5;
-__device__ __forceinline__ int xs_term_step(bool stacked) { return stacked ? 8 * kStackRows : 512; }
-__device__ __forceinline__ size_t xs_index(int row, int col, int ks, bool stacked) {
+__host__ __device__ __forceinline__ int xs_term_step(bool stacked) { return stacked ? 8 * kStackRows : 512; }
+__host__ __device__ __forceinline__ size_t xs_index(int row, int col, int ks, bool stacked) {
   const int lane_hi = 16 * ((col & 31) >> 3), s = col >> 5, j = col & 7;
   if (stacked) {
     const size_t frag = (size_t)(row / kStackRows) * (ks + 1) + s;
@@ -94,13 +95,15 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64
   }
 }
 
-// Uniforms of batch row b, position i: word 0 -> r (ratio test), word 1 -> u
-// (inverse CDF); top 24 bits scaled by 2^-24, exact in fp32.
-__device__ __forceinline__ void row_uniforms(uint64_t seed, int b, int i, float& r, float& u) {
+// Uniforms of batch row b, position i: word 0 -> r (ratio test), its top 24
+// bits scaled by 2^-24, exact in fp32 where the test runs; word 1 -> u
+// (inverse CDF), its top 53 bits scaled by 2^-53, exact in fp64 where u * R
+// is formed, so the sampled law is not rounded to steps of 2^-24.
+__device__ __forceinline__ void row_uniforms(uint64_t seed, int b, int i, float& r, double& u) {
   uint64_t c[4] = {(uint64_t)i, (uint64_t)b, 0ull, 0ull};
   philox4x64_10(c, seed, 0ull);
   r = (float)(uint32_t)(c[0] >> 40) * 0x1.0p-24f;
-  u = (float)(uint32_t)(c[1] >> 40) * 0x1.0p-24f;
+  u = (double)(c[1] >> 11) * 0x1.0p-53;
 }
 
 // ---- cross-lane steps ------------------------------------------------------

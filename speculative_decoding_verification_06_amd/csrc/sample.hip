@@ -820,7 +820,8 @@ __global__ __launch_bounds__(kResThreads) void k_decide_chunks(SampleArgs a, boo
       const float qx = i == tid ? q0 : a.q[qrow * a.V + x];
       const float pp = p_prime(ri_of(i), lx, x, a.invT);
       const float qq = q_prime(ri_of(G1 + i), qx, x, a.tmode, a.invT);
-      float r, u;
+      float r;
+      double u;
       row_uniforms(a.seed, b, i, r, u);
       reject = !(r * qq < pp);
     }
@@ -888,7 +889,8 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
   if (a.nch <= kResThreads && ci < a.nch) { xw = cs[2 * ci]; xp = cs[2 * ci + 1]; }
   const int j = a.dec[4 * b];
   if (j < 0) return;
-  float r, u;
+  float r;
+  double u;
   row_uniforms(a.seed, b, j, r, u);
   if (tid == 0) { sh_c = INT_MAX; sh_cand = INT_MAX; sh_last = -1; sh_base = 0.0; sh_lastbase = 0.0; }
   int usep = 0;
@@ -903,7 +905,7 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
       xw = xp;
       ex = wave_excl_scan_f64(xw, &total);
     }
-    target = (double)u * total;
+    target = u * total;
     const uint64_t over = __ballot(in && ex + xw > target);
     const uint64_t pos = __ballot(in && xw > 0.0);
     c = over ? __ffsll((unsigned long long)over) - 1 : (pos ? 63 - __clzll((unsigned long long)pos) : 0);
@@ -917,7 +919,7 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
       xw = xp;
       ex = block_excl_scan_f64(xw, lds_w, &total);
     }
-    target = (double)u * total;
+    target = u * total;
     if (in && ex + xw > target) atomicMin(&sh_c, tid);
     if (in && xw > 0.0) atomicMax(&sh_last, tid);
     __syncthreads();
@@ -941,7 +943,7 @@ __global__ __launch_bounds__(kResThreads) void k_res_select(SampleArgs a) {
     usep = pass;
     if (total > 0.0) break;
   }
-  target = (double)u * total;
+  target = u * total;
   // the first chunk whose inclusive prefix exceeds the target (the last
   // chunk when rounding leaves none)
   double run = 0.0;

@@ -1,9 +1,11 @@
 """Shared helpers for parity tests: workload construction and comparison.
 
 Inputs are built with synth (random draws) and the oracle (target logits,
-softmax), never with the HIP path.  Comparison follows the margin rule: a
-GPU row must equal the oracle row unless the oracle made a knife-edge
-decision (margin < oracle.MARGIN) in that row.
+softmax), never with the HIP path.  Comparison follows the oracle's decision
+records: a GPU row must equal the oracle row unless its first difference is
+a decision the oracle flags (its margin is below the slack the other side's
+arithmetic may use), and then the GPU's token must lie in that decision's
+band; such rows are capped at 0.1% of the draws.
 """
 
 import collections
@@ -85,6 +87,14 @@ def greedy_drafts(ell, key, agree=0.75):
 
 # ---------------------------------------------------------------- comparison
 
+# Logit tolerance the token comparison of a full pass assumes (the GEMM
+# path's logits of a row within LOGIT_TOL * max |logit| of the float64
+# forward).  Tests assert it before comparing tokens; it is tighter than the
+# 1e-3 logit contract because a decision can only be checked against the
+# oracle if the logits it reads are close.
+LOGIT_TOL = 1e-5
+
+
 def logits_rel_err(gpu, ref):
     """Per row max |gpu - ref| / max |ref|."""
     gpu = np.asarray(gpu, dtype=np.float64)
@@ -92,25 +102,73 @@ def logits_rel_err(gpu, ref):
     return np.abs(gpu - ref).max(axis=-1) / np.maximum(np.abs(ref).max(axis=-1), 1e-30)
 
 
+class TokenReport:
+    """Row-by-row comparison of GPU outputs with the oracle's decisions."""
+
+    def __init__(self):
+        self.rows = 0
+        self.mismatched = []      # rows that differ in any way
+        self.unexplained = []     # rows whose first difference no flagged decision explains
+        self.flagged = collections.Counter()    # flagged decisions by kind
+        self.total = collections.Counter()      # decisions by kind
+        self.knife = 0            # ratio tests with |r - p'/q'| < MARGIN (the north-star count)
+        self.band_sizes = []      # band sizes of flagged token decisions
+
+    @property
+    def draws(self):
+        return sum(self.total.values())
+
+    def record(self):
+        return {"rows": self.rows, "mismatched_rows": len(self.mismatched),
+                "unexplained_rows": len(self.unexplained), "draws": self.draws,
+                "ratio_knife_edges": self.knife, "flagged": dict(self.flagged),
+                "decisions": dict(self.total),
+                "flagged_band_max": max(self.band_sizes) if self.band_sizes else 0}
+
+
+def _row_explained(n_g, e_g, n_r, e_r, decs, draft_row):
+    """Whether GPU row (n_g, e_g) is one the oracle's decisions allow."""
+    if n_r < 0:
+        return False
+    if n_g != n_r:
+        # the first ratio test (or argmax check) the two sides took
+        # differently must be a flagged one
+        j = min(n_g, n_r)
+        d = next((d for d in decs if d.pos == j and d.kind in ("accept", "argmax")), None)
+        if d is None or not d.flagged or not (0 <= n_g <= len(draft_row)):
+            return False
+        if d.kind == "argmax" and not d.allows(draft_row[j]):
+            return False
+        return np.array_equal(e_g[:n_g], draft_row[:n_g])
+    final = decs[-1]
+    return np.array_equal(e_g[:n_g], e_r[:n_r]) and final.flagged and final.allows(e_g[n_g]) \
+        and (e_g[n_g + 1:] == -1).all()
+
+
 def compare_tokens(n_gpu, emit_gpu, ref, rows=None):
-    """Returns (mismatched rows, unexplained rows, flagged decisions by kind,
-    decisions by kind)."""
+    """TokenReport of GPU rows against the oracle result `ref` (rows: the
+    oracle's row indices the GPU rows correspond to)."""
     rows = range(len(ref.n_accepted)) if rows is None else rows
-    mism, unexplained = [], []
+    rep = TokenReport()
     for j, b in enumerate(rows):
-        same = int(n_gpu[j]) == int(ref.n_accepted[b]) and \
-            np.array_equal(np.asarray(emit_gpu[j]), ref.emitted[b])
-        if not same:
-            mism.append(b)
-            if ref.row_min_margin(b) >= oracle.MARGIN:
-                unexplained.append(b)
-    flagged, total = collections.Counter(), collections.Counter()
-    for b in rows:
-        for kind, _, m in ref.margins[b]:
-            total[kind] += 1
-            if m < oracle.MARGIN:
-                flagged[kind] += 1
-    return mism, unexplained, flagged, total
+        rep.rows += 1
+        n_g, e_g = int(n_gpu[j]), np.asarray(emit_gpu[j])
+        n_r, e_r = int(ref.n_accepted[b]), ref.emitted[b]
+        decs = ref.decisions[b]
+        for d in decs:
+            rep.total[d.kind] += 1
+            if d.flagged:
+                rep.flagged[d.kind] += 1
+                if d.kind != "accept":
+                    rep.band_sizes.append(len(d.band) if d.band is not None else -1)
+            if d.kind == "accept" and d.raw is not None and d.raw < oracle.MARGIN:
+                rep.knife += 1
+        if n_g == n_r and np.array_equal(e_g, e_r):
+            continue
+        rep.mismatched.append(b)
+        if not _row_explained(n_g, e_g, n_r, e_r, decs, np.asarray(ref.drafts[b])):
+            rep.unexplained.append(b)
+    return rep
 
 
 def log_measurement(record):
@@ -121,43 +179,82 @@ def log_measurement(record):
             f.write(json.dumps(record) + "\n")
 
 
-def assert_tokens_match(n_gpu, emit_gpu, ref, rows=None, what=""):
-    """Rows must match unless the oracle made a knife-edge decision in them;
-    knife-edge ratio tests (|r - p'/q'| < 1e-5) must stay under 0.1% of the
-    ratio tests; the other knife-edge kinds are counted and reported."""
-    mism, unexplained, flagged, total = compare_tokens(n_gpu, emit_gpu, ref, rows)
-    log_measurement({"what": what, "rows": len(ref.n_accepted) if rows is None else len(rows),
-                     "mismatched_rows": len(mism), "flagged": dict(flagged),
-                     "decisions": dict(total)})
-    assert not unexplained, f"{what}: rows differ without a knife-edge decision: {unexplained[:10]}"
-    assert flagged["accept"] <= max(1, 0.001 * total["accept"]), \
-        f"{what}: {flagged['accept']} knife-edge ratio tests of {total['accept']}"
-    return mism, sum(flagged.values()), sum(total.values())
+def cap_applies(V, top_p, same_logits):
+    """Whether the 0.1% cap on differing rows is held.  Not for vocabularies
+    of 65536 tokens and more when the oracle recomputed the logits in
+    float64 or a nucleus is cut: one token then holds about 1e-5 of the mass,
+    so a logit difference of 1e-6 relative, or the float32 error of the
+    cumulative mass at the cut, moves a sample's CDF by as much as a token's
+    width, and a few percent of the samples may land on a neighbour.  Those
+    rows are still held to the decision records (flagged, token in band) and
+    counted."""
+    return V < 65536 or (same_logits and top_p >= 1.0)
 
 
-def ref_probs(ell, q, T, top_p):
-    """Oracle p' [B][gamma+1][V] and q' [B][gamma][V] (float64)."""
+def assert_tokens_match(n_gpu, emit_gpu, ref, rows=None, what="", cap=True):
+    """The token contract:
+      * every GPU row equals the oracle row, except rows whose first
+        difference is a flagged decision of the oracle (a ratio test within
+        its slack, or a sample / argmax within its slack that emitted a token
+        of the decision's band);
+      * with `cap` (both sides read the same logits), such rows are fewer
+        than 0.1% of the draws (decisions); without it (the oracle recomputed
+        the logits in float64) they are counted and logged;
+      * ratio tests with |r - p'/q'| < 1e-5 stay under 0.1% of the ratio
+        tests (at least one allowed).
+    Counts of every kind are logged; the report is returned."""
+    rep = compare_tokens(n_gpu, emit_gpu, ref, rows)
+    rec = rep.record()
+    rec["what"] = what
+    log_measurement(rec)
+    assert not rep.unexplained, \
+        f"{what}: rows differ without a flagged decision: {rep.unexplained[:10]} ({rec})"
+    if cap:
+        assert len(rep.mismatched) <= 0.001 * rep.draws, \
+            f"{what}: {len(rep.mismatched)} differing rows in {rep.draws} draws ({rec})"
+    assert rep.knife <= max(1, 0.001 * rep.total["accept"]), \
+        f"{what}: {rep.knife} knife-edge ratio tests of {rep.total['accept']}"
+    return rep
+
+
+def ref_probs(ell, q, T, top_p, logit_tol=0.0):
+    """Oracle p' [B][gamma+1][V] and q' [B][gamma][V] (float64) and their
+    cuts, as the oracle's spec_verify_from_logits forms them."""
     B, G1, V = ell.shape
-    p = np.stack([[oracle.warp_logits(ell[b, i], T, top_p)[0] for i in range(G1)] for b in range(B)])
-    qq = np.stack([[oracle.warp_probs(q[b, i], T, top_p)[0] for i in range(G1 - 1)]
-                   for b in range(B)]) if G1 > 1 else np.zeros((B, 0, V))
-    return p, qq
+    pw = [[oracle.warp_logits(ell[b, i], T, top_p, logit_tol * np.abs(ell[b, i]).max())
+           for i in range(G1)] for b in range(B)]
+    qw = [[oracle.warp_probs(q[b, i], T, top_p) for i in range(G1 - 1)] for b in range(B)]
+    return pw, qw
 
 
-def compare_probs(p_gpu, q_gpu, ref, ell, q, T, top_p, rows, what):
-    """p' and q' within 1e-5 absolute, on every row whose nucleus is certain
-    (a knife-edge cut renormalises the whole row by one token's mass)."""
-    pr, qr = ref_probs(ell, q, T, top_p)
-    worst = 0.0
+def compare_probs(p_gpu, q_gpu, ref, ell, q, T, top_p, rows, what, logit_tol=0.0):
+    """p' and q' within 1e-5 absolute on every row.  The entries of tokens
+    whose nucleus membership is uncertain are checked to be either dropped
+    (0) or kept (their renormalised value), and every other entry of such a
+    row may also move by its renormalisation, value x uncertain mass."""
+    pw, qw = ref_probs(ell, q, T, top_p, logit_tol)
+    worst, masked, rows_masked = 0.0, 0, 0
     for b in rows:
         if ref.n_accepted[b] < 0:
             continue
-        up, uq = ref.nucleus_uncertain(b)
-        for i in range(pr.shape[1]):
-            if i not in up:
-                worst = max(worst, float(np.abs(p_gpu[b, i] - pr[b, i]).max()))
-        for i in range(qr.shape[1]):
-            if i not in uq:
-                worst = max(worst, float(np.abs(q_gpu[b, i] - qr[b, i]).max()))
-    log_measurement({"what": f"{what} probs", "abs_err_max": worst})
-    assert worst <= 1e-5, f"{what}: p'/q' abs err {worst:.2e}"
+        for gpu_row, warps in ((p_gpu[b], pw[b]), (q_gpu[b], qw[b])):
+            for i, (w, cut) in enumerate(warps):
+                g = np.asarray(gpu_row[i], dtype=np.float64)
+                tol = 1e-5 + 2.0 * cut.mass * w
+                diff = np.abs(g - w)
+                if cut.uncertain:
+                    rows_masked += 1
+                    unc = np.array(sorted(cut.uncertain))
+                    masked += len(unc)
+                    alt = np.array([cut.alt[v] for v in unc])
+                    ok = (np.abs(g[unc]) <= 1e-5) | (np.abs(g[unc] - np.maximum(w[unc], alt))
+                                                      <= 1e-5 + 2.0 * cut.mass * alt)
+                    assert ok.all(), f"{what}: uncertain nucleus token neither kept nor dropped"
+                    diff[unc] = 0.0
+                excess = diff - tol
+                worst = max(worst, float((diff - (tol - 1e-5)).max()))
+                assert (excess <= 0).all(), \
+                    f"{what}: p'/q' abs err {float(diff.max()):.2e} (row {b}, {i})"
+    log_measurement({"what": f"{what} probs", "abs_err_max": worst,
+                     "uncertain_entries_masked": masked, "rows_with_uncertain_cut": rows_masked})
+    return worst, masked, rows_masked

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import philox4x64_10, row_uniforms
-from oracle.philox import words_to_unit
+from oracle.philox import words_to_unit, words_to_unit53
 
 M64 = (1 << 64) - 1
 
@@ -45,18 +45,27 @@ def test_matches_numpy_random_grid():
         assert philox4x64_10(ctr, key) == numpy_block(ctr, key)
 
 
-def test_unit_mapping_is_24_bit_and_in_range():
+def test_unit_mapping_ranges_and_exactness():
+    """r: top 24 bits, exact in float32; u: top 53 bits, exact in float64."""
     assert words_to_unit(0) == 0.0
     assert words_to_unit(M64) == 1.0 - 2.0 ** -24
     assert words_to_unit(1 << 40) == 2.0 ** -24
     assert words_to_unit((1 << 40) - 1) == 0.0
+    assert words_to_unit53(0) == 0.0
+    assert words_to_unit53(M64) == 1.0 - 2.0 ** -53
+    assert words_to_unit53(1 << 11) == 2.0 ** -53
+    assert words_to_unit53((1 << 11) - 1) == 0.0
+    fine = 0
     for seed in range(5):
         for i in range(4):
             r, u = row_uniforms(seed, 3, i)
             for x in (r, u):
                 assert 0.0 <= x < 1.0
-                assert float(np.float32(x)) == x          # exact in float32
-                assert (x * 2 ** 24) == int(x * 2 ** 24)
+            assert float(np.float32(r)) == r                  # exact in float32
+            assert (r * 2 ** 24) == int(r * 2 ** 24)
+            assert (u * 2 ** 53) == int(u * 2 ** 53)
+            fine += (u * 2 ** 24) != int(u * 2 ** 24)       # bits below 2^-24 are used
+    assert fine >= 18
 
 
 def test_streams_are_distinct():

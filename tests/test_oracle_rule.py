@@ -105,12 +105,16 @@ def test_top_p_uncertain_tokens():
 def test_uncertain_token_ratio_test_is_a_knife_edge():
     ell = np.log(np.array([0.5, 0.2, 0.2 * (1 - 1e-9), 0.1]))
     p, cut = warp_logits(ell, 1.0, 0.6)
+    assert not cut.uncertain              # same logits on both sides: the order is exact
+    p, cut = warp_logits(ell, 1.0, 0.6, logit_err=1e-6)
     assert cut.uncertain == {1, 2}
     q = np.full(4, 0.25)
     _, _, mg = verify_row([p, p], [q], [2], [(0.1, 0.5), (0.5, 0.5)], p_cuts=[cut, cut])
-    assert mg[0][0] == "accept" and mg[0][2] == 0.0
+    assert mg[0].kind == "accept" and mg[0].flagged and mg[0].slack == np.inf
     _, _, mg = verify_row([p, p], [q], [0], [(0.999, 0.5), (0.5, 0.5)], p_cuts=[cut, cut])
-    assert mg[0][2] < abs(0.999 - p[0] / 0.25)
+    # a certain token's ratio test widens its slack by ratio x uncertain mass
+    assert mg[0].margin == abs(0.999 - p[0] / 0.25)
+    assert mg[0].slack >= oracle.MARGIN + p[0] / 0.25 * cut.mass
 
 
 def test_warp_logits_is_library_softmax():
@@ -242,7 +246,12 @@ def test_greedy_is_the_zero_temperature_limit():
 def test_greedy_ties_take_lowest_index():
     ell = np.array([[1.0, 3.0, 3.0], [0.0, 0.0, 0.0]])
     n, tok, m = verify_row_greedy(ell, [2])
-    assert (n, tok) == (0, 1) and m[0][2] == 0.0
+    assert (n, tok) == (0, 1) and m[0].margin == 0.0
+    # reading the same logits, an exact tie is no knife edge: both sides
+    # take the lowest index
+    assert not m[0].flagged
+    n, tok, m = verify_row_greedy(ell, [2], logit_err=1e-3)
+    assert m[0].flagged and m[0].band == {1, 2}
 
 
 def test_bad_token_row_is_rejected_whole():
