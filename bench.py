@@ -13,6 +13,7 @@ GEMM kernels (algorithmic weight bytes / their event-timed duration vs
 8 TB/s), and the float64 CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload mid]
+    python bench.py --sweep-gamma      (verify cost per pass against gamma)
 """
 
 import argparse
@@ -28,7 +29,11 @@ sys.path.insert(0, ROOT)
 METRIC = "verify passes/sec & accepted tokens/sec at B=1, γ=4; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
-MFMA_BOUND_ROWS = 112            # above this many rows the three-term MFMA work exceeds the weight stream
+# The method's own work per weight is 2 flops per row (one multiply-add), so
+# a GEMM of M rows over bf16 weights has M flop per weight byte (M / 2 over
+# fp32 weights).  It is MFMA-bound only above the bf16 ridge,
+# 2500 TFLOP/s / 8 TB/s = 312.5 flop/B.
+RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 POOL = 8
 
 
@@ -43,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--sweep-gamma", action="store_true",
+                    help="only print the verify cost per pass for gamma = 0..8, 16 .. 160 at B = 1 "
+                         "on the mid and large models (one JSON line per point)")
     return ap.parse_args()
 
 
@@ -79,6 +87,60 @@ def copy_probe(mib):
         torch.mul(a, 1.0, out=b)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}))
+
+
+def read_ceiling(torch, sv, nbytes, launches=40):
+    """Average bandwidth of one streaming-read launch of nbytes (fresh data
+    each launch: windows of a buffer larger than the 256 MB Infinity Cache),
+    timed with HIP events on the launch stream."""
+    nbytes = max(16, int(nbytes) // 16 * 16)
+    windows = max(4, -(-(1 << 30) // nbytes))
+    buf = torch.ones(windows * nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(5):
+        sv.stream_read(buf[(i % windows) * nbytes // 4:], sink, nbytes)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        sv.stream_read(buf[(i % windows) * nbytes // 4:], sink, nbytes)
+        b.record()
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in ev) / launches * 1e3
+    del buf
+    torch.cuda.empty_cache()
+    return {"bytes_per_launch": nbytes, "avg_launch_us": us, "gbs": nbytes / us / 1e3,
+            "kernel": "spec_stream_read (16-byte non-temporal loads, one launch, fresh data)"}
+
+
+def roofline_of(wl, M, per_launch_bytes, per_launch_s, traffic, ceiling):
+    """Roofline of the weight-streaming GEMMs: the method's own flops
+    (2 M K N per launch), the bound from its intensity against the bf16
+    ridge, and, as a side field, the MFMA rate the kernels execute (three
+    bf16 terms per fp32 activation: 6 M K N)."""
+    wbytes = 4 if wl.wdtype == "f32" else 2
+    kn = per_launch_bytes / wbytes
+    intensity = 2.0 * M * kn / per_launch_bytes
+    gbs = per_launch_bytes / per_launch_s / 1e9
+    method_tflops = 2.0 * M * kn / per_launch_s / 1e12
+    out = {"intensity_flop_per_byte": intensity, "ridge_flop_per_byte": RIDGE_FLOP_PER_BYTE}
+    if intensity < RIDGE_FLOP_PER_BYTE:
+        out.update({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": gbs / HBM_PEAK_GBS})
+    else:
+        out.update({"bound": "mfma", "achieved": method_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": method_tflops / MFMA_BF16_PEAK_TFLOPS})
+    out["traffic"] = traffic
+    out["method_tflops"] = method_tflops
+    if wl.wdtype == "bf16":
+        ex = 3.0 * method_tflops
+        out["mfma_executed"] = {"tflops": ex, "frac_of_bf16_peak": ex / MFMA_BF16_PEAK_TFLOPS,
+                                "note": "three bf16 MFMA terms per fp32 activation"}
+    if ceiling:
+        out["read_ceiling_gbs"] = ceiling["gbs"]
+        out["frac_of_read_ceiling"] = gbs / ceiling["gbs"]
+    return out
 
 
 # ---------------------------------------------------------------- workload (harness side)
@@ -191,6 +253,69 @@ def cpu_baseline(torch, synth, wl, host_weights, hidden0, sig, key, seconds):
                       f"(B={B}, one input set, float64 weights resident) in {el:.1f} s"}
 
 
+# ---------------------------------------------------------------- gamma sweep
+
+SWEEP_GAMMAS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 16, 32, 64, 128, 160]
+
+
+def sweep_gamma(progress, steps=200, warmup=20):
+    """Cost of one verify pass at B = 1 as the number of drafted positions
+    grows, on the mid (d = 4096) and large (d = 8192) models: gamma = 0 is a
+    plain decode step (one row), gamma drafts add gamma rows to the same
+    weight stream.  One JSON line per (model, gamma)."""
+    import torch
+    import synth
+    import speculative_decoding_verification_06_amd as sv
+    torch.cuda.set_device(0)
+    for name in ("mid", "large"):
+        wl = synth.WORKLOADS[name]
+        key = (300 + list(synth.WORKLOADS).index(name),)
+        model = synth.model_torch(key, wl.d, wl.ffn, wl.n_blocks, wl.V, wl.wdtype, "cuda")
+        w = sv.Weights(model["blocks"], model["lm_head"])
+        del model
+        torch.cuda.empty_cache()
+        base_us = None
+        for gamma in SWEEP_GAMMAS:
+            G1 = gamma + 1
+            hid = synth.normal_torch((*key, synth.T_HIDDEN, 100 + gamma), (1, G1, wl.d), 1.0, "cuda")
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(synth.torch_seed(*key, synth.T_DRAFT, 100 + gamma))
+            q = torch.softmax(torch.randn((1, gamma, wl.V), generator=gen, device="cuda") * 2, -1)
+            draft = torch.randint(0, wl.V, (1, gamma), generator=gen, device="cuda").to(torch.int32)
+            qa = q.contiguous() if gamma else None
+            ws = w.workspace(1, gamma)
+            n = torch.empty(1, dtype=torch.int32, device="cuda")
+            e = torch.empty((1, G1), dtype=torch.int32, device="cuda")
+            for k in range(warmup):
+                sv.verify(w, hid, draft, qa, 1.0, 1.0, k, workspace=ws, n_accepted=n, emitted=e)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for k in range(steps):
+                sv.verify(w, hid, draft, qa, 1.0, 1.0, k, workspace=ws, n_accepted=n, emitted=e)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / steps * 1e3
+            w.profile(True)
+            for k in range(50):
+                sv.verify(w, hid, draft, qa, 1.0, 1.0, k, workspace=ws, n_accepted=n, emitted=e)
+            gemm_ms, launches, wbytes = w.profile_read()
+            w.profile(False)
+            gemm_us = gemm_ms * 1e3 / 50
+            base_us = us if gamma == 0 else base_us
+            gbs = wbytes / 50 / (gemm_us * 1e-6) / 1e9
+            print(json.dumps({
+                "sweep": "gamma", "model": name, "B": 1, "gamma": gamma, "rows": G1,
+                "d": wl.d, "ffn": wl.ffn, "blocks": wl.n_blocks, "V": wl.V,
+                "us_per_pass": us, "rel_to_decode": us / base_us,
+                "gemm_us_per_pass": gemm_us, "gemm_hbm_gbs": gbs, "gemm_hbm_frac": gbs / HBM_PEAK_GBS,
+                "method_tflops": 2.0 * G1 * (wbytes / 50 / 2) / (gemm_us * 1e-6) / 1e12,
+                "positions_scored_per_s": G1 / (us * 1e-6)}), flush=True)
+            progress(f"sweep {name} gamma={gamma}: {us:.1f} us/pass")
+        w.close()
+        torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -206,6 +331,10 @@ def main():
 
     def progress(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.sweep_gamma:
+        sweep_gamma(progress)
+        return
 
     progress("importing torch")
     import torch
@@ -268,10 +397,9 @@ def main():
     per_launch_bytes = wbytes / launches
     per_launch_s = gemm_ms / 1e3 / launches
     achieved = per_launch_bytes / per_launch_s / 1e9
-    # executed bf16 MFMA flops: every fp32 x bf16 product is three bf16
-    # products (hi, mid, lo terms), 2 flops each, for M = B (gamma + 1) rows
     M = B * G1
-    mfma_tflops = 6.0 * M * (per_launch_bytes / 2) / per_launch_s / 1e12
+    ceiling = read_ceiling(torch, sv, per_launch_bytes)
+    progress(f"read ceiling {ceiling['gbs']:.0f} GB/s at {per_launch_bytes / 1e6:.1f} MB")
 
     weight_bytes = wbytes / kp
     other = 4 * (B * G1 * wl.d + (B * gamma * wl.V if T > 0 else 0) + B * gamma)
@@ -292,17 +420,12 @@ def main():
         "hbm_gbs_whole_step": step_gbs,
         "hbm_frac_whole_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": weight_bytes + other,
-        "roofline": ({"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
-                     if wl.wdtype == "f32" or M <= MFMA_BOUND_ROWS else
-                     {"bound": "mfma", "achieved": mfma_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                      "unit": "TFLOP/s", "frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS,
-                      "traffic": traffic, "hbm_gbs": achieved}),
+        "roofline": roofline_of(wl, M, per_launch_bytes, per_launch_s, traffic, ceiling),
         "gemm": {"kernel": "weight-streaming GEMMs (MLP up/down, LM head)",
                  "bytes_per_launch": per_launch_bytes, "launches": launches,
                  "avg_launch_us": per_launch_s * 1e6, "hbm_gbs": achieved,
-                 "hbm_frac": achieved / HBM_PEAK_GBS, "mfma_tflops": mfma_tflops,
-                 "mfma_frac": mfma_tflops / MFMA_BF16_PEAK_TFLOPS},
+                 "hbm_frac": achieved / HBM_PEAK_GBS},
+        "read_ceiling": ceiling,
         "cpu_baseline": None,
     }
     if host is not None:

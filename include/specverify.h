@@ -174,6 +174,17 @@ spec_status spec_profile_enable(spec_weights_t w, int32_t on);
 spec_status spec_profile_read(spec_weights_t w, double* gemm_ms, int64_t* launches,
                               int64_t* weight_bytes);
 
+/* Streaming-read probe for benchmarks: one launch that reads `bytes` from
+ * the device buffer `src` with 16-byte non-temporal loads (the access the
+ * weight-streaming GEMMs make) and discards them, so that the time of a
+ * launch gives the read bandwidth this device reaches for that size.
+ *   src    device, 16-byte aligned, `bytes` readable (a multiple of 16)
+ *   sink   device uint32 the kernel may write (it does only when the folded
+ *          words hit a fixed key); owned by the caller
+ * Asynchronous on `stream`; SPEC_EINVAL for a null pointer, zero or
+ * unaligned size. */
+spec_status spec_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static text for a status code. */
 const char* spec_status_string(spec_status s);
 

@@ -22,7 +22,9 @@ SPEC_FLAG_KEEP_ROWMAJOR = 1
 EXPORTS = ["spec_weights_create", "spec_weights_destroy", "spec_workspace_size", "spec_verify",
            "spec_verify_debug", "spec_workspace_size_from_logits", "spec_verify_from_logits",
            "spec_status_string", "spec_default_mfma_min_rows", "spec_profile_enable",
-           "spec_profile_read"]
+           "spec_profile_read", "spec_stream_read"]
+# Every symbol include/specverify_diag.h declares.
+DIAG_EXPORTS = ["spec_diag_access_check"]
 
 
 class SpecError(RuntimeError):
@@ -75,6 +77,10 @@ def load():
     lib.spec_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
     lib.spec_profile_read.restype = i32
+    lib.spec_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.spec_stream_read.restype = i32
+    lib.spec_diag_access_check.argtypes = [i32] * 10 + [ctypes.c_char_p, sz, ctypes.POINTER(ctypes.c_int64)]
+    lib.spec_diag_access_check.restype = i32
     _lib = lib
     return lib
 
@@ -250,6 +256,24 @@ def verify_from_logits(logits, draft_tokens, q, temperature, top_p, seed, worksp
                                           workspace.numel(), _stream(stream)),
            "spec_verify_from_logits")
     return n_accepted, emitted
+
+
+def stream_read(src, sink, nbytes=None, stream=None):
+    """spec_stream_read over the first nbytes of the device tensor src."""
+    nbytes = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(load().spec_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
+           "spec_stream_read")
+
+
+def access_check(d, ffn, n_blocks, vocab, wdtype, B, gamma, mfma_min_rows=0, keep_rowmajor=False,
+                 shrink_bytes=0):
+    """spec_diag_access_check: (status, message, ranges checked); host only."""
+    buf = ctypes.create_string_buffer(512)
+    n = ctypes.c_int64()
+    st = load().spec_diag_access_check(int(d), int(ffn), int(n_blocks), int(vocab), int(wdtype),
+                                       int(mfma_min_rows), 1 if keep_rowmajor else 0, int(B),
+                                       int(gamma), int(shrink_bytes), buf, 512, ctypes.byref(n))
+    return st, buf.value.decode(), n.value
 
 
 def default_mfma_min_rows():

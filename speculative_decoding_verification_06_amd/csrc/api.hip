@@ -1,13 +1,16 @@
 // C ABI of the verification step: argument checks, workspace layout, weight
 // registration and the launch sequence (target pass, then the rule).
 
+#include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <new>
 #include <vector>
 
 #include "common.h"
 #include "internal.h"
 #include "specverify.h"
+#include "specverify_diag.h"
 
 using namespace sv;
 
@@ -328,6 +331,300 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
   return err == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
+// ---------------------------------------------------------------- access check
+// Host-side model of every global and LDS access the kernels of one pass
+// make, at the extremes of their index ranges (the block, wave, lane and
+// k-step that reach the lowest and highest element of each buffer), for the
+// launch plans verify_impl would choose.  The address formulas are the
+// kernels' own (xs_index is shared with them; the rest restate gemm.hip's
+// k_gemm_mfma, k_gemm_wide, k_epi_wide, k_gemm_fma, run_epilogue and
+// sample.hip's k_prep line for line).  Nothing is launched.
+struct AccessCheck {
+  char* msg = nullptr;
+  size_t msg_len = 0;
+  int64_t checks = 0;
+  bool ok = true;
+  void range(const char* what, const char* buf, int64_t lo, int64_t hi, int64_t cap) {
+    ++checks;
+    if (lo >= 0 && hi < cap) return;
+    if (ok && msg && msg_len)
+      snprintf(msg, msg_len, "%s: %s elements [%lld, %lld] outside [0, %lld)", what, buf,
+               (long long)lo, (long long)hi, (long long)cap);
+    ok = false;
+  }
+};
+
+// Buffer capacities of a pass, in the unit each kernel indexes them with.
+struct PassBufs {
+  int64_t h, xg, ss, act, logits, pst, pidx, qst, xsd, xsf, part, rms;
+};
+
+PassBufs pass_bufs(const spec_weights* w, const Layout& L, int B, int gamma, int shrink) {
+  PassBufs c;
+  const int64_t M = L.M;
+  c.h = c.xg = M * L.ldd;
+  c.ss = M * (L.ldd / kSub);
+  c.act = M * L.ldf;
+  c.logits = M * L.Vs;
+  c.pst = 2 * M * L.G;
+  c.pidx = M * L.G;
+  c.qst = 2 * (int64_t)B * gamma * L.G;
+  c.xsd = L.ksd ? (int64_t)xs_bytes(L.M, L.ksd) / 2 : 0;   // bf16 elements
+  c.xsf = L.ksf ? (int64_t)xs_bytes(L.M, L.ksf) / 2 : 0;
+  c.part = (int64_t)wide_part_bytes(w, L.M) / 4;
+  c.rms = M;
+  if (shrink > 0) {
+    // a planted inconsistency: every buffer `shrink` bytes short
+    for (int64_t* x : {&c.h, &c.xg, &c.ss, &c.act, &c.logits, &c.pst, &c.pidx, &c.qst, &c.part, &c.rms})
+      *x -= (shrink + 3) / 4;
+    c.xsd -= (shrink + 1) / 2;
+    c.xsf -= (shrink + 1) / 2;
+  }
+  return c;
+}
+
+// Split-activation stores of an epilogue or of k_prep: pass rows [row0,
+// row0 + rows), columns below cols and below 32 ks.  A chunk's kernels add
+// the chunk's first row tile to the buffer pointer and index with local
+// rows, which for the plain packing (16-row tiles, chunks on tile bounds)
+// is xs_index of the pass row.
+void check_xs_store(AccessCheck& C, const char* what, const char* buf, int64_t cap, int row0,
+                    int rows, int cols, int ks, bool stacked) {
+  const int ncol = std::min(cols, kKStep * ks);
+  if (rows <= 0 || ncol <= 0) return;
+  int64_t lo = INT64_MAX, hi = -1;
+  const int st = xs_term_step(stacked);
+  const int last = (ncol - 1) / kKStep;   // columns of the first and last k-step
+  for (int r = row0; r < row0 + rows; ++r)
+    for (int s = 0; s <= last; s += std::max(1, last))
+      for (int j = 0; j < kKStep; ++j) {
+        const int col = s * kKStep + j;
+        if (col >= ncol) break;
+        const int64_t i = (int64_t)xs_index(r, col, ks, stacked);
+        lo = std::min(lo, i);
+        hi = std::max(hi, i + 2 * st);
+      }
+  C.range(what, buf, lo, hi, cap);
+}
+
+// Epilogue accesses for rows [row0, row0 + rows) of the pass and 16-column
+// tiles [t0, t1) of the GEMM's output.
+struct EpiCheck {
+  int kind, N, Np, ldo, nt;                // nt: tiles of one statistics unit
+  bool to_xs, stacked;
+  int xs_ks;
+  const char* xs_name;
+  int64_t xs_cap;                          // next GEMM's split buffer (bf16 elements)
+  bool wide_rms;
+  int B, gamma, V, G, M_total;
+};
+
+void check_epilogue(AccessCheck& C, const char* what, const EpiCheck& e, const PassBufs& c,
+                    const Layout& L, int row0, int rows, int t0, int t1) {
+  if (rows <= 0 || t1 <= t0) return;
+  const int nlast = t1 * kSub - 1;         // highest column a live item touches
+  const int64_t r_lo = row0, r_hi = row0 + rows - 1;
+  const int ss_ld = L.ldd / kSub;
+  if (e.kind == EPI_UP) {
+    if (e.wide_rms) C.range(what, "rms", r_lo, r_hi, c.rms);
+    else C.range(what, "ss (sums of squares)", r_lo * ss_ld, r_hi * ss_ld + ss_ld - 1, c.ss);
+    if (!e.to_xs) C.range(what, "act", r_lo * e.ldo + t0 * kSub, r_hi * e.ldo + nlast, c.act);
+  } else if (e.kind == EPI_DOWN) {
+    C.range(what, "h", r_lo * e.ldo + t0 * kSub, r_hi * e.ldo + nlast, c.h);
+    if (!e.to_xs) C.range(what, "xg", r_lo * e.ldo + t0 * kSub, r_hi * e.ldo + nlast, c.xg);
+    C.range(what, "ss (sums of squares)", r_lo * ss_ld + t0, r_hi * ss_ld + t1 - 1, c.ss);
+  } else {
+    const int nv = std::min(nlast, e.N - 1);
+    C.range(what, "logits", r_lo * e.ldo + t0 * kSub, r_hi * e.ldo + nv, c.logits);
+    const int u0 = t0 / e.nt, u1 = (t1 - 1) / e.nt;
+    C.range(what, "pst", 2 * (r_lo * e.G + u0), 2 * (r_hi * e.G + u1) + 1, c.pst);
+    C.range(what, "pidx", r_lo * e.G + u0, r_hi * e.G + u1, c.pidx);
+    // draft rows among them: b * gamma + i for rows b (gamma + 1) + i, i < gamma
+    int64_t q_lo = INT64_MAX, q_hi = -1;
+    for (int64_t g = r_lo; g <= r_hi; ++g) {
+      const int64_t b = g / (e.gamma + 1), i = g - b * (e.gamma + 1);
+      if (i < e.gamma) { q_lo = std::min(q_lo, b * e.gamma + i); q_hi = std::max(q_hi, b * e.gamma + i); }
+    }
+    if (q_hi >= 0) C.range(what, "qst", 2 * (q_lo * e.G + u0), 2 * (q_hi * e.G + u1) + 1, c.qst);
+  }
+  if (e.to_xs) check_xs_store(C, what, e.xs_name, e.xs_cap, row0, rows, t1 * kSub, e.xs_ks, e.stacked);
+}
+
+void check_mfma(AccessCheck& C, const char* what, const GemmPlan& p, const Mat& W, int M,
+                const char* xs_name, int64_t xs_cap, int64_t xs_off_units, const EpiCheck& e,
+                const PassBufs& c, const Layout& L, int row0) {
+  const int KS = W.Kp / kKStep, NT = p.nt;
+  const int FPT = p.stack ? 1 : 3, RPT = p.stack ? kStackRows : 16, TERMS = p.stack ? 3 : 1;
+  const int MT = (M + RPT - 1) / RPT, MG = p.mg, KG = p.kg, nwaves = MG * KG;
+  const int64_t wcap = (int64_t)W.Kp * W.Np / 8;     // bf16x8 fragments
+  if ((int64_t)p.blocks * NT * kSub != W.Np) { C.range(what, "column blocks", 0, p.blocks * NT * kSub, W.Np + 1); }
+  for (int bx : {0, p.blocks - 1})
+    for (int wave = 0; wave < nwaves; ++wave) {
+      const int mg = wave % MG, kg = wave / MG, mt0 = mg * p.mtw;
+      if (!(mt0 < MT) || kg >= KS) continue;
+      const int n = (KS - kg + KG - 1) / KG, klast = kg + (n - 1) * KG;
+      const int64_t wg = (int64_t)bx * KS * NT * 64;
+      C.range(what, "weights", wg + (int64_t)kg * NT * 64, wg + 63 + (int64_t)klast * NT * 64 + (NT - 1) * 64, wcap);
+      for (int i = 0; i < p.mtw; ++i) {
+        const int mt = std::min(mt0 + i, MT - 1);
+        const int rows = std::min(RPT, M - mt * RPT);
+        for (int lane = 0; lane < 64; lane += 63) {
+          const int ar = lane & 15;
+          int al;
+          if (p.stack) {
+            const int pp = std::min(ar / kStackRows, 2);
+            al = (lane & 48) + pp * kStackRows + std::min(ar - pp * kStackRows, rows - 1);
+          } else {
+            al = (lane & 48) + std::min(ar, rows - 1);
+          }
+          const int64_t base = xs_off_units + (int64_t)mt * (KS + 1) * FPT * 64 + al;
+          C.range(what, xs_name, base + (int64_t)kg * FPT * 64, base + (int64_t)KS * FPT * 64 + (FPT - 1) * 64, xs_cap);
+        }
+      }
+    }
+  const int ldr = NT * kSub + 1;
+  const int64_t lds = (int64_t)p.lds / 4;
+  C.range(what, "LDS k-group tiles", 0, ((((int64_t)KG - 1) * M + M - 1) * TERMS + TERMS - 1) * ldr + NT * kSub - 1, lds);
+  if (p.stack) C.range(what, "LDS summed tile", 0, (int64_t)KG * M * TERMS * ldr + (int64_t)(M - 1) * ldr + NT * kSub - 1, lds);
+  check_epilogue(C, what, e, c, L, row0, M, 0, NT);
+  check_epilogue(C, what, e, c, L, row0, M, (p.blocks - 1) * NT, p.blocks * NT);
+}
+
+void check_wide(AccessCheck& C, const char* what, const WidePlan& p, const Mat& W, int M,
+                const char* xs_name, int64_t xs_cap, const EpiCheck& e, const PassBufs& c,
+                const Layout& L) {
+  const int KS = W.Kp / kKStep, MT = p.MT, tiles = W.Np / kSub;
+  const int threads = 64 * p.mg * p.cg;
+  const int cpt = (p.mtw * p.mg * 3 * 64 + threads - 1) / threads;
+  const int64_t nfrp = (int64_t)cpt * threads, nfr = (int64_t)MT * 192;
+  const int64_t wcap = (int64_t)W.Kp * W.Np / 8;
+  C.range(what, "LDS activation tiles", 0, 2 * nfrp - 1, (int64_t)p.lds / 16);
+  for (int by = 0; by < p.S; ++by) {
+    const int s0 = by * p.ks_slice, s1 = std::min(KS, s0 + p.ks_slice);
+    if (s1 <= s0) continue;
+    for (int tid = 0; tid < threads; tid += threads - 1)
+      for (int i = 0; i < cpt; ++i) {
+        const int64_t cc = std::min<int64_t>(tid + (int64_t)i * threads, nfr - 1);
+        const int64_t mt = cc / 192, rem = cc - mt * 192;
+        const int64_t base = mt * (KS + 1) * 192 + rem;
+        C.range(what, xs_name, base + (int64_t)s0 * 192, base + (int64_t)KS * 192, xs_cap);
+      }
+    for (int bx : {0, p.colblocks - 1})
+      for (int cg = 0; cg < p.cg; ++cg)
+        for (int t = 0; t < p.ntc; ++t) {
+          const int tile = bx * (p.ntc * p.cg) + cg * p.ntc + t;
+          const int tt = std::min(tile, tiles - 1);
+          const int b = tt / W.nt, tp = tt - b * W.nt;
+          const int64_t wp = ((int64_t)b * KS * W.nt + tp) * 64;
+          C.range(what, "weights", wp + (int64_t)s0 * W.nt * 64, wp + 63 + (int64_t)(s1 - 1) * W.nt * 64, wcap);
+        }
+  }
+  const bool fuse_lm = p.S == 1 && e.kind == EPI_LM;
+  if (fuse_lm) {
+    if (p.ntc == 2) {
+      const int64_t R = (int64_t)p.mg * p.mtw * 16;
+      C.range(what, "LDS half-unit statistics", 0, (int64_t)p.cg * R * 16 - 1, (int64_t)p.lds);
+    }
+    check_epilogue(C, what, e, c, L, 0, M, 0, 4);
+    check_epilogue(C, what, e, c, L, 0, M, tiles - 4, tiles);
+    return;
+  }
+  // partial sums P[slice][row][col], then k_epi_wide per (4 tiles, 16 rows)
+  const int64_t ss = (int64_t)M * W.Np;
+  C.range(what, "partial sums (write)", 0, (int64_t)(p.S - 1) * ss + (int64_t)(M - 1) * W.Np + (tiles - 1) * kSub + 15, c.part);
+  for (int by = 0; by * 16 < M; by += std::max(1, ((M + 15) / 16) - 1)) {
+    const int m0 = by * 16, mb = std::min(16, M - m0);
+    const int64_t c0 = tiles - 4;
+    C.range(what, "partial sums (read)", (int64_t)m0 * W.Np,
+            (int64_t)(m0 + mb - 1) * W.Np + c0 * kSub + 63 + (int64_t)(p.S - 1) * ss, c.part);
+    check_epilogue(C, what, e, c, L, m0, mb, 0, 4);
+    check_epilogue(C, what, e, c, L, m0, mb, tiles - 4, tiles);
+    if (by == (M + 15) / 16 - 1) break;
+  }
+}
+
+void check_fma(AccessCheck& C, const char* what, const GemmPlan& p, const Mat& W, int M, int ldx,
+               int64_t x_cap, const char* x_name, int64_t x_off, const EpiCheck& e,
+               const PassBufs& c, const Layout& L, int row0) {
+  const int Kp = W.Kp;
+  C.range(what, x_name, x_off, x_off + (int64_t)(M - 1) * ldx + Kp - 1, x_cap);
+  C.range(what, "weights (row-major)", 0, (int64_t)(p.blocks - 1) * kGroupCols + 63 + (int64_t)(Kp - 1) * W.Np,
+          (int64_t)Kp * W.Np);
+  C.range(what, "LDS", 0, (int64_t)M * (kGroupCols + 1) + 32 * (kGroupCols + 1) - 1, (int64_t)p.lds / 4);
+  check_epilogue(C, what, e, c, L, row0, M, 0, 4);
+  check_epilogue(C, what, e, c, L, row0, M, (p.blocks - 1) * 4, p.blocks * 4);
+}
+
+spec_status access_check_pass(const spec_weights* w, int B, int gamma, int shrink, AccessCheck& C) {
+  const Layout L = make_layout(w, B, gamma);
+  const PassBufs c = pass_bufs(w, L, B, gamma, shrink);
+  const int M = L.M, path = gemm_path(w, M);
+  const bool stack = path == PATH_MFMA && xs_stacked(M);
+  const bool wide = path == PATH_MFMA && wide_rows(M);
+  // k_prep
+  {
+    const char* what = "k_prep";
+    C.range(what, "h", 0, (int64_t)(M - 1) * L.ldd + L.ldd - 1, c.h);
+    C.range(what, "ss (sums of squares)", 0, (int64_t)(M - 1) * (L.ldd / kSub) + L.ldd / kSub - 1, c.ss);
+    if (path == PATH_MFMA) {
+      check_xs_store(C, what, "xs (d-wide)", c.xsd, 0, M, L.ldd, L.ksd, stack);
+      const int rpt = stack ? kStackRows : 16, fpt = stack ? 1 : 3;
+      const int mtn = (M + rpt - 1) / rpt;
+      for (int pass = 0; pass < 2; ++pass) {
+        const int ks = pass ? L.ksf : L.ksd;
+        const int64_t cap = pass ? c.xsf : c.xsd;
+        if (pass && !w->n_blocks) break;
+        C.range(what, pass ? "xs zero step (ffn-wide)" : "xs zero step (d-wide)",
+                ((int64_t)0 * (ks + 1) + ks) * fpt * 512,
+                ((int64_t)(mtn - 1) * (ks + 1) + ks) * fpt * 512 + ((fpt - 1) * 64 + 63) * 8 + 7, cap);
+      }
+    }
+  }
+  const int chunk = max_rows(path);
+  auto gemm = [&](const char* what, const Mat& W, int kind, bool in_ffn) {
+    EpiCheck e;
+    e.kind = kind;
+    e.N = W.N; e.Np = W.Np;
+    e.ldo = kind == EPI_UP ? L.ldf : (kind == EPI_DOWN ? L.ldd : L.Vs);
+    e.stacked = stack;
+    e.to_xs = path == PATH_MFMA && kind != EPI_LM;
+    e.xs_ks = kind == EPI_UP ? L.ksf : L.ksd;
+    e.xs_name = kind == EPI_UP ? "xs (ffn-wide, next input)" : "xs (d-wide, next input)";
+    e.xs_cap = kind == EPI_UP ? c.xsf : c.xsd;
+    e.wide_rms = wide && kind == EPI_UP;
+    e.B = B; e.gamma = gamma; e.V = w->V; e.G = L.G; e.M_total = M;
+    const char* xs_name = in_ffn ? "xs (ffn-wide)" : "xs (d-wide)";
+    const int64_t xs_cap = in_ffn ? c.xsf : c.xsd;
+    for (int m0 = 0; m0 < M; m0 += chunk) {
+      const int Mc = std::min(chunk, M - m0);
+      const int64_t xs_off = (int64_t)(m0 / 16) * (W.Kp / kKStep + 1) * 3 * 64;   // fragments
+      if (path != PATH_MFMA) {
+        const int ldx = in_ffn ? L.ldf : L.ldd;
+        const int64_t x_cap = in_ffn ? c.act : (kind == EPI_LM ? c.h : c.xg);
+        e.nt = 4;
+        check_fma(C, what, plan_gemm(path, Mc, W, false), W, Mc, ldx, x_cap,
+                  in_ffn ? "act" : (kind == EPI_LM ? "h" : "xg"), (int64_t)m0 * ldx, e, c, L, m0);
+      } else if (wide) {
+        e.nt = kGroupCols / kSub;
+        check_wide(C, what, plan_wide(Mc, W), W, Mc, xs_name, xs_cap / 8, e, c, L);
+      } else {
+        const GemmPlan p = plan_gemm(path, Mc, W, stack);
+        e.nt = p.nt;
+        check_mfma(C, what, p, W, Mc, xs_name, xs_cap / 8, xs_off, e, c, L, m0);
+      }
+    }
+  };
+  char name[64];
+  for (int l = 0; l < w->n_blocks; ++l) {
+    snprintf(name, sizeof name, "up projection, block %d", l);
+    gemm(name, w->up[l], EPI_UP, false);
+    snprintf(name, sizeof name, "down projection, block %d", l);
+    gemm(name, w->down[l], EPI_DOWN, true);
+  }
+  gemm("LM head", w->lm, EPI_LM, false);
+  return C.ok ? SPEC_OK : SPEC_EINVAL;
+}
+
 }  // namespace
 
 extern "C" {
@@ -449,6 +746,49 @@ spec_status spec_verify_debug(spec_weights_t w, int32_t B, int32_t gamma, const 
                               float* logits_out, float* p_out, float* q_out) {
   return verify_impl(w, B, gamma, hidden, draft_tokens, q, temperature, top_p, seed, n_accepted,
                      emitted, workspace, workspace_bytes, stream, logits_out, p_out, q_out);
+}
+
+spec_status spec_diag_access_check(int32_t d, int32_t ffn, int32_t n_blocks, int32_t vocab,
+                                   int32_t wdtype, int32_t mfma_min_rows, int32_t keep_rowmajor,
+                                   int32_t B, int32_t gamma, int32_t shrink_bytes, char* msg,
+                                   size_t msg_len, int64_t* checks) {
+  if (msg && msg_len) msg[0] = 0;
+  if (shrink_bytes < 0) return SPEC_EINVAL;
+  if (d < 1 || ffn < 1 || n_blocks < 0 || vocab < 1 || B < 1 || gamma < 0 || gamma > kMaxGamma)
+    return SPEC_EINVAL;
+  if (wdtype != SPEC_F32 && wdtype != SPEC_BF16) return SPEC_EDTYPE;
+  // shapes only: no device memory is touched
+  spec_weights w;
+  w.d = d; w.ffn = ffn; w.n_blocks = n_blocks; w.V = vocab; w.wdtype = wdtype;
+  w.mfma_min_rows = mfma_min_rows > 0 ? mfma_min_rows : kDefaultMfmaMinRows;
+  auto shape = [&](Mat& m, int K, int N) {
+    m.K = K; m.N = N; m.Kp = roundup(K, kKStep); m.Np = roundup(N, kGroupCols);
+    if (wdtype == SPEC_BF16) m.nt = mfma_block_tiles(m.Np);
+    if (wdtype == SPEC_BF16 && (keep_rowmajor || w.mfma_min_rows > 1))
+      m.rowmajor = reinterpret_cast<void*>(uintptr_t{256});   // marks a row-major copy; never read
+  };
+  w.up.resize(n_blocks);
+  w.down.resize(n_blocks);
+  for (int l = 0; l < n_blocks; ++l) { shape(w.up[l], d, ffn); shape(w.down[l], ffn, d); }
+  shape(w.lm, d, vocab);
+  AccessCheck C;
+  C.msg = msg; C.msg_len = msg_len;
+  const spec_status s = access_check_pass(&w, B, gamma, shrink_bytes, C);
+  for (auto& m : w.up) m.rowmajor = nullptr;
+  for (auto& m : w.down) m.rowmajor = nullptr;
+  w.lm.rowmajor = nullptr;
+  if (checks) *checks = C.checks;
+  return s;
+}
+
+spec_status spec_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
+    return SPEC_EINVAL;
+  (void)hipGetLastError();
+  return launch_stream_read(src, bytes, 0x9E3779B9u, sink, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? SPEC_OK
+             : SPEC_EHIP;
 }
 
 size_t spec_workspace_size_from_logits(int32_t B, int32_t gamma, int32_t vocab) {

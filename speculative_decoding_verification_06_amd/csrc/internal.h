@@ -176,6 +176,11 @@ hipError_t launch_copy_rowmajor(const void* src, int src_dtype, int K, int N, vo
                                 int dst_dtype, int Kp, int Np, hipStream_t st);
 hipError_t launch_vec_to_f32(const void* src, int src_dtype, int n, float* dst, hipStream_t st);
 
+// Streaming read of `bytes` (a multiple of 16, 16-byte aligned) from src
+// (probe.hip).
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t key, uint32_t* sink,
+                              hipStream_t st);
+
 constexpr int kResampleChunk = 1024;   // elements per resample chunk
 
 }  // namespace sv
