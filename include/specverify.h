@@ -64,7 +64,9 @@ typedef enum {
   SPEC_EDTYPE = -2,      /* unsupported weight dtype                       */
   SPEC_EWORKSPACE = -3,  /* workspace missing or smaller than required     */
   SPEC_EHIP = -4,        /* a HIP runtime call failed                      */
-  SPEC_ENOMEM = -5       /* device allocation failed (create only)         */
+  SPEC_ENOMEM = -5,      /* device allocation failed (create only)         */
+  SPEC_ESCRATCH = -6     /* pass larger than SPEC_NOALLOC_SCRATCH_BYTES
+                            (spec_verify_noalloc only)                     */
 } spec_status;
 
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
@@ -133,6 +135,30 @@ spec_status spec_verify(spec_weights_t w, int32_t B, int32_t gamma,
                         const float* q, float temperature, float top_p,
                         uint64_t seed, int32_t* n_accepted, int32_t* emitted,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Scratch bytes the allocation-free entry point holds per GPU. */
+#define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* spec_verify for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: the pass runs in a static per-GPU scratch array of
+ * SPEC_NOALLOC_SCRATCH_BYTES (128 MiB; reserved in each GPU's memory the
+ * library runs on until the process ends), whose address the library looks
+ * up once per device in spec_weights_create.  The call allocates nothing
+ * (no hipMalloc, hipFree, event creation or allocating library routine);
+ * timing (spec_profile_enable) does not apply to it.  The caller still
+ * passes inputs and outputs, as for spec_verify.  Every call on a GPU
+ * shares that GPU's scratch and leaves its contents behind (the kernels
+ * read no workspace content they have not written in the same call), so
+ * calls that overlap in time on one GPU, on any streams, race: serialise
+ * them.  Returns SPEC_ESCRATCH, before any launch, when
+ * spec_workspace_size(w, B, gamma) exceeds the scratch; other arguments and
+ * errors as for spec_verify. */
+spec_status spec_verify_noalloc(spec_weights_t w, int32_t B, int32_t gamma,
+                                const float* hidden, const int32_t* draft_tokens,
+                                const float* q, float temperature, float top_p,
+                                uint64_t seed, int32_t* n_accepted, int32_t* emitted,
+                                void* stream);
 
 /* spec_verify plus optional dumps for parity checks (not a timed path).
  *   logits_out  device fp32 [B][gamma+1][vocab] or NULL: target logits

@@ -14,7 +14,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
-SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_ENOMEM = 0, -1, -2, -3, -4, -5
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_ENOMEM, SPEC_ESCRATCH = \
+    0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 128 << 20
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_FLAG_KEEP_ROWMAJOR = 1
 
@@ -22,7 +24,7 @@ SPEC_FLAG_KEEP_ROWMAJOR = 1
 EXPORTS = ["spec_weights_create", "spec_weights_destroy", "spec_workspace_size", "spec_verify",
            "spec_verify_debug", "spec_workspace_size_from_logits", "spec_verify_from_logits",
            "spec_status_string", "spec_default_mfma_min_rows", "spec_profile_enable",
-           "spec_profile_read", "spec_stream_read"]
+           "spec_profile_read", "spec_stream_read", "spec_verify_noalloc"]
 # Every symbol include/specverify_diag.h declares.
 DIAG_EXPORTS = ["spec_diag_access_check"]
 
@@ -62,6 +64,8 @@ def load():
     common = [vp, i32, i32, vp, vp, vp, f32, f32, u64, vp, vp, vp, sz, vp]
     lib.spec_verify.argtypes = common
     lib.spec_verify.restype = i32
+    lib.spec_verify_noalloc.argtypes = [vp, i32, i32, vp, vp, vp, f32, f32, u64, vp, vp, vp]
+    lib.spec_verify_noalloc.restype = i32
     lib.spec_verify_debug.argtypes = common + [vp, vp, vp]
     lib.spec_verify_debug.restype = i32
     lib.spec_workspace_size_from_logits.argtypes = [i32, i32, i32]
@@ -208,6 +212,27 @@ def verify(w, hidden, draft_tokens, q, temperature, top_p, seed, workspace=None,
                               float(temperature), float(top_p), int(seed), _ptr(n_accepted),
                               _ptr(emitted), _ptr(workspace), workspace.numel(), _stream(stream)),
            "spec_verify")
+    return n_accepted, emitted
+
+
+def verify_noalloc(w, hidden, draft_tokens, q, temperature, top_p, seed, n_accepted, emitted,
+                   stream=None):
+    """spec_verify_noalloc: the pass in the library's static scratch, into
+    caller-allocated outputs n_accepted [B] and emitted [B][gamma+1]."""
+    B, G1, d = hidden.shape
+    gamma = G1 - 1
+    _dev(hidden, torch.float32, "hidden")
+    _dev(draft_tokens, torch.int32, "draft_tokens")
+    if q is not None:
+        _dev(q, torch.float32, "q")
+    _dev(n_accepted, torch.int32, "n_accepted")
+    _dev(emitted, torch.int32, "emitted")
+    if tuple(n_accepted.shape) != (B,) or tuple(emitted.shape) != (B, G1):
+        raise ValueError("outputs must be n_accepted [B] and emitted [B][gamma+1]")
+    _check(load().spec_verify_noalloc(w.handle, B, gamma, _ptr(hidden), _ptr(draft_tokens), _ptr(q),
+                                      float(temperature), float(top_p), int(seed), _ptr(n_accepted),
+                                      _ptr(emitted), _stream(stream)),
+           "spec_verify_noalloc")
     return n_accepted, emitted
 
 

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -14,12 +15,40 @@
 
 using namespace sv;
 
+// Scratch of the allocation-free entry point: one array per GPU, holding
+// the pass's workspace for callers that cannot allocate.  In host code the
+// name `scratch` is a host-side stand-in, never a device address: its device
+// address is taken once per device with hipGetSymbolAddress and kept in
+// g_scratch; kernels receive that pointer like any workspace.
+constexpr size_t kScratchBytes = SPEC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of this device's scratch (the current device must be
+// `dev`); nullptr when the lookup fails.
+void* scratch_address(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+
 struct spec_weights {
   int d = 0, ffn = 0, n_blocks = 0, V = 0, wdtype = 0;
   float eps = 0.f;
   uint32_t flags = 0;
   int mfma_min_rows = 1;
   int device = 0;
+  void* scratch = nullptr;          // this device's scratch (spec_verify_noalloc)
   std::vector<Mat> up, down;
   Mat lm;
   std::vector<float*> gain;
@@ -188,8 +217,8 @@ hipError_t prof_events(spec_weights* w, size_t idx, hipEvent_t& e0, hipEvent_t& 
 // start on 16-row tiles (the chunk sizes are multiples of 16), so a
 // chunk's split fragments begin at tile m0 / 16.  With timing on, every
 // launch carries a pair of events and its algorithmic weight bytes.
-hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, const uint16_t* XS,
-                    int ldx, int M, EpiArgs e, float* part, hipStream_t st) {
+hipError_t run_gemm(spec_weights* w, bool prof, int path, const Mat& W, const float* X,
+                    const uint16_t* XS, int ldx, int M, EpiArgs e, float* part, hipStream_t st) {
   const int chunk = max_rows(path);
   // the packing and the kernel follow the whole pass's row count (stacked
   // and wide passes are one chunk)
@@ -217,7 +246,7 @@ hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, con
     a.e.xs_stack = stack;
     a.e.row0 = m0;
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (w->prof) {
+    if (prof) {
       const hipError_t err = prof_events(w, w->ev_used, e0, e1);
       if (err != hipSuccess) return err;
     }
@@ -233,7 +262,7 @@ hipError_t run_gemm(spec_weights* w, int path, const Mat& W, const float* X, con
       err = launch_gemm(plan_gemm(path, a.M, W, stack), a, st, e0, e1);
     }
     if (err != hipSuccess) return err;
-    if (w->prof) {
+    if (prof) {
       w->ev_bytes.resize(w->ev_used + 1);
       w->ev_bytes[w->ev_used] = (int64_t)W.K * W.N * (w->wdtype == SPEC_F32 ? 4 : 2);
       ++w->ev_used;
@@ -252,7 +281,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
                         const int32_t* draft, const float* q, float T, float top_p,
                         uint64_t seed, int32_t* n_acc, int32_t* emitted, void* ws,
                         size_t ws_bytes, void* stream, float* logits_out, float* p_out,
-                        float* q_out) {
+                        float* q_out, bool noalloc = false) {
   if (!w || B < 1 || gamma < 0 || gamma > kMaxGamma || !hidden || !n_acc || !emitted)
     return SPEC_EINVAL;
   if (gamma > 0 && !draft) return SPEC_EINVAL;
@@ -260,10 +289,18 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
   if (T > 0.f && gamma > 0 && !q) return SPEC_EINVAL;
   if ((size_t)B * (gamma + 1) > (size_t)INT32_MAX / 2) return SPEC_EINVAL;
   const Layout L = make_layout(w, B, gamma);
+  if (noalloc) {
+    if (L.total > kScratchBytes) return SPEC_ESCRATCH;
+    ws = w->scratch;
+    ws_bytes = kScratchBytes;
+    if (!ws) return SPEC_EHIP;
+  }
   if (!ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(ws) & 255)) return SPEC_EWORKSPACE;
   if (spec_status s = check_device(w); s != SPEC_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  // timing events are created on demand: never on the allocation-free path
+  const bool prof = w->prof && !noalloc;
 
   const int M = L.M, path = gemm_path(w, M);
   float* h = at<float>(ws, L.h);
@@ -290,7 +327,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
     up.inv_d = 1.0f / (float)w->d; up.eps = w->eps;
     up.rms = rms;
     up.xs = xsf; up.xs_ks = L.ksf;
-    err = run_gemm(w, path, w->up[l], xg, xsd, L.ldd, M, up, part, st);
+    err = run_gemm(w, prof, path, w->up[l], xg, xsd, L.ldd, M, up, part, st);
     if (err != hipSuccess) break;
     EpiArgs dn;
     dn.kind = EPI_DOWN;
@@ -298,7 +335,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
     dn.xg = xg; dn.gain_next = l + 1 < w->n_blocks ? w->gain[l + 1] : nullptr;
     dn.ss_out = ss; dn.ss_ld = ss_ld;
     dn.xs = xsd; dn.xs_ks = L.ksd;
-    err = run_gemm(w, path, w->down[l], act, xsf, L.ldf, M, dn, part, st);
+    err = run_gemm(w, prof, path, w->down[l], act, xsf, L.ldf, M, dn, part, st);
   }
   if (err == hipSuccess) {
     EpiArgs lm;
@@ -308,7 +345,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
     lm.pst = at<float>(ws, L.pst); lm.pidx = at<int>(ws, L.pidx); lm.qst = at<float>(ws, L.qst);
     lm.q = q; lm.G = L.G; lm.G1 = gamma + 1; lm.gamma = gamma; lm.V = w->V;
     lm.tmode = tmode; lm.invT = tmode ? 1.0f / T : 1.0f;
-    err = run_gemm(w, path, w->lm, h, xsd, L.ldd, M, lm, part, st);
+    err = run_gemm(w, prof, path, w->lm, h, xsd, L.ldd, M, lm, part, st);
   }
   SampleArgs sa;
   if (err == hipSuccess) {
@@ -637,6 +674,7 @@ const char* spec_status_string(spec_status s) {
     case SPEC_EWORKSPACE: return "workspace missing, misaligned or too small";
     case SPEC_EHIP: return "HIP runtime error";
     case SPEC_ENOMEM: return "device allocation failed";
+    case SPEC_ESCRATCH: return "pass needs more workspace than the allocation-free scratch holds";
   }
   return "unknown status";
 }
@@ -659,6 +697,9 @@ spec_status spec_weights_create(const spec_weights_desc* desc, void* stream, spe
   w->wdtype = desc->wdtype; w->eps = desc->rms_eps; w->flags = desc->flags;
   w->mfma_min_rows = desc->mfma_min_rows > 0 ? desc->mfma_min_rows : kDefaultMfmaMinRows;
   if (hipGetDevice(&w->device) != hipSuccess) { delete w; return SPEC_EHIP; }
+  // set-up of the allocation-free entry point: this device's scratch address
+  w->scratch = scratch_address(w->device);
+  if (!w->scratch) { delete w; return SPEC_EHIP; }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool keep_rm = w->wdtype == SPEC_BF16 &&
                        ((desc->flags & SPEC_FLAG_KEEP_ROWMAJOR) || w->mfma_min_rows > 1);
@@ -737,6 +778,14 @@ spec_status spec_verify(spec_weights_t w, int32_t B, int32_t gamma, const float*
                         void* workspace, size_t workspace_bytes, void* stream) {
   return verify_impl(w, B, gamma, hidden, draft_tokens, q, temperature, top_p, seed, n_accepted,
                      emitted, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+spec_status spec_verify_noalloc(spec_weights_t w, int32_t B, int32_t gamma, const float* hidden,
+                                const int32_t* draft_tokens, const float* q, float temperature,
+                                float top_p, uint64_t seed, int32_t* n_accepted, int32_t* emitted,
+                                void* stream) {
+  return verify_impl(w, B, gamma, hidden, draft_tokens, q, temperature, top_p, seed, n_accepted,
+                     emitted, nullptr, 0, stream, nullptr, nullptr, nullptr, true);
 }
 
 spec_status spec_verify_debug(spec_weights_t w, int32_t B, int32_t gamma, const float* hidden,
