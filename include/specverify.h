@@ -172,6 +172,39 @@ spec_status spec_verify_debug(spec_weights_t w, int32_t B, int32_t gamma,
                               size_t workspace_bytes, void* stream,
                               float* logits_out, float* p_out, float* q_out);
 
+/* Greedy verification of a draft tree ("Speculative Decoding: Speeding
+ * Sequential Generation", aicomputerinstitute.com, Tree-Based Drafting,
+ * Constructing the Tree Attention Mask in Code, Expected Tokens per
+ * Verification Round: Chain vs. Tree).  One pass scores the root row and
+ * one row per node; node j passes when its token equals the argmax of its
+ * parent's row (temperature 0).  From the root, the walk descends to the
+ * lowest-index passing child until a row has none, and emits that row's
+ * argmax (correction, or bonus at a leaf).  The synthetic target has no
+ * attention, so node rows are scored independently: a caller whose model
+ * attends builds the node rows with the tree mask (node i sees itself and
+ * its ancestors) and position id = depth before this call.
+ *   hidden      device fp32 [B][n_nodes+1][d]: row 0 the root (the last
+ *               committed position), row 1 + j node j
+ *   parent      device int32 [B][n_nodes]: -1 for a child of the root, else
+ *               a node index below j (parents precede children)
+ *   tokens      device int32 [B][n_nodes]: the draft token of each node
+ *   n_accepted  device int32 [B] out: depth of the accepted path, or -1
+ *               when a parent or token of the sequence is out of range
+ *   emitted     device int32 [B][n_nodes+1] out: the accepted path's tokens,
+ *               then the argmax of its last row, then -1 padding
+ *   path        device int32 [B][n_nodes] out or NULL: node indices of the
+ *               accepted path, -1 padding (what a KV cache commits)
+ *   workspace   spec_workspace_size(w, B, n_nodes) bytes (a pass of
+ *               n_nodes + 1 rows per sequence), 256-byte aligned
+ *   logits_out  device fp32 [B][n_nodes+1][vocab] or NULL (parity checks)
+ * Ties: the lowest token id for an argmax, the lowest node index among
+ * children with equal tokens. */
+spec_status spec_verify_tree_greedy(spec_weights_t w, int32_t B, int32_t n_nodes,
+                                    const float* hidden, const int32_t* parent,
+                                    const int32_t* tokens, int32_t* n_accepted,
+                                    int32_t* emitted, int32_t* path, void* workspace,
+                                    size_t workspace_bytes, void* stream, float* logits_out);
+
 /* Workspace bytes for spec_verify_from_logits, or 0 on invalid arguments. */
 size_t spec_workspace_size_from_logits(int32_t B, int32_t gamma, int32_t vocab);
 

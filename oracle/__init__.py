@@ -34,6 +34,8 @@ Modules:
   rule    -- temperature, top-p, the ratio test, residual resampling, bonus,
              greedy branch, and the margin, slack and token band of every decision
   verify  -- spec_verify / spec_verify_from_logits over a batch
+  tree    -- greedy verification of a draft tree: ancestor mask, depths,
+             the walk down passing children
 
 Parity status of each part (what pins it) is listed in the module docstrings.
 """
@@ -44,6 +46,7 @@ from .rule import (warp_logits, warp_probs, nucleus_mask, accept_test,
                    inverse_cdf, cdf_band, verify_row, verify_row_greedy, MARGIN, TopP,
                    Decision)
 from .verify import spec_verify, spec_verify_from_logits, VerifyResult
+from . import tree
 
 __all__ = [
     "philox4x64_10", "row_uniforms", "PURPOSE_VERIFY", "PURPOSE_DRAFT",

@@ -24,7 +24,8 @@ SPEC_FLAG_KEEP_ROWMAJOR = 1
 EXPORTS = ["spec_weights_create", "spec_weights_destroy", "spec_workspace_size", "spec_verify",
            "spec_verify_debug", "spec_workspace_size_from_logits", "spec_verify_from_logits",
            "spec_status_string", "spec_default_mfma_min_rows", "spec_profile_enable",
-           "spec_profile_read", "spec_stream_read", "spec_verify_noalloc"]
+           "spec_profile_read", "spec_stream_read", "spec_verify_noalloc",
+           "spec_verify_tree_greedy"]
 # Every symbol include/specverify_diag.h declares.
 DIAG_EXPORTS = ["spec_diag_access_check"]
 
@@ -66,6 +67,8 @@ def load():
     lib.spec_verify.restype = i32
     lib.spec_verify_noalloc.argtypes = [vp, i32, i32, vp, vp, vp, f32, f32, u64, vp, vp, vp]
     lib.spec_verify_noalloc.restype = i32
+    lib.spec_verify_tree_greedy.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.spec_verify_tree_greedy.restype = i32
     lib.spec_verify_debug.argtypes = common + [vp, vp, vp]
     lib.spec_verify_debug.restype = i32
     lib.spec_workspace_size_from_logits.argtypes = [i32, i32, i32]
@@ -256,6 +259,28 @@ def verify_debug(w, hidden, draft_tokens, q, temperature, top_p, seed, want_prob
                                     _stream(stream), _ptr(logits), _ptr(p_out), _ptr(q_out)),
            "spec_verify_debug")
     return n_accepted, emitted, logits, p_out, q_out
+
+
+def verify_tree_greedy(w, hidden, parent, tokens, want_logits=False, workspace=None, stream=None):
+    """spec_verify_tree_greedy; hidden [B][n+1][d] (row 0 the root), parent
+    and tokens [B][n] int32.  Returns (n_accepted [B], emitted [B][n+1],
+    path [B][n], logits [B][n+1][V] or None)."""
+    B, G1, d = hidden.shape
+    n = G1 - 1
+    _dev(hidden, torch.float32, "hidden")
+    _dev(parent, torch.int32, "parent")
+    _dev(tokens, torch.int32, "tokens")
+    n_acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    emitted = torch.empty((B, G1), dtype=torch.int32, device="cuda")
+    path = torch.empty((B, max(n, 1)), dtype=torch.int32, device="cuda")[:, :n]
+    logits = torch.empty((B, G1, w.V), dtype=torch.float32, device="cuda") if want_logits else None
+    if workspace is None:
+        workspace = w.workspace(B, n)
+    _check(load().spec_verify_tree_greedy(w.handle, B, n, _ptr(hidden), _ptr(parent), _ptr(tokens),
+                                          _ptr(n_acc), _ptr(emitted), _ptr(path), _ptr(workspace),
+                                          workspace.numel(), _stream(stream), _ptr(logits)),
+           "spec_verify_tree_greedy")
+    return n_acc, emitted, path, logits
 
 
 def workspace_size_from_logits(B, gamma, V):

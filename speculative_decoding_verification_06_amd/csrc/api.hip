@@ -277,14 +277,22 @@ spec_status check_device(const spec_weights* w) {
   return dev == w->device ? SPEC_OK : SPEC_EINVAL;
 }
 
+// Draft tree of a greedy tree verification (spec_verify_tree_greedy).
+struct TreeArgs {
+  const int32_t* parent = nullptr;   // [B][n]
+  const int32_t* tokens = nullptr;   // [B][n]
+  int32_t* path = nullptr;           // [B][n] or null
+};
+
 spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float* hidden,
                         const int32_t* draft, const float* q, float T, float top_p,
                         uint64_t seed, int32_t* n_acc, int32_t* emitted, void* ws,
                         size_t ws_bytes, void* stream, float* logits_out, float* p_out,
-                        float* q_out, bool noalloc = false) {
+                        float* q_out, bool noalloc = false, const TreeArgs* tree = nullptr) {
   if (!w || B < 1 || gamma < 0 || gamma > kMaxGamma || !hidden || !n_acc || !emitted)
     return SPEC_EINVAL;
-  if (gamma > 0 && !draft) return SPEC_EINVAL;
+  if (tree && gamma > 0 && (!tree->parent || !tree->tokens)) return SPEC_EINVAL;
+  if (!tree && gamma > 0 && !draft) return SPEC_EINVAL;
   if (bad_scalars(T, top_p)) return SPEC_EINVAL;
   if (T > 0.f && gamma > 0 && !q) return SPEC_EINVAL;
   if ((size_t)B * (gamma + 1) > (size_t)INT32_MAX / 2) return SPEC_EINVAL;
@@ -356,7 +364,8 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
     sa.pst = at<float>(ws, L.pst); sa.pidx = at<int>(ws, L.pidx); sa.qst = at<float>(ws, L.qst);
     sa.rowinfo = at<float>(ws, L.rowinfo); sa.dec = at<int>(ws, L.dec);
     sa.csum = at<double>(ws, L.csum); sa.nch = L.nch;
-    err = launch_sampling(sa, st);
+    err = tree ? launch_tree_walk(sa, tree->parent, tree->tokens, tree->path, st)
+               : launch_sampling(sa, st);
   }
   if (err == hipSuccess && (p_out || q_out)) {
     sa.p_out = p_out; sa.q_out = q_out;
@@ -786,6 +795,17 @@ spec_status spec_verify_noalloc(spec_weights_t w, int32_t B, int32_t gamma, cons
                                 void* stream) {
   return verify_impl(w, B, gamma, hidden, draft_tokens, q, temperature, top_p, seed, n_accepted,
                      emitted, nullptr, 0, stream, nullptr, nullptr, nullptr, true);
+}
+
+spec_status spec_verify_tree_greedy(spec_weights_t w, int32_t B, int32_t n_nodes,
+                                    const float* hidden, const int32_t* parent,
+                                    const int32_t* tokens, int32_t* n_accepted, int32_t* emitted,
+                                    int32_t* path, void* workspace, size_t workspace_bytes,
+                                    void* stream, float* logits_out) {
+  TreeArgs t;
+  t.parent = parent; t.tokens = tokens; t.path = path;
+  return verify_impl(w, B, n_nodes, hidden, nullptr, nullptr, 0.0f, 1.0f, 0, n_accepted, emitted,
+                     workspace, workspace_bytes, stream, logits_out, nullptr, nullptr, false, &t);
 }
 
 spec_status spec_verify_debug(spec_weights_t w, int32_t B, int32_t gamma, const float* hidden,

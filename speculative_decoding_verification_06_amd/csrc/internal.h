@@ -168,6 +168,10 @@ hipError_t launch_prep(float* h, float* xg, float* ss, int ss_ld, const float* h
 hipError_t launch_tile_stats(const SampleArgs& a, hipStream_t st);
 hipError_t launch_sampling(const SampleArgs& a, hipStream_t st);
 hipError_t launch_dump_probs(const SampleArgs& a, hipStream_t st);
+// Greedy tree walk after a T = 0 pass over B (n + 1) rows (a.gamma = n
+// nodes): per-row argmax, then the walk per sequence.
+hipError_t launch_tree_walk(const SampleArgs& a, const int* parent, const int* tokens, int* path,
+                            hipStream_t st);
 
 // Weight conversion launchers (pack.hip).
 hipError_t launch_pack_mfma(const void* src, int src_dtype, int K, int N, void* dst, int Kp,

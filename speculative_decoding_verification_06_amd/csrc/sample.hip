@@ -1020,6 +1020,73 @@ hipError_t launch_dump_probs(const SampleArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- tree walk
+// Greedy verification of a draft tree ("Speculative Decoding: Speeding
+// Sequential Generation", aicomputerinstitute.com, Tree-Based Drafting and
+// Expected Tokens per Verification Round: Chain vs. Tree): one wave per
+// sequence.  The pass scored the root row (local row 0) and one row per node
+// (row 1 + j), whose argmax k_rowstats left in the row table.  From the
+// root, the walk descends to the lowest-index child whose token equals the
+// argmax of the current row, and stops at the first row none of whose
+// children does, emitting that row's argmax.  Parents precede children
+// (parent[j] < j), so every step moves to a higher node index and the walk
+// ends within n + 1 steps.  A sequence with a parent outside [-1, j) or a
+// token outside [0, V) gets n_accepted = -1 and all -1 outputs.
+__global__ __launch_bounds__(kWave) void k_tree_walk(SampleArgs a, const int* parent,
+                                                     const int* tokens, int* path) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int n = a.gamma, G1 = n + 1;
+  const int* par = parent + (size_t)b * n;
+  const int* tok = tokens + (size_t)b * n;
+  int* em = a.emitted + (size_t)b * G1;
+  int* pth = path ? path + (size_t)b * n : nullptr;
+  bool bad = false;
+  for (int j = lane; j < n; j += kWave) {
+    const int pj = par[j], tj = tok[j];
+    bad |= pj < -1 || pj >= j || tj < 0 || tj >= a.V;
+  }
+  if (__any(bad)) {
+    for (int i = lane; i < G1; i += kWave) em[i] = -1;
+    if (pth)
+      for (int i = lane; i < n; i += kWave) pth[i] = -1;
+    if (lane == 0) a.n_acc[b] = -1;
+    return;
+  }
+  const float* ri = a.rowinfo + (size_t)b * G1 * kRowInfo;
+  int cur = -1, depth = 0;
+  for (int step = 0; step <= n; ++step) {
+    const int am = __float_as_int(ri[(size_t)(cur + 1) * kRowInfo + RI_M]);
+    int next = INT_MAX;
+    for (int j0 = cur + 1; j0 < n; j0 += kWave) {   // children have higher indices
+      const int j = j0 + lane;
+      const bool hit = j < n && par[j] == cur && tok[j] == am;
+      const uint64_t m = __ballot(hit);
+      if (m) { next = j0 + __ffsll((unsigned long long)m) - 1; break; }
+    }
+    if (next == INT_MAX) {
+      if (lane == 0) em[depth] = am;
+      break;
+    }
+    if (lane == 0) {
+      em[depth] = am;
+      if (pth) pth[depth] = next;
+    }
+    ++depth;
+    cur = next;
+  }
+  for (int i = depth + 1 + lane; i < G1; i += kWave) em[i] = -1;
+  if (pth)
+    for (int i = depth + lane; i < n; i += kWave) pth[i] = -1;
+  if (lane == 0) a.n_acc[b] = depth;
+}
+
+hipError_t launch_tree_walk(const SampleArgs& a, const int* parent, const int* tokens, int* path,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_rowstats, dim3(a.M), dim3(kRowThreads), 0, st, a);
+  hipLaunchKernelGGL(k_tree_walk, dim3(a.B), dim3(kWave), 0, st, a, parent, tokens, path);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- sequencing
 hipError_t launch_sampling(const SampleArgs& a, hipStream_t st) {
   const int qrows = a.B * a.gamma;

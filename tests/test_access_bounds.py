@@ -80,6 +80,14 @@ def test_a_short_workspace_is_caught(wl):
     assert st == sv.SPEC_EINVAL and "outside" in msg
 
 
+def test_tree_test_shapes():
+    from test_gpu_tree import TREE_CASES
+    for name, B, n, kind, d, ffn, nb, V in TREE_CASES:
+        check(d, ffn, nb, V, BF16, B, n)
+    wl = synth.WORKLOADS["mid"]
+    check(wl.d, wl.ffn, wl.n_blocks, wl.V, BF16, 4, 14)
+
+
 def test_bad_arguments():
     assert sv.access_check(0, 1, 1, 1, F32, 1, 0)[0] == sv.SPEC_EINVAL
     assert sv.access_check(8, 8, 1, 8, 7, 1, 0)[0] == sv.SPEC_EDTYPE
