@@ -244,6 +244,66 @@ spec_status spec_profile_read(spec_weights_t w, double* gemm_ms, int64_t* launch
  * unaligned size. */
 spec_status spec_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/* ---- Host policy around the step ("Build a Speculative Decoding Engine
+ * to Cut LLM Latency by 3x", scalablesystem.dev, Dynamic Gamma Controller
+ * and Batch-Level Speculation). */
+
+/* Speculation-depth controller for n_seq sequences (host memory only, no
+ * GPU work).  Each sequence keeps the last 20 (accepted, rejected) counts,
+ * rejected = gamma used - accepted; its rolling acceptance rate is
+ * sum(accepted) / sum(accepted + rejected) (0.80 before any step).  From 5
+ * recorded steps on, each update sets its gamma to the value in
+ * [gamma_min, gamma_max] maximising
+ *     E(g) / (g * draft_ms_per_token + target_ms[g]),
+ *     E(g) = (1 - alpha^(g+1)) / (1 - alpha)   (g + 1 at alpha = 1),
+ * the smallest such g on ties.
+ *   target_ms  host [gamma_max + 1]: verification time of a pass with g
+ *              drafts (entries gamma_min .. gamma_max read, each > 0); a
+ *              constant array gives the article's fixed target time
+ * SPEC_EINVAL for bad bounds or times; *out set on SPEC_OK. */
+typedef struct spec_gamma_ctl* spec_gamma_ctl_t;
+spec_status spec_gamma_ctl_create(int32_t n_seq, int32_t gamma_min, int32_t gamma_max,
+                                  int32_t gamma_init, double draft_ms_per_token,
+                                  const double* target_ms, spec_gamma_ctl_t* out);
+spec_status spec_gamma_ctl_destroy(spec_gamma_ctl_t c);
+
+/* Record one step of every sequence and return the gamma of its next step.
+ *   n_accepted  host [n_seq]: the step's n_accepted (-1: refused row, which
+ *               records nothing)
+ *   gamma_used  host [n_seq]: the gamma each sequence was verified with
+ *   gamma_next  host [n_seq] out
+ * SPEC_EINVAL (nothing recorded) when some n_accepted exceeds its gamma. */
+spec_status spec_gamma_ctl_update(spec_gamma_ctl_t c, const int32_t* n_accepted,
+                                  const int32_t* gamma_used, int32_t* gamma_next);
+
+/* Rolling acceptance rate of sequence seq (-1 for a bad index). */
+double spec_gamma_ctl_alpha(spec_gamma_ctl_t c, int32_t seq);
+
+/* The gamma the controller picks for acceptance rate alpha in [0, 1]
+ * (-1 for a bad alpha). */
+int32_t spec_gamma_ctl_optimal(spec_gamma_ctl_t c, double alpha);
+
+/* Ragged repacking after a verification step of B sequences, on the device
+ * (one work group, asynchronous on `stream`, no host round trip).  Row b
+ * emitted count_b = n_accepted[b] + 1 tokens when 0 <= n_accepted[b] <=
+ * gamma, else none (a refused row).  All pointers are device memory:
+ *   n_accepted   int32 [B], emitted int32 [B][gamma+1] (spec_verify's outputs)
+ *   committed    int32 [B] in/out: committed length, advanced by count_b
+ *   tokens       int32 [B*(gamma+1)] out: the emitted tokens, rows end to end
+ *   offsets      int32 [B+1] out: row b's tokens are tokens[offsets[b] ..
+ *                offsets[b+1])
+ *   order        int32 [B] out: sequence ids sorted by count, stably (ids
+ *                ascending within a count): micro-batches by accepted count
+ *   bin_offsets  int32 [gamma+3] out: sequences with count c are
+ *                order[bin_offsets[c] .. bin_offsets[c+1]), c = 0 .. gamma+1
+ *   stats        int32 [2] out: padded width max(count) of one padded batch,
+ *                and its waste B * width - sum(count)
+ * SPEC_EINVAL for B < 1, gamma < 0, gamma > 254 or a null pointer. */
+spec_status spec_repack(int32_t B, int32_t gamma, const int32_t* n_accepted,
+                        const int32_t* emitted, int32_t* committed, int32_t* tokens,
+                        int32_t* offsets, int32_t* order, int32_t* bin_offsets, int32_t* stats,
+                        void* stream);
+
 /* Static text for a status code. */
 const char* spec_status_string(spec_status s);
 

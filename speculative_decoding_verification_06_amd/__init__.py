@@ -25,7 +25,8 @@ EXPORTS = ["spec_weights_create", "spec_weights_destroy", "spec_workspace_size",
            "spec_verify_debug", "spec_workspace_size_from_logits", "spec_verify_from_logits",
            "spec_status_string", "spec_default_mfma_min_rows", "spec_profile_enable",
            "spec_profile_read", "spec_stream_read", "spec_verify_noalloc",
-           "spec_verify_tree_greedy"]
+           "spec_verify_tree_greedy", "spec_gamma_ctl_create", "spec_gamma_ctl_destroy",
+           "spec_gamma_ctl_update", "spec_gamma_ctl_alpha", "spec_gamma_ctl_optimal", "spec_repack"]
 # Every symbol include/specverify_diag.h declares.
 DIAG_EXPORTS = ["spec_diag_access_check"]
 
@@ -69,6 +70,20 @@ def load():
     lib.spec_verify_noalloc.restype = i32
     lib.spec_verify_tree_greedy.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.spec_verify_tree_greedy.restype = i32
+    lib.spec_gamma_ctl_create.argtypes = [i32, i32, i32, i32, ctypes.c_double,
+                                          ctypes.POINTER(ctypes.c_double), ctypes.POINTER(vp)]
+    lib.spec_gamma_ctl_create.restype = i32
+    lib.spec_gamma_ctl_destroy.argtypes = [vp]
+    lib.spec_gamma_ctl_destroy.restype = i32
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.spec_gamma_ctl_update.argtypes = [vp, ip, ip, ip]
+    lib.spec_gamma_ctl_update.restype = i32
+    lib.spec_gamma_ctl_alpha.argtypes = [vp, i32]
+    lib.spec_gamma_ctl_alpha.restype = ctypes.c_double
+    lib.spec_gamma_ctl_optimal.argtypes = [vp, ctypes.c_double]
+    lib.spec_gamma_ctl_optimal.restype = i32
+    lib.spec_repack.argtypes = [i32, i32] + [vp] * 8 + [vp]
+    lib.spec_repack.restype = i32
     lib.spec_verify_debug.argtypes = common + [vp, vp, vp]
     lib.spec_verify_debug.restype = i32
     lib.spec_workspace_size_from_logits.argtypes = [i32, i32, i32]
@@ -281,6 +296,60 @@ def verify_tree_greedy(w, hidden, parent, tokens, want_logits=False, workspace=N
                                           workspace.numel(), _stream(stream), _ptr(logits)),
            "spec_verify_tree_greedy")
     return n_acc, emitted, path, logits
+
+
+class GammaController:
+    """spec_gamma_ctl_*: per-sequence speculation-depth choice (host only).
+    target_ms: verification time per pass for gamma = 0 .. gamma_max."""
+
+    def __init__(self, n_seq, gamma_min, gamma_max, gamma_init, draft_ms_per_token, target_ms):
+        lib = load()
+        arr = (ctypes.c_double * len(target_ms))(*[float(x) for x in target_ms])
+        if len(target_ms) <= gamma_max:
+            raise ValueError("target_ms needs gamma_max + 1 entries")
+        h = ctypes.c_void_p()
+        _check(lib.spec_gamma_ctl_create(int(n_seq), int(gamma_min), int(gamma_max), int(gamma_init),
+                                         float(draft_ms_per_token), arr, ctypes.byref(h)),
+               "spec_gamma_ctl_create")
+        self.handle, self.n_seq = h, int(n_seq)
+
+    def update(self, n_accepted, gamma_used):
+        n = (ctypes.c_int32 * self.n_seq)(*[int(x) for x in n_accepted])
+        g = (ctypes.c_int32 * self.n_seq)(*[int(x) for x in gamma_used])
+        out = (ctypes.c_int32 * self.n_seq)()
+        _check(load().spec_gamma_ctl_update(self.handle, n, g, out), "spec_gamma_ctl_update")
+        return list(out)
+
+    def alpha(self, seq):
+        return load().spec_gamma_ctl_alpha(self.handle, int(seq))
+
+    def optimal(self, alpha):
+        return load().spec_gamma_ctl_optimal(self.handle, float(alpha))
+
+    def close(self):
+        if getattr(self, "handle", None):
+            load().spec_gamma_ctl_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def repack(n_accepted, emitted, committed, stream=None):
+    """spec_repack on device tensors (committed is advanced in place).
+    Returns (tokens, offsets, order, bin_offsets, stats) device tensors."""
+    B, G1 = emitted.shape
+    for t, name in ((n_accepted, "n_accepted"), (emitted, "emitted"), (committed, "committed")):
+        _dev(t, torch.int32, name)
+    z = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")
+    tokens, offsets, order, bins, stats = z(B * G1), z(B + 1), z(B), z(G1 + 2), z(2)
+    _check(load().spec_repack(B, G1 - 1, _ptr(n_accepted), _ptr(emitted), _ptr(committed),
+                              _ptr(tokens), _ptr(offsets), _ptr(order), _ptr(bins), _ptr(stats),
+                              _stream(stream)), "spec_repack")
+    return tokens, offsets, order, bins, stats
 
 
 def workspace_size_from_logits(B, gamma, V):
