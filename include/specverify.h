@@ -304,6 +304,58 @@ spec_status spec_repack(int32_t B, int32_t gamma, const int32_t* n_accepted,
                         int32_t* offsets, int32_t* order, int32_t* bin_offsets, int32_t* stats,
                         void* stream);
 
+/* ---- Attention of the verification pass's new rows over a KV-cached
+ * prefix, and the commit of the accepted rows ("Build a Speculative
+ * Decoding Engine to Cut LLM Latency by 3x", scalablesystem.dev, KV Cache
+ * Management for Dual Models and Rollback Protocol; "Speculative Decoding:
+ * Speeding Sequential Generation", aicomputerinstitute.com, Constructing
+ * the Tree Attention Mask in Code).
+ *
+ * Cache layout (device, bf16 bits): k_cache, v_cache [B][Hkv][max_seq][hd].
+ * Sequence b has cache_len[b] committed positions; the keys and values of
+ * its n_new new rows (the root, then the drafts in chain or tree order,
+ * already projected and position-encoded by the caller, position id =
+ * depth) sit at slots cache_len[b] .. cache_len[b] + n_new - 1.  A
+ * cache_len outside [0, max_seq - n_new] is clamped into it. */
+
+/* Workspace bytes of spec_decode_attention, 0 for invalid shapes. */
+size_t spec_attention_workspace_size(int32_t B, int32_t n_new, int32_t H, int32_t Hkv,
+                                     int32_t head_dim, int32_t max_seq);
+
+/* out[b][i][h][:] = sum_t softmax_t(scale * q[b][i][h] . k[b][kv][t]) v[b][kv][t]
+ * over the slots new row i sees: every committed slot, itself, and its
+ * ancestors among the new rows; kv = h / (H / Hkv) (grouped-query heads).
+ *   q          device fp32 [B][n_new][H][hd]
+ *   cache_len  device int32 [B]
+ *   parent     device int32 [B][n_new] or NULL: the parent of each new row
+ *              among the new rows (-1: none; parents precede children, a
+ *              value outside [-1, i) counts as -1); NULL is a chain
+ *              (parent i - 1), i.e. the causal mask
+ *   out        device fp32 [B][n_new][H][hd]
+ *   workspace  spec_attention_workspace_size bytes, 256-byte aligned
+ * Shapes: 1 <= n_new <= 64, H a multiple of Hkv, hd 64 or 128, caches
+ * 16-byte aligned; SPEC_EINVAL / SPEC_EWORKSPACE otherwise.  Results are
+ * run-to-run identical (no atomics; partials merged in a fixed order). */
+spec_status spec_decode_attention(int32_t B, int32_t n_new, int32_t H, int32_t Hkv,
+                                  int32_t head_dim, int32_t max_seq, const float* q,
+                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const int32_t* cache_len, const int32_t* parent, float scale,
+                                  float* out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* Commit one step: keep the root and the n_accepted[b] accepted rows, drop
+ * the rest by not moving past them (the memory is reused next step).  With
+ * path (device int32 [B][n_new - 1], the accepted nodes of a tree walk,
+ * node j being new row j + 1), the accepted rows' keys and values are first
+ * gathered to slots cache_len[b] + 1 .. cache_len[b] + n_accepted[b] for
+ * every KV head; path NULL is a chain, whose accepted rows already sit
+ * there (k_cache and v_cache may then be NULL).  Then cache_len[b] +=
+ * n_accepted[b] + 1 on the device; a row with n_accepted < 0 is left alone. */
+spec_status spec_kv_commit(int32_t B, int32_t n_new, int32_t Hkv, int32_t head_dim,
+                           int32_t max_seq, uint16_t* k_cache, uint16_t* v_cache,
+                           int32_t* cache_len, const int32_t* n_accepted, const int32_t* path,
+                           void* stream);
+
 /* Static text for a status code. */
 const char* spec_status_string(spec_status s);
 

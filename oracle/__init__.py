@@ -36,6 +36,9 @@ Modules:
   verify  -- spec_verify / spec_verify_from_logits over a batch
   tree    -- greedy verification of a draft tree: ancestor mask, depths,
              the walk down passing children
+  control -- the gamma controller and the ragged repack of a batch
+  attention -- the new rows' attention over a KV-cached prefix (chain or
+             tree mask, grouped-query heads) and the KV commit
 
 Parity status of each part (what pins it) is listed in the module docstrings.
 """
@@ -46,7 +49,7 @@ from .rule import (warp_logits, warp_probs, nucleus_mask, accept_test,
                    inverse_cdf, cdf_band, verify_row, verify_row_greedy, MARGIN, TopP,
                    Decision)
 from .verify import spec_verify, spec_verify_from_logits, VerifyResult
-from . import tree
+from . import attention, control, tree
 
 __all__ = [
     "philox4x64_10", "row_uniforms", "PURPOSE_VERIFY", "PURPOSE_DRAFT",

@@ -26,7 +26,8 @@ EXPORTS = ["spec_weights_create", "spec_weights_destroy", "spec_workspace_size",
            "spec_status_string", "spec_default_mfma_min_rows", "spec_profile_enable",
            "spec_profile_read", "spec_stream_read", "spec_verify_noalloc",
            "spec_verify_tree_greedy", "spec_gamma_ctl_create", "spec_gamma_ctl_destroy",
-           "spec_gamma_ctl_update", "spec_gamma_ctl_alpha", "spec_gamma_ctl_optimal", "spec_repack"]
+           "spec_gamma_ctl_update", "spec_gamma_ctl_alpha", "spec_gamma_ctl_optimal", "spec_repack",
+           "spec_attention_workspace_size", "spec_decode_attention", "spec_kv_commit"]
 # Every symbol include/specverify_diag.h declares.
 DIAG_EXPORTS = ["spec_diag_access_check"]
 
@@ -84,6 +85,12 @@ def load():
     lib.spec_gamma_ctl_optimal.restype = i32
     lib.spec_repack.argtypes = [i32, i32] + [vp] * 8 + [vp]
     lib.spec_repack.restype = i32
+    lib.spec_attention_workspace_size.argtypes = [i32] * 6
+    lib.spec_attention_workspace_size.restype = sz
+    lib.spec_decode_attention.argtypes = [i32] * 6 + [vp] * 5 + [f32, vp, vp, sz, vp]
+    lib.spec_decode_attention.restype = i32
+    lib.spec_kv_commit.argtypes = [i32] * 5 + [vp] * 6
+    lib.spec_kv_commit.restype = i32
     lib.spec_verify_debug.argtypes = common + [vp, vp, vp]
     lib.spec_verify_debug.restype = i32
     lib.spec_workspace_size_from_logits.argtypes = [i32, i32, i32]
@@ -350,6 +357,54 @@ def repack(n_accepted, emitted, committed, stream=None):
                               _ptr(tokens), _ptr(offsets), _ptr(order), _ptr(bins), _ptr(stats),
                               _stream(stream)), "spec_repack")
     return tokens, offsets, order, bins, stats
+
+
+def _bf16_bits(t, name):
+    if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+    return t
+
+
+def attention_workspace_size(B, n_new, H, Hkv, head_dim, max_seq):
+    return int(load().spec_attention_workspace_size(B, n_new, H, Hkv, head_dim, max_seq))
+
+
+def decode_attention(q, k_cache, v_cache, cache_len, parent=None, scale=None, out=None,
+                     workspace=None, stream=None):
+    """spec_decode_attention; q [B][n_new][H][hd] fp32, caches
+    [B][Hkv][max_seq][hd] bf16, cache_len [B] int32, parent [B][n_new] int32
+    or None (chain).  Returns out [B][n_new][H][hd] fp32."""
+    B, n_new, H, hd = q.shape
+    Hkv, max_seq = k_cache.shape[1], k_cache.shape[2]
+    _dev(q, torch.float32, "q")
+    _bf16_bits(k_cache, "k_cache")
+    _bf16_bits(v_cache, "v_cache")
+    _dev(cache_len, torch.int32, "cache_len")
+    if parent is not None:
+        _dev(parent, torch.int32, "parent")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = attention_workspace_size(B, n_new, H, Hkv, hd, max_seq)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / hd ** 0.5 if scale is None else float(scale)
+    _check(load().spec_decode_attention(B, n_new, H, Hkv, hd, max_seq, _ptr(q), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(cache_len), _ptr(parent), scale,
+                                        _ptr(out), _ptr(workspace), workspace.numel(),
+                                        _stream(stream)), "spec_decode_attention")
+    return out
+
+
+def kv_commit(k_cache, v_cache, cache_len, n_accepted, n_new, path=None, stream=None):
+    """spec_kv_commit (cache_len advanced in place, the caches gathered for a tree)."""
+    B, Hkv, max_seq, hd = k_cache.shape
+    _dev(cache_len, torch.int32, "cache_len")
+    _dev(n_accepted, torch.int32, "n_accepted")
+    if path is not None:
+        _dev(path, torch.int32, "path")
+    _check(load().spec_kv_commit(B, n_new, Hkv, hd, max_seq, _ptr(_bf16_bits(k_cache, "k_cache")),
+                                 _ptr(_bf16_bits(v_cache, "v_cache")), _ptr(cache_len),
+                                 _ptr(n_accepted), _ptr(path), _stream(stream)), "spec_kv_commit")
 
 
 def workspace_size_from_logits(B, gamma, V):

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["gemm.hip", "sample.hip", "pack.hip", "probe.hip", "control.hip", "api.hip"]
+SOURCES = ["gemm.hip", "sample.hip", "pack.hip", "probe.hip", "control.hip", "attention.hip",
+           "api.hip"]
 ARCH = "gfx950"
 
 
