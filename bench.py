@@ -14,6 +14,7 @@ GEMM kernels (algorithmic weight bytes / their event-timed duration vs
 
     python bench.py [--steps K] [--warmup W] [--workload mid]
     python bench.py --sweep-gamma      (verify cost per pass against gamma)
+    python bench.py --attention        (decode attention over a KV-cached prefix)
 """
 
 import argparse
@@ -48,17 +49,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--attention", action="store_true",
+                    help="only time the decode attention over a KV-cached prefix on its three "
+                         "workloads (one JSON line each)")
     ap.add_argument("--sweep-gamma", action="store_true",
                     help="only print the verify cost per pass for gamma = 0..8, 16 .. 160 at B = 1 "
                          "on the mid and large models (one JSON line per point)")
     return ap.parse_args()
 
 
+# the sources the weight-streaming GEMM kernels are built from
+GEMM_SOURCES = ("gemm.hip", "common.h", "internal.h")
+
+
 def source_hash():
-    """Hash of the kernel sources, to tie stored counter readings to them."""
+    """Hash of the GEMM kernels' sources, to tie stored counter readings to them."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_verification_06_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in GEMM_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -316,6 +324,71 @@ def sweep_gamma(progress, steps=200, warmup=20):
         torch.cuda.empty_cache()
 
 
+# ---------------------------------------------------------------- decode attention
+
+# (name, B, new rows, H, Hkv, head dim, committed length, tree): a 70B-class
+# target layer held on one GPU (64 query heads over 8 KV heads of 128
+# dimensions, the KV layout of the scalablesystem.dev article) with an 8K
+# context and a gamma = 4 chain; 32 sequences at the article's typical 2K
+# chat context with gamma = 6; and the 14-node tree of the
+# aicomputerinstitute.com chapter plus its root, 4 sequences at 8K.
+ATTN_WORKLOADS = [
+    ("attn-chain-8k", 1, 5, 64, 8, 128, 8187, False),
+    ("attn-batch-2k", 32, 7, 64, 8, 128, 2048, False),
+    ("attn-tree-8k", 4, 15, 64, 8, 128, 8177, True),
+]
+
+
+def bench_attention(progress, steps=200, warmup=20):
+    """Decode attention: per call, the keys and values of every visible
+    position are read once (2 * Hkv * hd * 2 bytes per position) plus the
+    queries and outputs; GB/s against 8 TB/s and the measured read ceiling."""
+    import numpy as np
+    import torch
+    import synth
+    import speculative_decoding_verification_06_amd as sv
+    torch.cuda.set_device(0)
+    for name, B, n_new, H, Hkv, hd, L, tree in ATTN_WORKLOADS:
+        max_seq = (L + n_new + 7) // 8 * 8
+        g = torch.Generator(device="cuda")
+        g.manual_seed(synth.torch_seed(400, len(name)))
+        q = torch.randn((B, n_new, H, hd), generator=g, device="cuda")
+        kc = torch.randn((B, Hkv, max_seq, hd), generator=g, device="cuda").to(torch.bfloat16)
+        vc = torch.randn((B, Hkv, hd, max_seq), generator=g, device="cuda").to(torch.bfloat16)
+        cl = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        parent = None
+        if tree:
+            par = [-1] + [0, 0] + [1 + (j - 3) // 2 for j in range(3, n_new)]   # root, 2, 4, 8 children
+            parent = torch.tensor([par] * B, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(q)
+        ws = torch.empty(sv.attention_workspace_size(B, n_new, H, Hkv, hd, max_seq),
+                         dtype=torch.uint8, device="cuda")
+        for _ in range(warmup):
+            sv.decode_attention(q, kc, vc, cl, parent, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            sv.decode_attention(q, kc, vc, cl, parent, out=out, workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        kv_bytes = B * (L + n_new) * Hkv * hd * 2 * 2
+        io_bytes = 2 * B * n_new * H * hd * 4
+        gbs = (kv_bytes + io_bytes) / (us * 1e-6) / 1e9
+        ceiling = read_ceiling(torch, sv, kv_bytes)
+        print(json.dumps({
+            "bench": "decode_attention", "workload": name, "B": B, "new_rows": n_new, "H": H,
+            "Hkv": Hkv, "head_dim": hd, "committed_len": L, "tree": tree,
+            "us_per_call": us, "bytes_per_call": kv_bytes + io_bytes, "hbm_gbs": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS, "read_ceiling_gbs": ceiling["gbs"],
+            "frac_of_read_ceiling": gbs / ceiling["gbs"],
+            "note": "one call = the attention launch plus the split-combine launch"}), flush=True)
+        progress(f"attention {name}: {us:.1f} us/call, {gbs:.0f} GB/s")
+        del kc, vc
+        torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -334,6 +407,9 @@ def main():
 
     if args.sweep_gamma:
         sweep_gamma(progress)
+        return
+    if args.attention:
+        bench_attention(progress)
         return
 
     progress("importing torch")

@@ -311,7 +311,10 @@ spec_status spec_repack(int32_t B, int32_t gamma, const int32_t* n_accepted,
  * Speeding Sequential Generation", aicomputerinstitute.com, Constructing
  * the Tree Attention Mask in Code).
  *
- * Cache layout (device, bf16 bits): k_cache, v_cache [B][Hkv][max_seq][hd].
+ * Cache layout (device, bf16 bits): k_cache [B][Hkv][max_seq][hd] (a key's
+ * head dimension contiguous) and v_cache [B][Hkv][hd][max_seq] (values
+ * head-dimension major, so eight consecutive positions of one dimension
+ * are one 16-byte MFMA operand); max_seq a multiple of 8.
  * Sequence b has cache_len[b] committed positions; the keys and values of
  * its n_new new rows (the root, then the drafts in chain or tree order,
  * already projected and position-encoded by the caller, position id =
@@ -333,8 +336,10 @@ size_t spec_attention_workspace_size(int32_t B, int32_t n_new, int32_t H, int32_
  *              (parent i - 1), i.e. the causal mask
  *   out        device fp32 [B][n_new][H][hd]
  *   workspace  spec_attention_workspace_size bytes, 256-byte aligned
- * Shapes: 1 <= n_new <= 64, H a multiple of Hkv, hd 64 or 128, caches
- * 16-byte aligned; SPEC_EINVAL / SPEC_EWORKSPACE otherwise.  Results are
+ * Shapes: 1 <= n_new <= 64, H a multiple of Hkv, hd 64 or 128, max_seq a
+ * multiple of 8, caches 16-byte aligned; SPEC_EINVAL / SPEC_EWORKSPACE
+ * otherwise.  Both products run on bf16 MFMA with the queries and the
+ * probabilities split into three bf16 terms (exact).  Results are
  * run-to-run identical (no atomics; partials merged in a fixed order). */
 spec_status spec_decode_attention(int32_t B, int32_t n_new, int32_t H, int32_t Hkv,
                                   int32_t head_dim, int32_t max_seq, const float* q,
@@ -348,7 +353,8 @@ spec_status spec_decode_attention(int32_t B, int32_t n_new, int32_t H, int32_t H
  * path (device int32 [B][n_new - 1], the accepted nodes of a tree walk,
  * node j being new row j + 1), the accepted rows' keys and values are first
  * gathered to slots cache_len[b] + 1 .. cache_len[b] + n_accepted[b] for
- * every KV head; path NULL is a chain, whose accepted rows already sit
+ * every KV head (caches in the layout above); path NULL is a chain, whose
+ * accepted rows already sit
  * there (k_cache and v_cache may then be NULL).  Then cache_len[b] +=
  * n_accepted[b] + 1 on the device; a row with n_accepted < 0 is left alone. */
 spec_status spec_kv_commit(int32_t B, int32_t n_new, int32_t Hkv, int32_t head_dim,

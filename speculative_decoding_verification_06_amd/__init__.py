@@ -371,11 +371,14 @@ def attention_workspace_size(B, n_new, H, Hkv, head_dim, max_seq):
 
 def decode_attention(q, k_cache, v_cache, cache_len, parent=None, scale=None, out=None,
                      workspace=None, stream=None):
-    """spec_decode_attention; q [B][n_new][H][hd] fp32, caches
-    [B][Hkv][max_seq][hd] bf16, cache_len [B] int32, parent [B][n_new] int32
-    or None (chain).  Returns out [B][n_new][H][hd] fp32."""
+    """spec_decode_attention; q [B][n_new][H][hd] fp32, k_cache
+    [B][Hkv][max_seq][hd] and v_cache [B][Hkv][hd][max_seq] bf16, cache_len
+    [B] int32, parent [B][n_new] int32 or None (chain).  Returns out
+    [B][n_new][H][hd] fp32."""
     B, n_new, H, hd = q.shape
     Hkv, max_seq = k_cache.shape[1], k_cache.shape[2]
+    if tuple(v_cache.shape) != (B, Hkv, hd, max_seq):
+        raise ValueError("v_cache must be [B][Hkv][hd][max_seq]")
     _dev(q, torch.float32, "q")
     _bf16_bits(k_cache, "k_cache")
     _bf16_bits(v_cache, "v_cache")
@@ -396,7 +399,8 @@ def decode_attention(q, k_cache, v_cache, cache_len, parent=None, scale=None, ou
 
 
 def kv_commit(k_cache, v_cache, cache_len, n_accepted, n_new, path=None, stream=None):
-    """spec_kv_commit (cache_len advanced in place, the caches gathered for a tree)."""
+    """spec_kv_commit (cache_len advanced in place, the caches gathered for a
+    tree); k_cache [B][Hkv][max_seq][hd], v_cache [B][Hkv][hd][max_seq]."""
     B, Hkv, max_seq, hd = k_cache.shape
     _dev(cache_len, torch.int32, "cache_len")
     _dev(n_accepted, torch.int32, "n_accepted")

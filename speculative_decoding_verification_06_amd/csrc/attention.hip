@@ -5,26 +5,35 @@
 // scalablesystem.dev, KV Cache Management for Dual Models, Rollback
 // Protocol).
 //
-// Cache layout [B][Hkv][max_seq][HD] bf16: one key's (or value's) head
-// dimension is one contiguous 2*HD-byte row.  New row i of sequence b is the
-// query q[b][i][h][:] (fp32); its key and value sit at slot L_b + i.  Row i
-// sees slots 0 .. L_b - 1 and the new slots of itself and its ancestors.
+// Cache layout, bf16: keys [B][Hkv][max_seq][HD] (one key's head dimension
+// is a contiguous row), values [B][Hkv][HD][max_seq] (head-dimension major:
+// eight consecutive positions of one dimension are 16 contiguous bytes, the
+// B operand of the P V product).  New row i of sequence b is the query
+// q[b][i][h][:] (fp32); its key and value sit at slot L_b + i.  Row i sees
+// slots 0 .. L_b - 1 and the new slots of itself and its ancestors.
 //
 // Work decomposition: a work group of 4 waves owns (sequence, KV head, group
-// of up to kRows query rows: new rows x the H / Hkv query heads sharing the
-// KV head, split of the keys); each wave streams its own tiles of 64 keys,
-// so every key and value byte of a split is read once for all query rows of
+// of up to 64 query rows: new rows x the H / Hkv query heads sharing the KV
+// head, split of the keys); each wave streams its own tiles of 64 keys, so
+// every key and value byte of a split is read once for all query rows of
 // the group (the weight-streaming idea of the GEMMs, applied to the cache).
-// Scores: lane = key, the lane's key row in registers, the group's query
-// rows read with wave-uniform addresses.  P V: lane = 2 (HD 128) or 1 (HD
-// 64) head dimensions, one coalesced value row per key, the tile's
-// probabilities through LDS.  Online softmax per row; every wave writes its
-// partial (max, sum, unnormalised output), and a second kernel merges the
-// partials in a fixed order, so results are run-to-run identical.
+// Both products run on bf16 MFMA (16x16x32): the queries are split once
+// into three bf16 terms (exact) and staged in LDS as A fragments; the keys
+// are B fragments loaded straight from the cache; the scores' softmax runs
+// on the accumulators (a row's 64 scores sit in one 16-lane group x 4
+// tiles); the probabilities go through LDS into the A layout, split into
+// two terms (2^-16 relative), against value fragments loaded straight from
+// the head-dimension-major value cache.  Online softmax per row; the four
+// waves' states are merged in LDS and every work group writes one partial
+// (max, sum, unnormalised output); a second kernel merges the splits'
+// partials in a fixed order, so results are run-to-run identical.  The softmax uses the hardware exp (relative error about
+// |x| 2^-23 for an argument x, far below the score error of an fp32
+// 128-term dot product that bounds the output).
 
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -36,19 +45,19 @@ namespace sv {
 
 constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = kAttnWaves * kWave;
-constexpr int kAttnRows = 32;      // query rows of a work group
-constexpr int kAttnTile = 64;      // keys per wave tile
+constexpr int kAttnMaxRT = 4;      // 16-row MFMA tiles of query rows per work group (at most)
+constexpr int kAttnTile = 64;      // keys per wave tile: four 16-key MFMA tiles
 
 struct AttnArgs {
   int B, n_new, H, Hkv, G, max_seq, R, RG, S;   // R = n_new * G rows, RG row groups, S splits
   const float* q;            // [B][n_new][H][HD]
   const uint16_t* k;         // [B][Hkv][max_seq][HD]
-  const uint16_t* v;
+  const uint16_t* vt;        // [B][Hkv][HD][max_seq]  (values, head-dimension major)
   const int* cache_len;      // [B]
   const int* parent;         // [B][n_new] or null (chain)
   float scale;
-  float* part_o;             // [B][Hkv][RG][S * waves][kAttnRows][HD]
-  float* part_ml;            // [B][Hkv][RG][S * waves][kAttnRows][2]
+  float* part_o;             // [B][Hkv][RG][S][16 RT][HD]
+  float* part_ml;            // [B][Hkv][RG][S][16 RT][2]
   float* out;                // [B][n_new][H][HD]
 };
 
@@ -58,19 +67,83 @@ __device__ __forceinline__ int attn_len(const AttnArgs& a, int b) {
   return L < 0 ? 0 : (L > a.max_seq - a.n_new ? a.max_seq - a.n_new : L);
 }
 
-template <int HD>
+// Eight fp32 values as three bf16 A/B fragments (hi, mid, lo): exact, so a
+// bf16 MFMA over the three reproduces an fp32 product up to accumulation.
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 (&f)[3]) {
+  uint32_t t[3][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t a0, b0, c0, a1, b1, c1;
+    split3_bf16(x[2 * j], a0, b0, c0);
+    split3_bf16(x[2 * j + 1], a1, b1, c1);
+    t[0][j] = a0 | (a1 << 16);
+    t[1][j] = b0 | (b1 << 16);
+    t[2][j] = c0 | (c1 << 16);
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const u32x4 u = {t[p][0], t[p][1], t[p][2], t[p][3]};
+    f[p] = __builtin_bit_cast(bf16x8, u);
+  }
+}
+
+// Eight fp32 values in [0, 1] as two bf16 fragments (hi, lo by truncation):
+// |x - hi - lo| <= 2^-16 |x|, for the softmax probabilities.
+__device__ __forceinline__ void split8_2(const float (&x)[8], bf16x8 (&f)[2]) {
+  uint32_t t[2][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t h0 = __float_as_uint(x[2 * j]) & 0xffff0000u;
+    const uint32_t h1 = __float_as_uint(x[2 * j + 1]) & 0xffff0000u;
+    const uint32_t l0 = __float_as_uint(x[2 * j] - __uint_as_float(h0)) >> 16;
+    const uint32_t l1 = __float_as_uint(x[2 * j + 1] - __uint_as_float(h1)) >> 16;
+    t[0][j] = (h0 >> 16) | h1;
+    t[1][j] = l0 | (l1 << 16);
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const u32x4 u = {t[p][0], t[p][1], t[p][2], t[p][3]};
+    f[p] = __builtin_bit_cast(bf16x8, u);
+  }
+}
+
+// Zero the bf16 values of a fragment whose keys (first key k0, eight in a
+// row) are at or past `end`: memory past the visible keys may hold anything.
+__device__ __forceinline__ bf16x8 zero_past(bf16x8 f, int k0, int end) {
+  if (k0 + 8 <= end) return f;
+  u32x4 u = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w = u[j];
+    if (k0 + 2 * j >= end) w &= 0xffff0000u;
+    if (k0 + 2 * j + 1 >= end) w &= 0x0000ffffu;
+    u[j] = w;
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+template <int HD, int RT>
 __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
-  constexpr int DPL = HD / kWave;                  // head dimensions per lane in P V
-  constexpr int KCH = HD / 8;                      // 16-byte chunks of one key row
+  constexpr int KS = HD / 32;                      // 32-dimension k-steps of a score
+  constexpr int DT = HD / 16;                      // 16-dimension output tiles
+  constexpr int ROWS = 16 * RT;                    // query rows of the work group
   __shared__ uint64_t anc[64];                     // visible new rows of each new row
-  __shared__ float pbuf[kAttnWaves][kAttnRows][kAttnTile];
-  const int lane = threadIdx.x & 63;
+  // the loop's buffers (query A fragments in three terms; each wave's tile
+  // of probabilities), reused after the loop to merge the four waves' states
+  constexpr size_t kLoopBytes = sizeof(bf16x8) * RT * KS * 3 * kWave +
+                                sizeof(float) * kAttnWaves * ROWS * (kAttnTile + 4);
+  constexpr size_t kMergeBytes = sizeof(float) * kAttnWaves * ROWS * (HD + 2);
+  __shared__ __align__(16) unsigned char smem[kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes];
+  auto& qf = *reinterpret_cast<bf16x8 (*)[RT][KS][3][kWave]>(smem);
+  auto& pbuf = *reinterpret_cast<float (*)[kAttnWaves][ROWS][kAttnTile + 4]>(
+      smem + sizeof(bf16x8) * RT * KS * 3 * kWave);
+  const int lane = threadIdx.x & 63, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, rg = blockIdx.y % a.RG, kvh = blockIdx.y / a.RG, b = blockIdx.z;
   const int L = attn_len(a, b), T = L + a.n_new;
-  const int r0 = rg * kAttnRows, nr = min(kAttnRows, a.R - r0);
+  const int r0 = rg * ROWS, nr = min(ROWS, a.R - r0);
 
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     uint64_t m = 0;
     for (int i = 0; i < a.n_new; ++i) {
       int p = a.parent ? a.parent[(size_t)b * a.n_new + i] : i - 1;
@@ -78,6 +151,29 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
       m = (p >= 0 ? anc[p] : 0ull) | (1ull << i);
       anc[i] = m;
     }
+  }
+  // query fragments: lane L of tile rt, k-step ks holds row rt*16 + L%16 at
+  // dimensions 32 ks + 8 (L/16) .. + 7, as three bf16 terms (rows past the
+  // group are zero)
+  for (int x = tid; x < RT * KS * kWave; x += kAttnThreads) {
+    const int l = x % kWave, ks = (x / kWave) % KS, rt = x / (kWave * KS);
+    const int r = rt * 16 + (l & 15);
+    float v[8];
+    if (r < nr) {
+      const int rr = r0 + r, i = rr / a.G, h = kvh * a.G + rr % a.G;
+      const float4* qp = reinterpret_cast<const float4*>(
+          a.q + (((size_t)b * a.n_new + i) * a.H + h) * HD + ks * 32 + 8 * (l >> 4));
+      const float4 u0 = qp[0], u1 = qp[1];
+      v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+      v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.f;
+    }
+    bf16x8 f[3];
+    split8(v, f);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) qf[rt][ks][p][l] = f[p];
   }
   __syncthreads();
 
@@ -88,141 +184,224 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   const int w0 = min(s1, s0 + wave * per_wave), w1 = min(s1, w0 + per_wave);
 
   const uint16_t* K = a.k + ((size_t)b * a.Hkv + kvh) * a.max_seq * HD;
-  const uint16_t* V = a.v + ((size_t)b * a.Hkv + kvh) * a.max_seq * HD;
-  // query row r of the group: new row i = r / G, head kvh * G + r % G
-  auto qrow = [&](int r) -> const float* {
-    const int rr = r0 + r, i = rr / a.G, h = kvh * a.G + rr % a.G;
-    return a.q + (((size_t)b * a.n_new + i) * a.H + h) * HD;
+  const uint16_t* Vt = a.vt + ((size_t)b * a.Hkv + kvh) * (size_t)HD * a.max_seq;
+  const int g = lane >> 4, c = lane & 15;          // C layout: rows 4 g + j, column c
+
+  // per row this lane holds (tile rt, j): running max, sum; new-row index
+  float m[RT][4], l[RT][4];
+  int rowi[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[rt][j] = -INFINITY;
+      l[rt][j] = 0.f;
+      const int r = rt * 16 + 4 * g + j;
+      rowi[rt][j] = r < nr ? (r0 + r) / a.G : -1;
+    }
+  f32x4 acc_o[RT][DT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc_o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // key fragments: key tile kt, k-step ks: lane holds key t + 16 kt + c at
+  // dimensions 32 ks + 8 g .. + 7 (one 16-byte load from the key row)
+  bf16x8 kf[4][KS];
+  auto load_k = [&](int t) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = min(t + 16 * kt + c, w1 - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[kt][ks] = *reinterpret_cast<const bf16x8*>(K + (size_t)key * HD + 32 * ks + 8 * g);
+    }
   };
-
-  float m[kAttnRows], l[kAttnRows], o[kAttnRows][DPL];
+  // value fragments: k-step kv (32 keys), dimension tile dt: lane holds
+  // dimension 16 dt + c at keys t + 32 kv + 8 g .. + 7 (16 bytes of the
+  // head-dimension-major value row); keys past w1 are zeroed
+  bf16x8 vf[2][DT];
+  auto load_v = [&](int t) {
 #pragma unroll
-  for (int r = 0; r < kAttnRows; ++r) {
-    m[r] = -INFINITY;
-    l[r] = 0.f;
+    for (int kv = 0; kv < 2; ++kv) {
+      const int k0 = t + 32 * kv + 8 * g;
+      const int kl = min(k0, a.max_seq - 8);       // in bounds; the values past w1 are zeroed
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) o[r][j] = 0.f;
+      for (int dt = 0; dt < DT; ++dt)
+        vf[kv][dt] = zero_past(*reinterpret_cast<const bf16x8*>(Vt + (size_t)(16 * dt + c) * a.max_seq + kl),
+                               kl, w1);
+    }
+  };
+  // The loads rotate through the tiles: a tile's keys are consumed by the
+  // score MFMAs, after which the next tile's keys are requested; its values
+  // by the P V MFMAs, after which the next tile's values are; so each load
+  // is in flight while the other half of the tile computes.
+  if (w0 < w1) {
+    load_k(w0);
+    load_v(w0);
   }
-
   for (int t = w0; t < w1; t += kAttnTile) {
-    const int key = t + lane;
-    const bool kv_ok = key < w1;
-    const int kc = kv_ok ? key : w1 - 1;           // in-bounds row for idle lanes
-    // the lane's key row, all chunks in flight
-    u32x4 kr[KCH];
-    const u32x4* kp = reinterpret_cast<const u32x4*>(K + (size_t)kc * HD);
+    const bool more = t + kAttnTile < w1;
+    // scores S[row][key] for the two row tiles and four key tiles
+    f32x4 acc_s[RT][4];
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) kr[c] = kp[c];
-    float s[kAttnRows];
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int r = 0; r < kAttnRows; ++r) s[r] = 0.f;
+      for (int kt = 0; kt < 4; ++kt) acc_s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      float kf[8];
-      kf[0] = bf16_lo(kr[c].x); kf[1] = bf16_hi(kr[c].x); kf[2] = bf16_lo(kr[c].y); kf[3] = bf16_hi(kr[c].y);
-      kf[4] = bf16_lo(kr[c].z); kf[5] = bf16_hi(kr[c].z); kf[6] = bf16_lo(kr[c].w); kf[7] = bf16_hi(kr[c].w);
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int r = 0; r < kAttnRows; ++r) {
-        if (r < nr) {
-          const float* qp = qrow(r) + c * 8;
+      for (int p = 0; p < 3; ++p)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) s[r] = fmaf(qp[j], kf[j], s[r]);
+        for (int rt = 0; rt < RT; ++rt) {
+          const bf16x8 qa = qf[rt][ks][p][lane];
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+            acc_s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kt][ks], acc_s[rt][kt], 0, 0, 0);
         }
-      }
-    }
-    // mask, scale, online softmax per row; probabilities to LDS
-    const int jn = key - L;                         // new slot index, when >= 0
+    if (more) load_k(t + kAttnTile);
+    // mask and online softmax per row: a row's 64 scores sit in its lane
+    // group's 16 lanes x 4 key tiles.  A tile wholly inside this wave's
+    // committed keys is visible to every row (no mask work).
+    const bool plain = t + kAttnTile <= min(L, w1);
+    bool moved = false;                              // some row's running max rose
+    float corr[RT][4];
 #pragma unroll
-    for (int r = 0; r < kAttnRows; ++r) {
-      if (r >= nr) continue;
-      const int i = (r0 + r) / a.G;
-      const bool vis = kv_ok && (jn < 0 || ((anc[i] >> jn) & 1ull));
-      const float sc = vis ? s[r] * a.scale : -INFINITY;
-      const float mt = wave_max(sc);
-      const float mn = fmaxf(m[r], mt);
-      float p = 0.f, corr = 1.f;
-      if (mn > -INFINITY) {
-        p = vis ? expf(sc - mn) : 0.f;
-        corr = m[r] > -INFINITY ? expf(m[r] - mn) : 0.f;
-      }
-      l[r] = l[r] * corr + wave_sum(p);
-      m[r] = mn;
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) o[r][j] *= corr;
-      pbuf[wave][r][lane] = p;
+      for (int j = 0; j < 4; ++j) {
+        const int i = rowi[rt][j];
+        const uint64_t vis_new = i >= 0 ? anc[i] : 0ull;
+        float sv[4];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          bool vis = i >= 0;
+          if (!plain) {
+            const int key = t + 16 * kt + c, jn = key - L;
+            vis = vis && key < w1 && (jn < 0 || ((vis_new >> jn) & 1ull));
+          }
+          sv[kt] = vis ? acc_s[rt][kt][j] * a.scale : -INFINITY;
+          mt = fmaxf(mt, sv[kt]);
+        }
+        mt = max16(mt);
+        const float mn = fmaxf(m[rt][j], mt);
+        float cr = 1.f, ps = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const float pv = mn > -INFINITY && sv[kt] > -INFINITY ? __expf(sv[kt] - mn) : 0.f;
+          ps += pv;
+          pbuf[wave][rt * 16 + 4 * g + j][16 * kt + c] = pv;
+        }
+        if (mn > m[rt][j]) {
+          cr = m[rt][j] > -INFINITY ? __expf(m[rt][j] - mn) : 0.f;
+          moved = true;
+        }
+        corr[rt][j] = cr;
+        l[rt][j] = l[rt][j] * cr + sum16(ps);
+        m[rt][j] = mn;
+      }
+    // rescale the output accumulators only when some row's max rose (the
+    // accumulators live in the MFMA registers, so a rescale is a round trip)
+    if (__any(moved)) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc_o[rt][dt][j] *= corr[rt][j];
     }
-    // the tile's probabilities are read by every lane of the wave below
+    // the tile's probabilities are read back below in the A-operand layout
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // P V: lane owns dimensions DPL * lane .. + DPL - 1; keys of the tile in
-    // batches of 16 with their value loads in flight
-    const int nk = min(kAttnTile, w1 - t);
-    for (int k0 = 0; k0 < nk; k0 += 16) {
-      float vv[16][DPL];
+    // O += P V: P's A fragments (row 16 rt + c, keys 32 kv + 8 g .. + 7),
+    // split into two bf16 terms (probabilities to 2^-16 relative)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int kk = min(k0 + u, nk - 1);
-        const uint16_t* vp = V + (size_t)(t + kk) * HD + DPL * lane;
-        if constexpr (DPL == 2) {
-          const uint32_t w2 = *reinterpret_cast<const uint32_t*>(vp);
-          vv[u][0] = bf16_lo(w2);
-          vv[u][1] = bf16_hi(w2);
-        } else {
-          vv[u][0] = __uint_as_float((uint32_t)vp[0] << 16);
-        }
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const float4* pp = reinterpret_cast<const float4*>(&pbuf[wave][rt * 16 + c][32 * kv + 8 * g]);
+        const float4 u0 = pp[0], u1 = pp[1];
+        const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        bf16x8 pf[2];
+        split8_2(x, pf);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            acc_o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[p], vf[kv][dt], acc_o[rt][dt], 0, 0, 0);
       }
-#pragma unroll
-      for (int r = 0; r < kAttnRows; ++r) {
-        if (r >= nr) continue;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const float p = k0 + u < nk ? pbuf[wave][r][k0 + u] : 0.f;
-#pragma unroll
-          for (int j = 0; j < DPL; ++j) o[r][j] = fmaf(p, vv[u][j], o[r][j]);
-        }
-      }
-    }
+    if (more) load_v(t + kAttnTile);
     // every lane has read the tile's probabilities before the next tile's
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // this wave's partial state
-  const size_t unit = (((size_t)b * a.Hkv + kvh) * a.RG + rg) * (size_t)(a.S * kAttnWaves) +
-                      (size_t)split * kAttnWaves + wave;
-  float* po = a.part_o + unit * kAttnRows * HD;
-  float* pml = a.part_ml + unit * kAttnRows * 2;
+  // merge the four waves' states in LDS (the loop buffers are free now),
+  // in wave order, and write one partial per work group: rows 16 rt + 4 g +
+  // j, dimension 16 dt + c
+  __syncthreads();
+  float* obuf = reinterpret_cast<float*>(smem);                 // [waves][ROWS][HD]
+  float* mlbuf = obuf + (size_t)kAttnWaves * ROWS * HD;         // [waves][ROWS][2]
 #pragma unroll
-  for (int r = 0; r < kAttnRows; ++r) {
-    if (r >= nr) continue;
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) po[r * HD + DPL * lane + j] = o[r][j];
-    if (lane == 0) { pml[2 * r] = m[r]; pml[2 * r + 1] = l[r]; }
+    for (int j = 0; j < 4; ++j) {
+      const int r = rt * 16 + 4 * g + j;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) obuf[((size_t)wave * ROWS + r) * HD + 16 * dt + c] = acc_o[rt][dt][j];
+      if (c == 0) {
+        mlbuf[(wave * ROWS + r) * 2] = m[rt][j];
+        mlbuf[(wave * ROWS + r) * 2 + 1] = l[rt][j];
+      }
+    }
+  __syncthreads();
+  const size_t unit = (((size_t)b * a.Hkv + kvh) * a.RG + rg) * (size_t)a.S + split;
+  float* po = a.part_o + unit * ROWS * HD;
+  float* pml = a.part_ml + unit * ROWS * 2;
+  for (int x = tid; x < nr * HD; x += kAttnThreads) {
+    const int r = x / HD, d = x - r * HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mlbuf[(w * ROWS + r) * 2]);
+    float o = 0.f, lsum = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float mw = mlbuf[(w * ROWS + r) * 2];
+        if (mw == -INFINITY) continue;
+        const float e = __expf(mw - M);
+        o += obuf[((size_t)w * ROWS + r) * HD + d] * e;
+        lsum += mlbuf[(w * ROWS + r) * 2 + 1] * e;
+      }
+    }
+    po[r * HD + d] = o;
+    if (d == 0) { pml[2 * r] = M; pml[2 * r + 1] = lsum; }
   }
 }
 
-// Merge the S * waves partial states of every query row in order: out =
+// Merge the S partial states of every query row in order: out =
 // sum_p o_p exp(m_p - M) / sum_p l_p exp(m_p - M), M the largest m_p.
 template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a) {
+__global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, int rows) {
   const int d = threadIdx.x, r = blockIdx.x, rg = blockIdx.y % a.RG, kvh = blockIdx.y / a.RG,
             b = blockIdx.z;
-  const int rr = rg * kAttnRows + r;
+  const int rr = rg * rows + r;
   if (rr >= a.R) return;
-  const int P = a.S * kAttnWaves;
+  const int P = a.S;
   const size_t unit0 = (((size_t)b * a.Hkv + kvh) * a.RG + rg) * (size_t)P;
   float M = -INFINITY;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, a.part_ml[((unit0 + p) * kAttnRows + r) * 2]);
+  for (int p = 0; p < P; ++p) M = fmaxf(M, a.part_ml[((unit0 + p) * rows + r) * 2]);
   float num = 0.f, den = 0.f;
   if (M > -INFINITY) {
     for (int p = 0; p < P; ++p) {
-      const float mp = a.part_ml[((unit0 + p) * kAttnRows + r) * 2];
+      const float mp = a.part_ml[((unit0 + p) * rows + r) * 2];
       if (mp == -INFINITY) continue;
       const float w = expf(mp - M);
-      den += a.part_ml[((unit0 + p) * kAttnRows + r) * 2 + 1] * w;
-      num += a.part_o[((unit0 + p) * kAttnRows + r) * HD + d] * w;
+      den += a.part_ml[((unit0 + p) * rows + r) * 2 + 1] * w;
+      num += a.part_o[((unit0 + p) * rows + r) * HD + d] * w;
     }
   }
   const int i = rr / a.G, h = kvh * a.G + rr % a.G;
@@ -231,36 +410,44 @@ __global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a) {
 
 // ---------------------------------------------------------------- commit
 // Tree commit: the accepted path's rows (node j = new row j + 1) gathered to
-// slots L + 1 .. L + n, for every KV head; all rows are read before any is
-// written.  One work group per (KV head, sequence).
+// slots L + 1 .. L + n, for every KV head: key rows ([slot][HD]) and value
+// columns ([HD][slot]); everything is read before anything is written.  One
+// work group per (KV head, sequence).
 template <int HD>
 __global__ __launch_bounds__(256) void k_kv_gather(int B, int n_new, int Hkv, int max_seq,
-                                                   uint16_t* k, uint16_t* v, const int* cache_len,
+                                                   uint16_t* k, uint16_t* vt, const int* cache_len,
                                                    const int* n_accepted, const int* path) {
-  __shared__ uint32_t rows[2][64][HD / 2];
+  __shared__ uint32_t krows[64][HD / 2];
+  __shared__ uint16_t vcols[64][HD];
   const int kvh = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int n = n_accepted[b];
   if (n <= 0 || n > n_new - 1) return;
   int L = cache_len[b];
   L = L < 0 ? 0 : (L > max_seq - n_new ? max_seq - n_new : L);
-  const size_t base = ((size_t)b * Hkv + kvh) * max_seq;
-  uint32_t* K32 = reinterpret_cast<uint32_t*>(k + base * HD);
-  uint32_t* V32 = reinterpret_cast<uint32_t*>(v + base * HD);
+  const size_t base = ((size_t)b * Hkv + kvh) * max_seq * HD;
+  uint32_t* K32 = reinterpret_cast<uint32_t*>(k + base);
+  uint16_t* VT = vt + base;
   constexpr int W = HD / 2;
+  auto node_of = [&](int kk) {
+    const int node = path[(size_t)b * (n_new - 1) + kk];
+    return node < 0 ? 0 : (node > n_new - 2 ? n_new - 2 : node);
+  };
   for (int x = tid; x < n * W; x += 256) {
-    const int kk = x / W, c = x - kk * W;
-    int node = path[(size_t)b * (n_new - 1) + kk];
-    node = node < 0 ? 0 : (node > n_new - 2 ? n_new - 2 : node);
-    const size_t src = (size_t)(L + 1 + node) * W + c;
-    rows[0][kk][c] = K32[src];
-    rows[1][kk][c] = V32[src];
+    const int kk = x / W, cc = x - kk * W;
+    krows[kk][cc] = K32[(size_t)(L + 1 + node_of(kk)) * W + cc];
+  }
+  for (int x = tid; x < n * HD; x += 256) {
+    const int kk = x % n, d = x / n;
+    vcols[kk][d] = VT[(size_t)d * max_seq + L + 1 + node_of(kk)];
   }
   __syncthreads();
   for (int x = tid; x < n * W; x += 256) {
-    const int kk = x / W, c = x - kk * W;
-    const size_t dst = (size_t)(L + 1 + kk) * W + c;
-    K32[dst] = rows[0][kk][c];
-    V32[dst] = rows[1][kk][c];
+    const int kk = x / W, cc = x - kk * W;
+    K32[(size_t)(L + 1 + kk) * W + cc] = krows[kk][cc];
+  }
+  for (int x = tid; x < n * HD; x += 256) {
+    const int kk = x % n, d = x / n;
+    VT[(size_t)d * max_seq + L + 1 + kk] = vcols[kk][d];
   }
 }
 
@@ -277,7 +464,7 @@ using namespace sv;
 namespace {
 
 struct AttnShape {
-  int R = 0, RG = 0, S = 0;
+  int R = 0, RT = 0, RG = 0, S = 0;
   size_t o_off = 0, ml_off = 0, total = 0;
 };
 
@@ -285,23 +472,29 @@ AttnShape attn_shape(int B, int n_new, int H, int Hkv, int hd, int max_seq) {
   AttnShape s;
   const int G = H / Hkv;
   s.R = n_new * G;
-  s.RG = (s.R + kAttnRows - 1) / kAttnRows;
-  // enough work groups to cover the CUs about four times over, each split
-  // at least one tile per wave
+  // row tiles per work group: all rows in one group up to 64 (every key and
+  // value byte read once for them), else groups of 64
+  s.RT = std::min(kAttnMaxRT, (s.R + 15) / 16);
+  s.RG = (s.R + 16 * s.RT - 1) / (16 * s.RT);
+  // splits of the keys: about 2048 waves over the chip, but at least two
+  // 64-key tiles per wave so a wave's partial state (16 RT x hd floats)
+  // stays small next to the keys and values it streamed
   const int groups = B * Hkv * s.RG;
-  const int want = (1024 + groups - 1) / groups;
-  const int most = std::max(1, max_seq / (kAttnTile * kAttnWaves));
+  const int tiles = (max_seq + kAttnTile - 1) / kAttnTile;
+  const int want = (2048 + groups * kAttnWaves - 1) / (groups * kAttnWaves);
+  const int most = std::max(1, tiles / (2 * kAttnWaves));
   s.S = std::max(1, std::min(want, most));
-  const size_t units = (size_t)groups * s.S * kAttnWaves;
+  const size_t units = (size_t)groups * s.S;
+  const size_t rows = (size_t)16 * s.RT;
   s.o_off = 0;
-  s.ml_off = (units * kAttnRows * hd * sizeof(float) + 255) & ~(size_t)255;
-  s.total = s.ml_off + ((units * kAttnRows * 2 * sizeof(float) + 255) & ~(size_t)255);
+  s.ml_off = (units * rows * hd * sizeof(float) + 255) & ~(size_t)255;
+  s.total = s.ml_off + ((units * rows * 2 * sizeof(float) + 255) & ~(size_t)255);
   return s;
 }
 
 bool attn_args_ok(int B, int n_new, int H, int Hkv, int hd, int max_seq) {
   return B >= 1 && n_new >= 1 && n_new <= 64 && Hkv >= 1 && H >= Hkv && H % Hkv == 0 &&
-         (hd == 64 || hd == 128) && max_seq >= n_new;
+         (hd == 64 || hd == 128) && max_seq >= n_new && max_seq >= 8 && max_seq % 8 == 0;
 }
 
 }  // namespace
@@ -331,20 +524,28 @@ spec_status spec_decode_attention(int32_t B, int32_t n_new, int32_t H, int32_t H
   AttnArgs a;
   a.B = B; a.n_new = n_new; a.H = H; a.Hkv = Hkv; a.G = H / Hkv; a.max_seq = max_seq;
   a.R = s.R; a.RG = s.RG; a.S = s.S;
-  a.q = q; a.k = k_cache; a.v = v_cache; a.cache_len = cache_len; a.parent = parent;
+  a.q = q; a.k = k_cache; a.vt = v_cache; a.cache_len = cache_len; a.parent = parent;
   a.scale = scale; a.out = out;
   a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.o_off);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.ml_off);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const dim3 grid(s.S, Hkv * s.RG, B);
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(k_decode_attn<128>, grid, dim3(kAttnThreads), 0, st, a);
-    hipLaunchKernelGGL(k_attn_combine<128>, dim3(kAttnRows, Hkv * s.RG, B), dim3(128), 0, st, a);
-  } else {
-    hipLaunchKernelGGL(k_decode_attn<64>, grid, dim3(kAttnThreads), 0, st, a);
-    hipLaunchKernelGGL(k_attn_combine<64>, dim3(kAttnRows, Hkv * s.RG, B), dim3(64), 0, st, a);
-  }
+  const dim3 grid(s.S, Hkv * s.RG, B), cgrid(16 * s.RT, Hkv * s.RG, B);
+  auto go = [&](auto hd_tag, auto rt_tag) {
+    constexpr int HDc = decltype(hd_tag)::value, RTc = decltype(rt_tag)::value;
+    hipLaunchKernelGGL((k_decode_attn<HDc, RTc>), grid, dim3(kAttnThreads), 0, st, a);
+    hipLaunchKernelGGL(k_attn_combine<HDc>, cgrid, dim3(HDc), 0, st, a, 16 * RTc);
+  };
+  auto by_rt = [&](auto hd_tag) {
+    switch (s.RT) {
+      case 1: go(hd_tag, std::integral_constant<int, 1>{}); break;
+      case 2: go(hd_tag, std::integral_constant<int, 2>{}); break;
+      case 3: go(hd_tag, std::integral_constant<int, 3>{}); break;
+      default: go(hd_tag, std::integral_constant<int, 4>{}); break;
+    }
+  };
+  if (head_dim == 128) by_rt(std::integral_constant<int, 128>{});
+  else by_rt(std::integral_constant<int, 64>{});
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
@@ -361,6 +562,7 @@ spec_status spec_kv_commit(int32_t B, int32_t n_new, int32_t Hkv, int32_t head_d
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (path && n_new > 1) {
+    if (max_seq % 8) return SPEC_EINVAL;
     if (head_dim == 128)
       hipLaunchKernelGGL(k_kv_gather<128>, dim3(Hkv, B), dim3(256), 0, st, B, n_new, Hkv, max_seq,
                          k_cache, v_cache, cache_len, n_accepted, path);
