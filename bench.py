@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the timed oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gemm", choices=("auto", "fma"), default="auto",
+                    help="fma: bf16 weights kept row-major and every GEMM on the vector-FMA "
+                         "kernel (a comparison of the two GEMM paths at the same shape)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--attention", action="store_true",
@@ -422,7 +425,8 @@ def main():
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
     model = synth.model_torch(key, wl.d, wl.ffn, wl.n_blocks, wl.V, wl.wdtype, "cuda")
-    w = sv.Weights(model["blocks"], model["lm_head"])
+    wkw = {"keep_rowmajor": True, "mfma_min_rows": 10 ** 6} if args.gemm == "fma" else {}
+    w = sv.Weights(model["blocks"], model["lm_head"], **wkw)
     progress(f"weights registered {time.perf_counter() - t_setup:.1f}s")
     host = None
     if not args.no_cpu_baseline:
@@ -485,12 +489,13 @@ def main():
     out = {
         "metric": METRIC, "value": passes_s, "unit": "verify passes/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": ms / K, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.wdtype, "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={B} gamma={gamma} d={wl.d} ffn={wl.ffn} "
                                f"blocks={wl.n_blocks} V={wl.V} {wl.wdtype} weights, "
                                f"T={T} top_p={top_p}",
                    "B": B, "gamma": gamma, "d": wl.d, "ffn": wl.ffn, "blocks": wl.n_blocks,
-                   "V": wl.V, "temperature": T, "top_p": top_p},
+                   "V": wl.V, "temperature": T, "top_p": top_p,
+                   "gemm_path": "vector FMA" if args.gemm == "fma" else "library default"},
         "accepted_tokens_per_s": tokens / (ms / 1e3),
         "mean_tokens_per_pass": tokens / (K * B),
         "hbm_gbs_whole_step": step_gbs,
