@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the timed oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--exact-split", action="store_true",
+                    help="register the weights with SPEC_FLAG_EXACT_SPLIT (three exact bf16 terms "
+                         "per activation in every pass; by default passes of 113 to 224 rows "
+                         "carry two)")
     ap.add_argument("--gemm", choices=("auto", "fma"), default="auto",
                     help="fma: bf16 weights kept row-major and every GEMM on the vector-FMA "
                          "kernel (a comparison of the two GEMM paths at the same shape)")
@@ -426,6 +430,8 @@ def main():
     t_setup = time.perf_counter()
     model = synth.model_torch(key, wl.d, wl.ffn, wl.n_blocks, wl.V, wl.wdtype, "cuda")
     wkw = {"keep_rowmajor": True, "mfma_min_rows": 10 ** 6} if args.gemm == "fma" else {}
+    if args.exact_split:
+        wkw["exact_split"] = True
     w = sv.Weights(model["blocks"], model["lm_head"], **wkw)
     progress(f"weights registered {time.perf_counter() - t_setup:.1f}s")
     host = None
@@ -495,7 +501,9 @@ def main():
                                f"T={T} top_p={top_p}",
                    "B": B, "gamma": gamma, "d": wl.d, "ffn": wl.ffn, "blocks": wl.n_blocks,
                    "V": wl.V, "temperature": T, "top_p": top_p,
-                   "gemm_path": "vector FMA" if args.gemm == "fma" else "library default"},
+                   "gemm_path": "vector FMA" if args.gemm == "fma" else "library default",
+                   "activation_terms": 2 if (not args.exact_split and wl.wdtype == "bf16"
+                                             and 113 <= B * G1 <= 224 and args.gemm == "auto") else 3},
         "accepted_tokens_per_s": tokens / (ms / 1e3),
         "mean_tokens_per_pass": tokens / (K * B),
         "hbm_gbs_whole_step": step_gbs,

@@ -15,8 +15,8 @@
  *
  *   d, ffn, n_blocks, vocab, wdtype   the target's shape, as in
  *                                     spec_weights_desc
- *   mfma_min_rows, keep_rowmajor      the description's mfma_min_rows and
- *                                     SPEC_FLAG_KEEP_ROWMAJOR (bf16 only)
+ *   mfma_min_rows, flags              the description's mfma_min_rows and
+ *                                     SPEC_FLAG_* flags (bf16 only)
  *   B, gamma                          the pass
  *   shrink_bytes                      0 in use; > 0 checks against workspace
  *                                     buffers that many bytes short (a
@@ -44,7 +44,7 @@ extern "C" {
 #endif
 
 spec_status spec_diag_access_check(int32_t d, int32_t ffn, int32_t n_blocks, int32_t vocab,
-                                   int32_t wdtype, int32_t mfma_min_rows, int32_t keep_rowmajor,
+                                   int32_t wdtype, int32_t mfma_min_rows, uint32_t flags,
                                    int32_t B, int32_t gamma, int32_t shrink_bytes, char* msg,
                                    size_t msg_len, int64_t* checks);
 

@@ -19,6 +19,7 @@ SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_ENOMEM, SPEC
 NOALLOC_SCRATCH_BYTES = 128 << 20
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_FLAG_KEEP_ROWMAJOR = 1
+SPEC_FLAG_EXACT_SPLIT = 2
 
 # Every symbol include/specverify.h declares.
 EXPORTS = ["spec_weights_create", "spec_weights_destroy", "spec_workspace_size", "spec_verify",
@@ -108,7 +109,8 @@ def load():
     lib.spec_profile_read.restype = i32
     lib.spec_stream_read.argtypes = [vp, sz, vp, vp]
     lib.spec_stream_read.restype = i32
-    lib.spec_diag_access_check.argtypes = [i32] * 10 + [ctypes.c_char_p, sz, ctypes.POINTER(ctypes.c_int64)]
+    lib.spec_diag_access_check.argtypes = [i32] * 6 + [ctypes.c_uint32] + [i32] * 3 + [
+        ctypes.c_char_p, sz, ctypes.POINTER(ctypes.c_int64)]
     lib.spec_diag_access_check.restype = i32
     _lib = lib
     return lib
@@ -148,7 +150,7 @@ class Weights:
     """
 
     def __init__(self, blocks, lm_head, eps=1e-6, keep_rowmajor=False, mfma_min_rows=0,
-                 stream=None):
+                 exact_split=False, stream=None):
         lib = load()
         dtype = lm_head.dtype
         if dtype not in (torch.float32, torch.bfloat16):
@@ -174,7 +176,7 @@ class Weights:
                      ctypes.cast(self._down, ctypes.POINTER(ctypes.c_void_p)),
                      ctypes.cast(self._gain, ctypes.POINTER(ctypes.c_void_p)) if self._gain is not None else None,
                      ctypes.c_void_p(lm_head.data_ptr()),
-                     SPEC_FLAG_KEEP_ROWMAJOR if keep_rowmajor else 0, int(mfma_min_rows))
+                     _flags(keep_rowmajor, exact_split), int(mfma_min_rows))
         handle = ctypes.c_void_p()
         _check(lib.spec_weights_create(ctypes.byref(desc), _stream(stream), ctypes.byref(handle)),
                "spec_weights_create")
@@ -443,13 +445,17 @@ def stream_read(src, sink, nbytes=None, stream=None):
            "spec_stream_read")
 
 
+def _flags(keep_rowmajor, exact_split):
+    return (SPEC_FLAG_KEEP_ROWMAJOR if keep_rowmajor else 0) | (SPEC_FLAG_EXACT_SPLIT if exact_split else 0)
+
+
 def access_check(d, ffn, n_blocks, vocab, wdtype, B, gamma, mfma_min_rows=0, keep_rowmajor=False,
-                 shrink_bytes=0):
+                 shrink_bytes=0, exact_split=False):
     """spec_diag_access_check: (status, message, ranges checked); host only."""
     buf = ctypes.create_string_buffer(512)
     n = ctypes.c_int64()
     st = load().spec_diag_access_check(int(d), int(ffn), int(n_blocks), int(vocab), int(wdtype),
-                                       int(mfma_min_rows), 1 if keep_rowmajor else 0, int(B),
+                                       int(mfma_min_rows), _flags(keep_rowmajor, exact_split), int(B),
                                        int(gamma), int(shrink_bytes), buf, 512, ctypes.byref(n))
     return st, buf.value.decode(), n.value
 

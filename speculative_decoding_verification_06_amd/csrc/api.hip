@@ -82,6 +82,15 @@ int gemm_path(const spec_weights* w, int M) {
   return (M >= w->mfma_min_rows || !have_rm) ? PATH_MFMA : PATH_FMA_BF16;
 }
 
+// Whether a pass of M rows carries its activations as two bf16 terms:
+// passes the wide GEMM serves from kTwoTermMinRows rows on, unless the
+// weights were registered with SPEC_FLAG_EXACT_SPLIT.  Every producer of
+// the pass splits alike.
+bool two_term(const spec_weights* w, int M, int path) {
+  return !(w->flags & SPEC_FLAG_EXACT_SPLIT) && path == PATH_MFMA && wide_rows(M) &&
+         M >= kTwoTermMinRows;
+}
+
 // Statistics units per logits row: one per LM-head work group (nt tiles of
 // 16 columns; the vector-FMA path covers 4 tiles per work group).
 int lm_units(const spec_weights* w, int M) {
@@ -101,7 +110,7 @@ size_t wide_part_bytes(const spec_weights* w, int M) {
   const int rows = M;
   size_t best = 0;
   auto one = [&](const Mat& m) {
-    const WidePlan p = plan_wide(rows, m);
+    const WidePlan p = plan_wide(rows, m, two_term(w, M, path));
     best = std::max(best, (size_t)p.S * rows * m.Np * sizeof(float));
   };
   for (const Mat& m : w->up) one(m);
@@ -200,6 +209,7 @@ spec_status register_matrix(spec_weights* w, const void* src, int K, int N, bool
 
 const void* mat_ptr(const Mat& m, int path) { return path == PATH_MFMA ? m.mfma : m.rowmajor; }
 
+
 // Events for timed launch idx (created on first use).
 hipError_t prof_events(spec_weights* w, size_t idx, hipEvent_t& e0, hipEvent_t& e1) {
   while (w->ev.size() < 2 * (idx + 1)) {
@@ -219,6 +229,7 @@ hipError_t prof_events(spec_weights* w, size_t idx, hipEvent_t& e0, hipEvent_t& 
 // launch carries a pair of events and its algorithmic weight bytes.
 hipError_t run_gemm(spec_weights* w, bool prof, int path, const Mat& W, const float* X,
                     const uint16_t* XS, int ldx, int M, EpiArgs e, float* part, hipStream_t st) {
+  const bool two = two_term(w, M, path);
   const int chunk = max_rows(path);
   // the packing and the kernel follow the whole pass's row count (stacked
   // and wide passes are one chunk)
@@ -244,6 +255,7 @@ hipError_t run_gemm(spec_weights* w, bool prof, int path, const Mat& W, const fl
     }
     if (e.xs) a.e.xs = e.xs + (size_t)(m0 / 16) * (e.xs_ks + 1) * 3 * 512;
     a.e.xs_stack = stack;
+    a.e.xs_two = two;
     a.e.row0 = m0;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (prof) {
@@ -252,7 +264,7 @@ hipError_t run_gemm(spec_weights* w, bool prof, int path, const Mat& W, const fl
     }
     hipError_t err;
     if (wide) {
-      const WidePlan wp = plan_wide(a.M, W);
+      const WidePlan wp = plan_wide(a.M, W, two);
       WideArgs wa;
       wa.XS = a.XS; wa.W = W.mfma; wa.M = a.M; wa.MT = wp.MT; wa.KS = a.KS;
       wa.nt = W.nt; wa.tiles = W.Np / kSub; wa.ks_slice = wp.ks_slice; wa.S = wp.S;
@@ -326,7 +338,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
   uint16_t* xsf = path == PATH_MFMA ? at<uint16_t>(ws, L.xsf) : nullptr;
 
   hipError_t err = launch_prep(h, xg, ss, ss_ld, hidden, w->n_blocks ? w->gain[0] : nullptr, M,
-                               w->d, L.ldd, xsd, L.ksd, xsf, L.ksf, st);
+                               w->d, L.ldd, xsd, L.ksd, xsf, L.ksf, two_term(w, M, path), st);
   for (int l = 0; l < w->n_blocks && err == hipSuccess; ++l) {
     EpiArgs up;
     up.kind = EPI_UP;
@@ -541,8 +553,9 @@ void check_wide(AccessCheck& C, const char* what, const WidePlan& p, const Mat& 
                 const Layout& L) {
   const int KS = W.Kp / kKStep, MT = p.MT, tiles = W.Np / kSub;
   const int threads = 64 * p.mg * p.cg;
-  const int cpt = (p.mtw * p.mg * 3 * 64 + threads - 1) / threads;
-  const int64_t nfrp = (int64_t)cpt * threads, nfr = (int64_t)MT * 192;
+  const int fr = p.terms * 64;   // chunks of a row tile's k-step the GEMM reads
+  const int cpt = (p.mtw * p.mg * fr + threads - 1) / threads;
+  const int64_t nfrp = (int64_t)cpt * threads, nfr = (int64_t)MT * fr;
   const int64_t wcap = (int64_t)W.Kp * W.Np / 8;
   C.range(what, "LDS activation tiles", 0, 2 * nfrp - 1, (int64_t)p.lds / 16);
   for (int by = 0; by < p.S; ++by) {
@@ -551,7 +564,7 @@ void check_wide(AccessCheck& C, const char* what, const WidePlan& p, const Mat& 
     for (int tid = 0; tid < threads; tid += threads - 1)
       for (int i = 0; i < cpt; ++i) {
         const int64_t cc = std::min<int64_t>(tid + (int64_t)i * threads, nfr - 1);
-        const int64_t mt = cc / 192, rem = cc - mt * 192;
+        const int64_t mt = cc / fr, rem = cc - mt * fr;
         const int64_t base = mt * (KS + 1) * 192 + rem;
         C.range(what, xs_name, base + (int64_t)s0 * 192, base + (int64_t)KS * 192, xs_cap);
       }
@@ -652,7 +665,8 @@ spec_status access_check_pass(const spec_weights* w, int B, int gamma, int shrin
                   in_ffn ? "act" : (kind == EPI_LM ? "h" : "xg"), (int64_t)m0 * ldx, e, c, L, m0);
       } else if (wide) {
         e.nt = kGroupCols / kSub;
-        check_wide(C, what, plan_wide(Mc, W), W, Mc, xs_name, xs_cap / 8, e, c, L);
+        check_wide(C, what, plan_wide(Mc, W, two_term(w, M, path)), W, Mc, xs_name, xs_cap / 8, e, c,
+                   L);
       } else {
         const GemmPlan p = plan_gemm(path, Mc, W, stack);
         e.nt = p.nt;
@@ -818,7 +832,7 @@ spec_status spec_verify_debug(spec_weights_t w, int32_t B, int32_t gamma, const 
 }
 
 spec_status spec_diag_access_check(int32_t d, int32_t ffn, int32_t n_blocks, int32_t vocab,
-                                   int32_t wdtype, int32_t mfma_min_rows, int32_t keep_rowmajor,
+                                   int32_t wdtype, int32_t mfma_min_rows, uint32_t flags,
                                    int32_t B, int32_t gamma, int32_t shrink_bytes, char* msg,
                                    size_t msg_len, int64_t* checks) {
   if (msg && msg_len) msg[0] = 0;
@@ -828,12 +842,12 @@ spec_status spec_diag_access_check(int32_t d, int32_t ffn, int32_t n_blocks, int
   if (wdtype != SPEC_F32 && wdtype != SPEC_BF16) return SPEC_EDTYPE;
   // shapes only: no device memory is touched
   spec_weights w;
-  w.d = d; w.ffn = ffn; w.n_blocks = n_blocks; w.V = vocab; w.wdtype = wdtype;
+  w.d = d; w.ffn = ffn; w.n_blocks = n_blocks; w.V = vocab; w.wdtype = wdtype; w.flags = flags;
   w.mfma_min_rows = mfma_min_rows > 0 ? mfma_min_rows : kDefaultMfmaMinRows;
   auto shape = [&](Mat& m, int K, int N) {
     m.K = K; m.N = N; m.Kp = roundup(K, kKStep); m.Np = roundup(N, kGroupCols);
     if (wdtype == SPEC_BF16) m.nt = mfma_block_tiles(m.Np);
-    if (wdtype == SPEC_BF16 && (keep_rowmajor || w.mfma_min_rows > 1))
+    if (wdtype == SPEC_BF16 && ((flags & SPEC_FLAG_KEEP_ROWMAJOR) || w.mfma_min_rows > 1))
       m.rowmajor = reinterpret_cast<void*>(uintptr_t{256});   // marks a row-major copy; never read
   };
   w.up.resize(n_blocks);

@@ -43,6 +43,19 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid
   lo = __float_as_uint(r2) >> 16;
 }
 
+// Two-term split, both terms rounded to nearest even: |x - hi| <= 2^-8 |x|,
+// so x - hi is exact in fp32 (hi lies within a factor of two of x), and
+// lo = bf16(x - hi) leaves |x - hi - lo| <= 2^-16 |x|.  Finite x only.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u;
+}
+__device__ __forceinline__ void split2_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  const uint32_t b0 = bf16_rne_bits(x);
+  hi = b0 >> 16;
+  lo = bf16_rne_bits(x - __uint_as_float(b0)) >> 16;
+}
+
 // Split activations in MFMA A-operand order.  For a GEMM input X[M][K]
 // with KS k-steps of 32 (step KS is all zero), one 1 KiB fragment holds 64
 // lanes x 8 bf16, lane L holding A-rows L % 16 at columns
@@ -53,6 +66,8 @@ __device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid
 //             A-row 5 p + r holds term p of row 5 mt + r (A-row 15 unused),
 //             so a single MFMA covers every term of five rows and the
 //             terms are summed after the k-loop
+// With the two-term split (plain packing only) the third fragment holds
+// zeros, so a three-term reader of the buffer computes hi + lo.
 // xs_index returns the bf16 index of term 0 of (row, col); term p sits at
 // +p * xs_term_step(stacked).  Both are host functions too, so the host-side
 // access check evaluates the very formulas the kernels use.
@@ -68,9 +83,10 @@ __host__ __device__ __forceinline__ size_t xs_index(int row, int col, int ks, bo
   return (frag * 64 + lane_hi + (row & 15)) * 8 + j;
 }
 __device__ __forceinline__ void xs_store(uint16_t* xs, int row, int col, int ks, bool stacked,
-                                         float x) {
-  uint32_t a, b, c;
-  split3_bf16(x, a, b, c);
+                                         bool two, float x) {
+  uint32_t a, b, c = 0;
+  if (two) split2_bf16(x, a, b);
+  else split3_bf16(x, a, b, c);
   const size_t i = xs_index(row, col, ks, stacked);
   const int st = xs_term_step(stacked);
   xs[i] = (uint16_t)a;

@@ -251,7 +251,7 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
     if (e.kind == EPI_UP) {
       const float y = x.valid ? silu(v * sh_inv[x.r]) : 0.f;
       if (x.live && !e.xs) e.out[x.o] = y;   // the MFMA path reads only the split copy
-      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, e.xs_stack, y);
+      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, e.xs_stack, e.xs_two, y);
     } else if (e.kind == EPI_DOWN) {
       float hn = 0.f;
       if (x.valid) hn = (pre ? p0 : e.out[x.o]) + v;
@@ -263,7 +263,7 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
         const float sq = sum16(hn * hn);
         if (x.live && c == 0) e.ss_out[(size_t)x.r * e.ss_ld + x.tile] = sq;
       }
-      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, e.xs_stack, y);
+      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, e.xs_stack, e.xs_two, y);
     } else {
       if (x.valid && e.out) e.out[x.o] = v;   // no logits buffer: greedy, no debug copy
       const float qv = pre ? p0 : lm_item_q(e, x);
@@ -762,7 +762,7 @@ __device__ __forceinline__ void wide_lm_epilogue2(const EpiArgs& e, const f32x4 
 
 // ---------------------------------------------------------------- wide MFMA GEMM
 // Many rows (plain packing, 11 to 224 rows): the split activations of a
-// k-step, MT row tiles x 3 terms, are staged once per work group in LDS and
+// k-step, MT row tiles x TERMS terms, are staged once per work group in LDS and
 // shared by the group's 16 column tiles (256 columns), instead of being
 // read from L2 by every 16-column tile.  MG x CG waves: row groups of MTW
 // tiles times column groups of NTC tiles.  A fragments are loaded ahead
@@ -770,8 +770,10 @@ __device__ __forceinline__ void wide_lm_epilogue2(const EpiArgs& e, const f32x4 
 // row tile at a time with ds_read_b128; weights stream into a register
 // ring.  When the column blocks cannot fill the chip, K is split over
 // blockIdx.y and the slices are summed, in slice order, by k_epi_wide.
+// TERMS: the bf16 terms of each activation read (3, or 2 with the
+// two-term split, whose third fragment is zero and skipped).
 // Output: fp32 partial sums P[slice][row][col].
-template <int MTW, int NTC, int MG, int CG, int RING>
+template <int MTW, int NTC, int MG, int CG, int RING, int TERMS>
 __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs e) {
   // Load vmcnt completes in issue order, so waiting for the activations of
   // the next k-step also waits for every weight load issued before them:
@@ -789,7 +791,8 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs 
   constexpr bool kEarlyStore = ASETS >= 2 && MG == 2;
   static_assert(kWideRing % 2 == 0 && kWideRing % ASETS == 0, "ring slots must map to fixed A sets");
   constexpr int NW = MG * CG, THREADS = 64 * NW;
-  constexpr int CPT = (MTW * MG * 3 * 64 + THREADS - 1) / THREADS;   // A chunks per thread
+  static_assert(TERMS == 2 || TERMS == 3, "two or three activation terms");
+  constexpr int CPT = (MTW * MG * TERMS * 64 + THREADS - 1) / THREADS;   // A chunks per thread
   extern __shared__ bf16x8 lds_a[];                                   // [2][NFRP]
   const int lane = threadIdx.x & 63, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -798,7 +801,7 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs 
   const int s0 = blockIdx.y * a.ks_slice;
   const int s1 = min(KS, s0 + a.ks_slice);
   const int nsteps = s1 - s0;
-  const int nfr = MT * 3 * 64;
+  const int nfr = MT * TERMS * 64;
   const bf16x8* XS = reinterpret_cast<const bf16x8*>(a.XS);
   const bf16x8* W = reinterpret_cast<const bf16x8*>(a.W);
   // UP: 1 / rms of every row once per pass, for k_epi_wide (slice 0's work
@@ -832,15 +835,17 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs 
 
   bf16x8 areg[ASETS][CPT];
   bf16x8 bq[kWideRing][NTC];
-  // chunk c of a k-step: fragment (mt, p) = (c / 192, c / 64 % 3), lane
-  // c % 64.  The LDS tile is padded to CPT * THREADS chunks so the copy has
-  // no per-thread branch; chunks past the real ones copy the last real one.
+  // chunk c of a k-step: fragment (mt, p) = (c / (64 TERMS), c / 64 %
+  // TERMS), lane c % 64; a row tile's k-step spans three fragments in
+  // memory whatever TERMS is.  The LDS tile is padded to CPT * THREADS
+  // chunks so the copy has no per-thread branch; chunks past the real ones
+  // copy the last real one.
   constexpr int NFRP = CPT * THREADS;
   const bf16x8* asrc[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = min(tid + i * THREADS, nfr - 1);
-    const int mt = c / 192, rem = c - mt * 192;
+    const int mt = c / (TERMS * 64), rem = c - mt * (TERMS * 64);
     asrc[i] = XS + (size_t)mt * (KS + 1) * 192 + rem;
   }
   auto load_a = [&](int set, int s) {
@@ -887,22 +892,22 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs 
         // Tiles past MT repeat the last tile (no branch in the MFMA
         // stream); their rows are never stored.
         const bf16x8* abuf = lds_a + (u & 1) * NFRP + lane;
-        bf16x8 af[2][3];
+        bf16x8 af[2][TERMS];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) af[0][p] = abuf[(min(mg * MTW, MT - 1) * 3 + p) * 64];
+        for (int p = 0; p < TERMS; ++p) af[0][p] = abuf[(min(mg * MTW, MT - 1) * TERMS + p) * 64];
 #pragma unroll
         for (int i = 0; i < MTW; ++i) {
           if (i + 1 < MTW) {
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
-              af[(i + 1) & 1][p] = abuf[(min(mg * MTW + i + 1, MT - 1) * 3 + p) * 64];
+            for (int p = 0; p < TERMS; ++p)
+              af[(i + 1) & 1][p] = abuf[(min(mg * MTW + i + 1, MT - 1) * TERMS + p) * 64];
           }
           // Two row groups: the two waves of a SIMD (one per row group)
           // share the MFMA pipe; the one inside a tile's MFMA run keeps
           // issue priority until the run ends (measured +0.7% greedy).
           if constexpr (MG == 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-          for (int p = 0; p < 3; ++p)
+          for (int p = 0; p < TERMS; ++p)
 #pragma unroll
             for (int t = 0; t < NTC; ++t)
               acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i & 1][p], bq[u][t], acc[i][t], 0, 0, 0);
@@ -1156,9 +1161,10 @@ GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack) {
   return p;
 }
 
-WidePlan plan_wide(int M, const Mat& m) {
+WidePlan plan_wide(int M, const Mat& m, bool two_term) {
   WidePlan p;
   p.MT = (M + 15) / 16;
+  p.terms = two_term && M >= kTwoTermMinRows ? 2 : 3;
   // two row groups x 4 column groups of 4 tiles = 16 column tiles, 8 waves
   p.mtw = (p.MT + 1) / 2;
   p.mg = 2; p.ntc = 4; p.cg = 4;
@@ -1208,20 +1214,20 @@ WidePlan plan_wide(int M, const Mat& m) {
   p.ks_slice = (KS + S - 1) / S;
   p.S = (KS + p.ks_slice - 1) / p.ks_slice;
   const int threads = 64 * p.mg * p.cg;
-  const int cpt = (p.mtw * p.mg * 3 * 64 + threads - 1) / threads;
+  const int cpt = (p.mtw * p.mg * p.terms * 64 + threads - 1) / threads;
   p.lds = (size_t)2 * cpt * threads * 16;
   return p;
 }
 
-template <int MTW, int NTC, int MG, int CG, int RING = (MTW >= 5 ? 2 : 4)>
+template <int MTW, int NTC, int MG, int CG, int RING = (MTW >= 5 ? 2 : 4), int TERMS = 3>
 static void launch_wide_t(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
                           hipEvent_t e0, hipEvent_t e1) {
   // the double-buffered activation tile can exceed the default 64 KiB
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_gemm_wide<MTW, NTC, MG, CG, RING>),
+      reinterpret_cast<const void*>(&k_gemm_wide<MTW, NTC, MG, CG, RING, TERMS>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
   (void)attr;
-  hipExtLaunchKernelGGL((k_gemm_wide<MTW, NTC, MG, CG, RING>), dim3(p.colblocks, p.S),
+  hipExtLaunchKernelGGL((k_gemm_wide<MTW, NTC, MG, CG, RING, TERMS>), dim3(p.colblocks, p.S),
                         dim3(64 * MG * CG), p.lds, st, e0, e1, 0, a, e);
 }
 
@@ -1251,6 +1257,13 @@ hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e
         if (p.colblocks * p.S > SV_MIN_BLOCKS) launch_wide_t<5, 2, 1, 8, 2>(p, a, e, st, e0, e1);
         else launch_wide_t<5, 2, 1, 8, 4>(p, a, e, st, e0, e1);
         break;
+    }
+  } else if (p.terms == 2) {
+    switch (p.mtw) {   // 113 to 224 rows: 8 to 14 row tiles, mtw = 4 .. 7
+    case 4: launch_wide_t<4, 4, 2, 4, 4, 2>(p, a, e, st, e0, e1); break;
+    case 5: launch_wide_t<5, 4, 2, 4, 2, 2>(p, a, e, st, e0, e1); break;
+    case 6: launch_wide_t<6, 4, 2, 4, 2, 2>(p, a, e, st, e0, e1); break;
+    default: launch_wide_t<7, 4, 2, 4, 2, 2>(p, a, e, st, e0, e1); break;
     }
   } else {
     switch (p.mtw) {   // 6 to 14 row tiles: mtw = 3 .. 7

@@ -69,6 +69,7 @@ struct EpiArgs {
   uint16_t* xs = nullptr;
   int xs_ks = 0;
   bool xs_stack = false;      // stacked packing (xs_index)
+  bool xs_two = false;        // two-term split (split2_bf16), plain packing
 };
 
 struct GemmArgs {
@@ -112,6 +113,7 @@ GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack);
 // alone cannot fill the chip.
 struct WidePlan {
   int MT = 0, mtw = 0, ntc = 0, mg = 0, cg = 0;
+  int terms = 3;              // bf16 terms per activation the GEMM reads
   int colblocks = 0, S = 1, ks_slice = 0;
   size_t lds = 0;
 };
@@ -127,7 +129,10 @@ struct WideArgs {
   bool fuse_lm = false;       // LM head in one slice: the GEMM writes the
                               // logits and unit statistics, P is unused
 };
-WidePlan plan_wide(int M, const Mat& m);
+WidePlan plan_wide(int M, const Mat& m, bool two_term);
+// Wide passes of at least this many rows take the two-term split unless
+// SPEC_FLAG_EXACT_SPLIT: the wide GEMM is bound by its matrix operations there.
+constexpr int kTwoTermMinRows = 113;
 // Row counts the wide GEMM serves: the plain packing up to one 224-row chunk.
 inline bool wide_rows(int M) { return !xs_stacked(M) && M <= 224; }
 // The GEMM (timed by e0 / e1 when given) and then its epilogue kernel; an
@@ -161,10 +166,10 @@ struct SampleArgs {
 // squares; with xs0 non-null also writes the first GEMM's split input (xg,
 // or h when there is no MLP block) and clears the zero k-step of each of
 // the split buffers xs0 (ks0 k-steps) and xs1 (ks1 k-steps), packed as
-// xs_stacked(M) says.
+// xs_stacked(M) says, in two terms when `two`.
 hipError_t launch_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
                        const float* gain0, int M, int d, int ld, uint16_t* xs0, int ks0,
-                       uint16_t* xs1, int ks1, hipStream_t st);
+                       uint16_t* xs1, int ks1, bool two, hipStream_t st);
 hipError_t launch_tile_stats(const SampleArgs& a, hipStream_t st);
 hipError_t launch_sampling(const SampleArgs& a, hipStream_t st);
 hipError_t launch_dump_probs(const SampleArgs& a, hipStream_t st);

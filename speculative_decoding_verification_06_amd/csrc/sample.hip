@@ -72,7 +72,7 @@ __device__ __forceinline__ void clear_zero_step(uint16_t* xs, int mt, int ks, in
 
 __global__ void k_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
                        const float* gain0, int d, int ld, uint16_t* xs0, int ks0, uint16_t* xs1,
-                       int ks1, bool stacked) {
+                       int ks1, bool stacked, bool two) {
   const int lane = threadIdx.x, g = blockIdx.x, m = blockIdx.y;
   const int n = g * kGroupCols + lane;
   const float v = n < d ? hidden[(size_t)m * d + n] : 0.f;
@@ -85,7 +85,7 @@ __global__ void k_prep(float* h, float* xg, float* ss, int ss_ld, const float* h
     if ((lane & 15) == 0) ss[(size_t)m * ss_ld + g * 4 + (lane >> 4)] = sq;
   }
   if (xs0) {
-    if (n < kKStep * ks0) xs_store(xs0, m, n, ks0, stacked, x);
+    if (n < kKStep * ks0) xs_store(xs0, m, n, ks0, stacked, two, x);
     const int rpt = stacked ? kStackRows : 16, fpt = stacked ? 1 : 3;
     if (g == 0 && m * rpt < gridDim.y) {
       clear_zero_step(xs0, m, ks0, fpt, lane);
@@ -96,9 +96,9 @@ __global__ void k_prep(float* h, float* xg, float* ss, int ss_ld, const float* h
 
 hipError_t launch_prep(float* h, float* xg, float* ss, int ss_ld, const float* hidden,
                        const float* gain0, int M, int d, int ld, uint16_t* xs0, int ks0,
-                       uint16_t* xs1, int ks1, hipStream_t st) {
+                       uint16_t* xs1, int ks1, bool two, hipStream_t st) {
   hipLaunchKernelGGL(k_prep, dim3(ld / kGroupCols, M), dim3(kWave), 0, st, h, xg, ss, ss_ld,
-                     hidden, gain0, d, ld, xs0, ks0, xs1, ks1, xs_stacked(M));
+                     hidden, gain0, d, ld, xs0, ks0, xs1, ks1, xs_stacked(M), two);
   return hipGetLastError();
 }
 

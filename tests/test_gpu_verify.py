@@ -12,8 +12,9 @@ import torch
 
 import oracle
 import synth
-from harness import (LOGIT_TOL, assert_tokens_match, cap_applies, compare_probs, compare_tokens,
-                     draft_q, greedy_drafts, log_measurement, logits_rel_err, sample_drafts)
+from harness import (LOGIT_TOL, LOGIT_TOL_TWO, assert_tokens_match, cap_applies, compare_probs,
+                     compare_tokens, two_term_pass, draft_q, greedy_drafts, log_measurement, logits_rel_err,
+                     sample_drafts)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +58,7 @@ def run_gpu(w, hidden, draft, q, T, top_p, seed):
     return cpu(n), cpu(e), cpu(logits), cpu(p), cpu(qq)
 
 
-def check(m, hidden, ell, q, draft, T, top_p, seed, w, what):
+def check(m, hidden, ell, q, draft, T, top_p, seed, w, what, two_term=False):
     n, e, logits, p, qq = run_gpu(w, hidden, draft, q, T, top_p, seed)
     # the plain call (what the benchmark times) decides exactly as the debug call
     n2, e2 = sv.verify(w, dev(hidden), dev(draft), dev(q) if T > 0 else None, T, top_p, seed)
@@ -67,11 +68,13 @@ def check(m, hidden, ell, q, draft, T, top_p, seed, w, what):
     log_measurement({"what": f"{what} logits", "rel_err_max": float(err.max())})
     assert err.max() <= 1e-3, f"{what}: logits rel err {err.max():.2e}"
     # the token comparison below assumes the logits this close
-    assert err.max() <= LOGIT_TOL, f"{what}: logits rel err {err.max():.2e}"
-    ref = oracle.spec_verify_from_logits(ell, draft, q, T, top_p, seed, logit_tol=LOGIT_TOL)
-    assert_tokens_match(n, e, ref, what=what, cap=cap_applies(ell.shape[-1], top_p, False))
+    tol = LOGIT_TOL_TWO if two_term else LOGIT_TOL
+    assert err.max() <= tol, f"{what}: logits rel err {err.max():.2e}"
+    ref = oracle.spec_verify_from_logits(ell, draft, q, T, top_p, seed, logit_tol=tol)
+    assert_tokens_match(n, e, ref, what=what,
+                        cap=not two_term and cap_applies(ell.shape[-1], top_p, False))
     if T > 0:
-        compare_probs(p, qq, ref, ell, q, T, top_p, range(len(n)), what, LOGIT_TOL)
+        compare_probs(p, qq, ref, ell, q, T, top_p, range(len(n)), what, tol)
     return err.max()
 
 
@@ -94,6 +97,15 @@ CASES = [
     # row groups of 5 and of 6 row tiles (129 and 161 rows)
     ("bf16-wide-129-rows", 1, 128, 192, 320, 650, 2, "bf16", 0.8, 0.9, True, {}),
     ("bf16-wide-161-rows", 1, 160, 128, 256, 700, 1, "bf16", 1.0, 1.0, False, {}),
+    # the exact three-term split kept from 113 rows on (SPEC_FLAG_EXACT_SPLIT;
+    # the two cases above take two terms): 224 rows greedy, 129 rows sampled
+    # with top-p, and 90 rows, where the flag changes nothing
+    ("bf16-wide-224-greedy-exact", 32, 6, 160, 288, 700, 1, "bf16", 0.0, 1.0, False,
+     {"exact_split": True}),
+    ("bf16-wide-129-rows-exact", 1, 128, 192, 320, 650, 2, "bf16", 0.8, 0.9, True,
+     {"exact_split": True}),
+    ("bf16-wide-90-rows-exact-flag", 10, 8, 128, 256, 600, 1, "bf16", 1.0, 1.0, False,
+     {"exact_split": True}),
     # LM heads of more than 4096 tiles at up to 80 rows: the 1024-thread
     # one-row-group shape (18 rows, sampling with top-p; 16 rows, greedy)
     ("bf16-wide-lm-1024", 3, 5, 128, 192, 70000, 1, "bf16", 0.9, 0.95, False, {}),
@@ -119,8 +131,17 @@ def test_verify_parity_small(case):
     m, hidden, ell, q, draft = make_case(key, B, gamma, d, ffn, V, nb, wdtype, T, top_p, gains=gains)
     blocks, lm = host_to_torch_weights(m, wdtype)
     w = sv.Weights(blocks, lm, eps=m["eps"], **wkw)
+    M = B * (gamma + 1)
+    two = two_term_pass(M, wdtype, wkw.get("exact_split", False), "mfma_min_rows" in wkw)
     for seed in (0, 1, 12345):
-        check(m, hidden, ell, q, draft, T, top_p, seed, w, f"{name} seed {seed}")
+        check(m, hidden, ell, q, draft, T, top_p, seed, w, f"{name} seed {seed}", two_term=two)
+    if wkw.get("exact_split") and not two_term_pass(M, wdtype):
+        # where the default takes three terms the flag leaves the pass as it is
+        w3 = sv.Weights(blocks, lm, eps=m["eps"])
+        for a, b in zip(run_gpu(w, hidden, draft, q, T, top_p, 7),
+                        run_gpu(w3, hidden, draft, q, T, top_p, 7)):
+            assert np.array_equal(a, b)
+        w3.close()
     w.close()
 
 
