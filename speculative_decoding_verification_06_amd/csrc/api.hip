@@ -64,7 +64,7 @@ namespace {
 constexpr int kDefaultMfmaMinRows = 1;
 constexpr int kMaxGamma = 4096;
 constexpr int kMaxRowsMfma = 224;
-constexpr int kMaxRowsFma = 192;
+constexpr int kMaxRowsFma = 160;   // LDS: 160 result rows and 8 waves' sums within 64 KiB
 
 inline int roundup(int x, int m) { return (x + m - 1) / m * m; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -609,7 +609,8 @@ void check_fma(AccessCheck& C, const char* what, const GemmPlan& p, const Mat& W
   C.range(what, x_name, x_off, x_off + (int64_t)(M - 1) * ldx + Kp - 1, x_cap);
   C.range(what, "weights (row-major)", 0, (int64_t)(p.blocks - 1) * kGroupCols + 63 + (int64_t)(Kp - 1) * W.Np,
           (int64_t)Kp * W.Np);
-  C.range(what, "LDS", 0, (int64_t)M * (kGroupCols + 1) + 32 * (kGroupCols + 1) - 1, (int64_t)p.lds / 4);
+  C.range(what, "LDS", 0, (int64_t)M * (kGroupCols + 1) + kFmaWaves * 8 * (kGroupCols + 1) - 1,
+          (int64_t)p.lds / 4);
   check_epilogue(C, what, e, c, L, row0, M, 0, 4);
   check_epilogue(C, what, e, c, L, row0, M, (p.blocks - 1) * 4, p.blocks * 4);
 }

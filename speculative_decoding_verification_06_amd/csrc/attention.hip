@@ -18,12 +18,14 @@
 // every key and value byte of a split is read once for all query rows of
 // the group (the weight-streaming idea of the GEMMs, applied to the cache).
 // Both products run on bf16 MFMA (16x16x32): the queries are split once
-// into three bf16 terms (exact) and staged in LDS as A fragments; the keys
-// are B fragments loaded straight from the cache; the scores' softmax runs
-// on the accumulators (a row's 64 scores sit in one 16-lane group x 4
-// tiles); the probabilities go through LDS into the A layout, split into
-// two terms (2^-16 relative), against value fragments loaded straight from
-// the head-dimension-major value cache.  Online softmax per row; the four
+// into three bf16 terms (exact) and staged in LDS as fragments; the key
+// fragments are loaded straight from the cache; the products are taken
+// transposed (S^T = K Q^T, O^T = V^T P^T), so the scores' softmax runs on
+// the accumulators with each lane owning one query row per row tile (16 of
+// its 64 scores of a key tile in registers, the rest in three other
+// lanes); the probabilities go through LDS into the operand layout, split
+// into two terms (2^-16 relative), against value fragments loaded straight
+// from the head-dimension-major value cache.  Online softmax per row; the four
 // waves' states are merged in LDS and every work group writes one partial
 // (max, sum, unnormalised output); a second kernel merges the splits'
 // partials in a fixed order, so results are run-to-run identical.  The softmax uses the hardware exp (relative error about
@@ -47,6 +49,12 @@ constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kAttnMaxRT = 4;      // 16-row MFMA tiles of query rows per work group (at most)
 constexpr int kAttnTile = 64;      // keys per wave tile: four 16-key MFMA tiles
+#ifndef SV_ATTN_WAVES
+#define SV_ATTN_WAVES 1024         // waves a launch aims for (splits of the keys)
+#endif
+#ifndef SV_ATTN_MIN_TILES
+#define SV_ATTN_MIN_TILES 2        // fewest 64-key tiles per wave
+#endif
 
 struct AttnArgs {
   int B, n_new, H, Hkv, G, max_seq, R, RG, S;   // R = n_new * G rows, RG row groups, S splits
@@ -187,18 +195,25 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   const uint16_t* Vt = a.vt + ((size_t)b * a.Hkv + kvh) * (size_t)HD * a.max_seq;
   const int g = lane >> 4, c = lane & 15;          // C layout: rows 4 g + j, column c
 
-  // per row this lane holds (tile rt, j): running max, sum; new-row index
-  float m[RT][4], l[RT][4];
-  int rowi[RT][4];
+  // Both products are taken transposed, S^T = K Q^T and O^T = V^T P^T, so
+  // that in the MFMA output layout (lane (g, c) holds rows 4 g + j of column
+  // c) a lane owns one query row per row tile: query 16 rt + c, at keys
+  // 4 g + j of each 16-key tile (scores) and dimensions 16 dt + 4 g + j
+  // (output).  A row's 64 scores of a tile are then 16 values in a lane and
+  // one value in each of the four lanes c, c + 16, c + 32, c + 48: its max
+  // and sum take two cross-lane steps, and its rescale of the output is the
+  // lane's own factor.  The fragments are the same registers either way:
+  // the key and value fragments serve as A operands, the query and
+  // probability fragments as B operands.
+  float m[RT], l[RT];
+  int rowi[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      m[rt][j] = -INFINITY;
-      l[rt][j] = 0.f;
-      const int r = rt * 16 + 4 * g + j;
-      rowi[rt][j] = r < nr ? (r0 + r) / a.G : -1;
-    }
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = -INFINITY;
+    l[rt] = 0.f;
+    const int r = rt * 16 + c;
+    rowi[rt] = r < nr ? (r0 + r) / a.G : -1;
+  }
   f32x4 acc_o[RT][DT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -219,17 +234,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   };
   // value fragments: k-step kv (32 keys), dimension tile dt: lane holds
   // dimension 16 dt + c at keys t + 32 kv + 8 g .. + 7 (16 bytes of the
-  // head-dimension-major value row); keys past w1 are zeroed
+  // head-dimension-major value row); in the wave's last tile the keys past
+  // w1 are zeroed (the tile test is uniform over the wave)
   bf16x8 vf[2][DT];
   auto load_v = [&](int t) {
+    const bool tail = t + kAttnTile > w1;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       const int k0 = t + 32 * kv + 8 * g;
       const int kl = min(k0, a.max_seq - 8);       // in bounds; the values past w1 are zeroed
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        vf[kv][dt] = zero_past(*reinterpret_cast<const bf16x8*>(Vt + (size_t)(16 * dt + c) * a.max_seq + kl),
-                               kl, w1);
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 f = *reinterpret_cast<const bf16x8*>(Vt + (size_t)(16 * dt + c) * a.max_seq + kl);
+        vf[kv][dt] = tail ? zero_past(f, kl, w1) : f;
+      }
     }
   };
   // The loads rotate through the tiles: a tile's keys are consumed by the
@@ -242,7 +260,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   }
   for (int t = w0; t < w1; t += kAttnTile) {
     const bool more = t + kAttnTile < w1;
-    // scores S[row][key] for the two row tiles and four key tiles
+    // scores S^T[key][row] for the four key tiles and RT row tiles
     f32x4 acc_s[RT][4];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -254,69 +272,76 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
       for (int p = 0; p < 3; ++p)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const bf16x8 qa = qf[rt][ks][p][lane];
+          const bf16x8 qb = qf[rt][ks][p][lane];
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
-            acc_s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[kt][ks], acc_s[rt][kt], 0, 0, 0);
+            acc_s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][ks], qb, acc_s[rt][kt], 0, 0, 0);
         }
     if (more) load_k(t + kAttnTile);
-    // mask and online softmax per row: a row's 64 scores sit in its lane
-    // group's 16 lanes x 4 key tiles.  A tile wholly inside this wave's
+    // mask and online softmax per row.  A tile wholly inside this wave's
     // committed keys is visible to every row (no mask work).
     const bool plain = t + kAttnTile <= min(L, w1);
     bool moved = false;                              // some row's running max rose
-    float corr[RT][4];
+    float corr[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+      const int i = rowi[rt];
+      const uint64_t vis_new = i >= 0 ? anc[i] : 0ull;
+      float sv[4][4];
+      float mt = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = rowi[rt][j];
-        const uint64_t vis_new = i >= 0 ? anc[i] : 0ull;
-        float sv[4];
-        float mt = -INFINITY;
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int j = 0; j < 4; ++j) {
           bool vis = i >= 0;
           if (!plain) {
-            const int key = t + 16 * kt + c, jn = key - L;
+            const int key = t + 16 * kt + 4 * g + j, jn = key - L;
             vis = vis && key < w1 && (jn < 0 || ((vis_new >> jn) & 1ull));
           }
-          sv[kt] = vis ? acc_s[rt][kt][j] * a.scale : -INFINITY;
-          mt = fmaxf(mt, sv[kt]);
+          sv[kt][j] = vis ? acc_s[rt][kt][j] * a.scale : -INFINITY;
+          mt = fmaxf(mt, sv[kt][j]);
         }
-        mt = max16(mt);
-        const float mn = fmaxf(m[rt][j], mt);
-        float cr = 1.f, ps = 0.f;
+      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+      const float mn = fmaxf(m[rt], mt);
+      float ps = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const float pv = mn > -INFINITY && sv[kt] > -INFINITY ? __expf(sv[kt] - mn) : 0.f;
-          ps += pv;
-          pbuf[wave][rt * 16 + 4 * g + j][16 * kt + c] = pv;
-        }
-        if (mn > m[rt][j]) {
-          cr = m[rt][j] > -INFINITY ? __expf(m[rt][j] - mn) : 0.f;
-          moved = true;
-        }
-        corr[rt][j] = cr;
-        l[rt][j] = l[rt][j] * cr + sum16(ps);
-        m[rt][j] = mn;
+      for (int kt = 0; kt < 4; ++kt) {
+        float4 pv;
+        pv.x = mn > -INFINITY && sv[kt][0] > -INFINITY ? __expf(sv[kt][0] - mn) : 0.f;
+        pv.y = mn > -INFINITY && sv[kt][1] > -INFINITY ? __expf(sv[kt][1] - mn) : 0.f;
+        pv.z = mn > -INFINITY && sv[kt][2] > -INFINITY ? __expf(sv[kt][2] - mn) : 0.f;
+        pv.w = mn > -INFINITY && sv[kt][3] > -INFINITY ? __expf(sv[kt][3] - mn) : 0.f;
+        ps += (pv.x + pv.y) + (pv.z + pv.w);
+        *reinterpret_cast<float4*>(&pbuf[wave][rt * 16 + c][16 * kt + 4 * g]) = pv;
       }
+      ps += __shfl_xor(ps, 16, kWave);
+      ps += __shfl_xor(ps, 32, kWave);
+      float cr = 1.f;
+      if (mn > m[rt]) {
+        cr = m[rt] > -INFINITY ? __expf(m[rt] - mn) : 0.f;
+        moved = true;
+      }
+      corr[rt] = cr;
+      l[rt] = l[rt] * cr + ps;
+      m[rt] = mn;
+    }
     // rescale the output accumulators only when some row's max rose (the
     // accumulators live in the MFMA registers, so a rescale is a round trip)
     if (__any(moved)) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) acc_o[rt][dt][j] *= corr[rt][j];
+          for (int j = 0; j < 4; ++j) acc_o[rt][dt][j] *= corr[rt];
     }
-    // the tile's probabilities are read back below in the A-operand layout
+    // the tile's probabilities are read back below in the operand layout
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // O += P V: P's A fragments (row 16 rt + c, keys 32 kv + 8 g .. + 7),
-    // split into two bf16 terms (probabilities to 2^-16 relative)
+    // O^T += V^T P^T: P's B fragments (row 16 rt + c, keys 32 kv + 8 g ..
+    // + 7), split into two bf16 terms (probabilities to 2^-16 relative)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -330,7 +355,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
         for (int p = 0; p < 2; ++p)
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
-            acc_o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[p], vf[kv][dt], acc_o[rt][dt], 0, 0, 0);
+            acc_o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kv][dt], pf[p], acc_o[rt][dt], 0, 0, 0);
       }
     if (more) load_v(t + kAttnTile);
     // every lane has read the tile's probabilities before the next tile's
@@ -340,23 +365,24 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   }
 
   // merge the four waves' states in LDS (the loop buffers are free now),
-  // in wave order, and write one partial per work group: rows 16 rt + 4 g +
-  // j, dimension 16 dt + c
+  // in wave order, and write one partial per work group: row 16 rt + c,
+  // dimensions 16 dt + 4 g + j
   __syncthreads();
   float* obuf = reinterpret_cast<float*>(smem);                 // [waves][ROWS][HD]
   float* mlbuf = obuf + (size_t)kAttnWaves * ROWS * HD;         // [waves][ROWS][2]
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + c;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = rt * 16 + 4 * g + j;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) obuf[((size_t)wave * ROWS + r) * HD + 16 * dt + c] = acc_o[rt][dt][j];
-      if (c == 0) {
-        mlbuf[(wave * ROWS + r) * 2] = m[rt][j];
-        mlbuf[(wave * ROWS + r) * 2 + 1] = l[rt][j];
-      }
+    for (int dt = 0; dt < DT; ++dt) {
+      const float4 o = {acc_o[rt][dt][0], acc_o[rt][dt][1], acc_o[rt][dt][2], acc_o[rt][dt][3]};
+      *reinterpret_cast<float4*>(&obuf[((size_t)wave * ROWS + r) * HD + 16 * dt + 4 * g]) = o;
     }
+    if (g == 0) {
+      mlbuf[(wave * ROWS + r) * 2] = m[rt];
+      mlbuf[(wave * ROWS + r) * 2 + 1] = l[rt];
+    }
+  }
   __syncthreads();
   const size_t unit = (((size_t)b * a.Hkv + kvh) * a.RG + rg) * (size_t)a.S + split;
   float* po = a.part_o + unit * ROWS * HD;
@@ -476,13 +502,13 @@ AttnShape attn_shape(int B, int n_new, int H, int Hkv, int hd, int max_seq) {
   // value byte read once for them), else groups of 64
   s.RT = std::min(kAttnMaxRT, (s.R + 15) / 16);
   s.RG = (s.R + 16 * s.RT - 1) / (16 * s.RT);
-  // splits of the keys: about 2048 waves over the chip, but at least two
-  // 64-key tiles per wave so a wave's partial state (16 RT x hd floats)
-  // stays small next to the keys and values it streamed
+  // splits of the keys: about SV_ATTN_WAVES waves over the chip, but at
+  // least SV_ATTN_MIN_TILES 64-key tiles per wave so a wave's partial state
+  // (16 RT x hd floats) stays small next to the keys and values it streamed
   const int groups = B * Hkv * s.RG;
   const int tiles = (max_seq + kAttnTile - 1) / kAttnTile;
-  const int want = (2048 + groups * kAttnWaves - 1) / (groups * kAttnWaves);
-  const int most = std::max(1, tiles / (2 * kAttnWaves));
+  const int want = (SV_ATTN_WAVES + groups * kAttnWaves - 1) / (groups * kAttnWaves);
+  const int most = std::max(1, tiles / (SV_ATTN_MIN_TILES * kAttnWaves));
   s.S = std::max(1, std::min(want, most));
   const size_t units = (size_t)groups * s.S;
   const size_t rows = (size_t)16 * s.RT;

@@ -66,8 +66,9 @@ __device__ __forceinline__ void split2_bf16(float x, uint32_t& hi, uint32_t& lo)
 //             A-row 5 p + r holds term p of row 5 mt + r (A-row 15 unused),
 //             so a single MFMA covers every term of five rows and the
 //             terms are summed after the k-loop
-// With the two-term split (plain packing only) the third fragment holds
-// zeros, so a three-term reader of the buffer computes hi + lo.
+// With the two-term split (plain packing only) the third fragment is not
+// written: every GEMM of such a pass reads two fragments per row tile (the
+// all-zero k-step past the end holds zeros in all three).
 // xs_index returns the bf16 index of term 0 of (row, col); term p sits at
 // +p * xs_term_step(stacked).  Both are host functions too, so the host-side
 // access check evaluates the very formulas the kernels use.
@@ -91,7 +92,7 @@ __device__ __forceinline__ void xs_store(uint16_t* xs, int row, int col, int ks,
   const int st = xs_term_step(stacked);
   xs[i] = (uint16_t)a;
   xs[i + st] = (uint16_t)b;
-  xs[i + 2 * st] = (uint16_t)c;
+  if (!two) xs[i + 2 * st] = (uint16_t)c;
 }
 
 // ---- Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) -------------------

@@ -771,7 +771,7 @@ __device__ __forceinline__ void wide_lm_epilogue2(const EpiArgs& e, const f32x4 
 // ring.  When the column blocks cannot fill the chip, K is split over
 // blockIdx.y and the slices are summed, in slice order, by k_epi_wide.
 // TERMS: the bf16 terms of each activation read (3, or 2 with the
-// two-term split, whose third fragment is zero and skipped).
+// two-term split, whose third fragment is skipped).
 // Output: fp32 partial sums P[slice][row][col].
 template <int MTW, int NTC, int MG, int CG, int RING, int TERMS>
 __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs e) {
@@ -1019,10 +1019,11 @@ __global__ __launch_bounds__(kEpiThreads) void k_epi_wide(WideArgs a, EpiArgs e0
 }
 
 // ---------------------------------------------------------------- vector-FMA GEMM
-// Row-major weights (fp32 or bf16), 4 waves, 4 column tiles (64 columns) per
-// work group.  Lane = (row r = lane / 8 of an 8-row step, 8 columns at
-// 8 * (lane % 8)); the waves take interleaved 8-row steps of K; rows of X
-// are processed 8 at a time.
+// Row-major weights (fp32 or bf16), kFmaWaves waves, 4 column tiles (64
+// columns) per work group.  Lane = (row r = lane / 8 of an 8-row step, 8
+// columns at 8 * (lane % 8)); the waves take interleaved 8-row steps of K,
+// kFmaUnroll steps' loads issued together; rows of X are processed 8 at a
+// time.  The waves' sums meet in LDS in wave order.
 template <typename WT>
 __device__ __forceinline__ void load_w8(const WT* p, float (&w)[8]);
 template <>
@@ -1039,13 +1040,15 @@ __device__ __forceinline__ void load_w8<uint16_t>(const uint16_t* p, float (&w)[
   w[4] = bf16_lo(a.z); w[5] = bf16_hi(a.z); w[6] = bf16_lo(a.w); w[7] = bf16_hi(a.w);
 }
 
-constexpr int kFmaThreads = 256;
+constexpr int kFmaThreads = kFmaWaves * kWave;
+constexpr int kFmaUnroll = 4;
 
 template <typename WT>
 __global__ __launch_bounds__(kFmaThreads) void k_gemm_fma(GemmArgs a) {
   extern __shared__ float smem[];
   __shared__ float sh_inv[256];
   constexpr int ldr = kGroupCols + 1;
+  constexpr int kStep = kFmaWaves * 8;             // k rows of one step of the group
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = blockIdx.x;                        // 64-column block
   const int Kp = a.KS * kKStep;
@@ -1053,9 +1056,9 @@ __global__ __launch_bounds__(kFmaThreads) void k_gemm_fma(GemmArgs a) {
   const int rr = lane >> 3, cg = (lane & 7) * 8;
   const WT* W = reinterpret_cast<const WT*>(a.W) + (size_t)g * kGroupCols + cg;
   float* res = smem;                       // [M][ldr]
-  float* red = smem + M * ldr;             // [4][8][ldr]
+  float* red = smem + M * ldr;             // [kFmaWaves][8][ldr]
   float pv[8];
-  epi_prefetch(a.e, M, g * 4, 4, kFmaThreads / kWave, pv);
+  epi_prefetch(a.e, M, g * 4, 4, kFmaWaves, pv);
 
   for (int m0 = 0; m0 < M; m0 += 8) {
     const int mr = min(8, M - m0);
@@ -1064,17 +1067,24 @@ __global__ __launch_bounds__(kFmaThreads) void k_gemm_fma(GemmArgs a) {
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[m][j] = 0.f;
-    for (int k = wave * 8 + rr; k < Kp; k += 32) {
-      float w[8];
-      load_w8<WT>(W + (size_t)k * a.Np, w);
+    for (int k0 = wave * 8 + rr; k0 < Kp; k0 += kStep * kFmaUnroll) {
+      // kFmaUnroll steps: every load first (rows past Kp read row Kp - 1
+      // and count zero), then the FMAs
+      float w[kFmaUnroll][8], xv[kFmaUnroll][8];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        if (m < mr) {
-          const float x = a.X[(size_t)(m0 + m) * a.ldx + k];
+      for (int u = 0; u < kFmaUnroll; ++u) {
+        const int k = k0 + u * kStep;
+        load_w8<WT>(W + (size_t)min(k, Kp - 1) * a.Np, w[u]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[m][j] = fmaf(x, w[j], acc[m][j]);
-        }
+        for (int m = 0; m < 8; ++m)
+          xv[u][m] = m < mr && k < Kp ? a.X[(size_t)(m0 + m) * a.ldx + k] : 0.f;
       }
+#pragma unroll
+      for (int u = 0; u < kFmaUnroll; ++u)
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[m][j] = fmaf(xv[u][m], w[u][j], acc[m][j]);
     }
     // sum the 8 row-lanes that share a column group (lanes differ in bits 3..5)
 #pragma unroll
@@ -1098,12 +1108,12 @@ __global__ __launch_bounds__(kFmaThreads) void k_gemm_fma(GemmArgs a) {
       const int m = idx / kGroupCols, c = idx - m * kGroupCols;
       float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v += red[(w * 8 + m) * ldr + c];
+      for (int w = 0; w < kFmaWaves; ++w) v += red[(w * 8 + m) * ldr + c];
       res[(m0 + m) * ldr + c] = v;
     }
     __syncthreads();
   }
-  run_epilogue(a.e, M, g * 4, 4, res, ldr, sh_inv, kFmaThreads / kWave, pv);
+  run_epilogue(a.e, M, g * 4, 4, res, ldr, sh_inv, kFmaWaves, pv);
 }
 
 // ---------------------------------------------------------------- host side
@@ -1126,7 +1136,7 @@ GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack) {
   if (path != PATH_MFMA) {
     p.nt = 4; p.mg = 1; p.mtw = 1; p.kg = 4;
     p.blocks = m.Np / kGroupCols;
-    p.lds = ((size_t)M * (kGroupCols + 1) + 4 * 8 * (kGroupCols + 1)) * sizeof(float);
+    p.lds = ((size_t)M * (kGroupCols + 1) + kFmaWaves * 8 * (kGroupCols + 1)) * sizeof(float);
     return p;
   }
   p.stack = stack;

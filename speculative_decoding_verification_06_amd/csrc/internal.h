@@ -81,6 +81,9 @@ struct GemmArgs {
   EpiArgs e;
 };
 
+// Waves of a vector-FMA GEMM work group (k_gemm_fma).
+constexpr int kFmaWaves = 8;
+
 // Launch plan of one GEMM (chosen on the host by plan_gemm).
 enum GemmPath { PATH_FMA_F32 = 0, PATH_FMA_BF16 = 1, PATH_MFMA = 2 };
 
