@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   // of probabilities), reused after the loop to merge the four waves' states
   constexpr size_t kLoopBytes = sizeof(bf16x8) * RT * KS * 3 * kWave +
                                 sizeof(float) * kAttnWaves * ROWS * (kAttnTile + 4);
-  constexpr size_t kMergeBytes = sizeof(float) * kAttnWaves * ROWS * (HD + 2);
+  constexpr size_t kMergeBytes = sizeof(float) * kAttnWaves * ROWS * (HD + 3);
   __shared__ __align__(16) unsigned char smem[kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes];
   auto& qf = *reinterpret_cast<bf16x8 (*)[RT][KS][3][kWave]>(smem);
   auto& pbuf = *reinterpret_cast<float (*)[kAttnWaves][ROWS][kAttnTile + 4]>(
@@ -234,20 +234,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   };
   // value fragments: k-step kv (32 keys), dimension tile dt: lane holds
   // dimension 16 dt + c at keys t + 32 kv + 8 g .. + 7 (16 bytes of the
-  // head-dimension-major value row); in the wave's last tile the keys past
-  // w1 are zeroed (the tile test is uniform over the wave)
+  // head-dimension-major value row).  Plain loads, so they stay in flight
+  // under the next tile's scores; in the wave's last tile the keys past w1
+  // are zeroed where the values are used.
   bf16x8 vf[2][DT];
+  auto v_first = [&](int t, int kv) { return min(t + 32 * kv + 8 * g, a.max_seq - 8); };
   auto load_v = [&](int t) {
-    const bool tail = t + kAttnTile > w1;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
-      const int k0 = t + 32 * kv + 8 * g;
-      const int kl = min(k0, a.max_seq - 8);       // in bounds; the values past w1 are zeroed
+      const int kl = v_first(t, kv);               // in bounds (max_seq is a multiple of 8)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 f = *reinterpret_cast<const bf16x8*>(Vt + (size_t)(16 * dt + c) * a.max_seq + kl);
-        vf[kv][dt] = tail ? zero_past(f, kl, w1) : f;
-      }
+      for (int dt = 0; dt < DT; ++dt)
+        vf[kv][dt] = *reinterpret_cast<const bf16x8*>(Vt + (size_t)(16 * dt + c) * a.max_seq + kl);
     }
   };
   // The loads rotate through the tiles: a tile's keys are consumed by the
@@ -266,29 +264,34 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) acc_s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // query fragments stream from LDS two fragments ahead of the MFMAs that
+    // use them (a rolling buffer over (k-step, term, row tile)); the four-
+    // tile kernel has no registers for the buffer and reads each as it goes
+    constexpr int NQ = KS * 3 * RT, QA = RT >= 4 ? 1 : 3;
+    auto qfrag = [&](int n) { return qf[n % RT][n / (3 * RT)][(n / RT) % 3][lane]; };
+    bf16x8 qb[QA];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int n = 0; n < QA - 1; ++n) qb[n] = qfrag(n);
 #pragma unroll
-      for (int p = 0; p < 3; ++p)
+    for (int n = 0; n < NQ; ++n) {
+      if (n + QA - 1 < NQ) qb[(n + QA - 1) % QA] = qfrag(n + QA - 1);
+      const int rt = n % RT, ks = n / (3 * RT);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const bf16x8 qb = qf[rt][ks][p][lane];
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-            acc_s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][ks], qb, acc_s[rt][kt], 0, 0, 0);
-        }
+      for (int kt = 0; kt < 4; ++kt)
+        acc_s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][ks], qb[n % QA], acc_s[rt][kt], 0, 0, 0);
+    }
     if (more) load_k(t + kAttnTile);
     // mask and online softmax per row.  A tile wholly inside this wave's
     // committed keys is visible to every row (no mask work).
     const bool plain = t + kAttnTile <= min(L, w1);
     bool moved = false;                              // some row's running max rose
-    float corr[RT];
+    float corr[RT], mt[RT], mn[RT], ps[RT];
+    // phase 1: scaled, masked scores (in place) and each lane's max
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const int i = rowi[rt];
       const uint64_t vis_new = i >= 0 ? anc[i] : 0ull;
-      float sv[4][4];
-      float mt = -INFINITY;
+      mt[rt] = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -298,33 +301,47 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
             const int key = t + 16 * kt + 4 * g + j, jn = key - L;
             vis = vis && key < w1 && (jn < 0 || ((vis_new >> jn) & 1ull));
           }
-          sv[kt][j] = vis ? acc_s[rt][kt][j] * a.scale : -INFINITY;
-          mt = fmaxf(mt, sv[kt][j]);
+          acc_s[rt][kt][j] = vis ? acc_s[rt][kt][j] * a.scale : -INFINITY;
+          mt[rt] = fmaxf(mt[rt], acc_s[rt][kt][j]);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-      const float mn = fmaxf(m[rt], mt);
-      float ps = 0.f;
+    }
+    // phase 2: row maxima over the four lanes of a row, every row tile's
+    // exchange in flight together
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 16, kWave));
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 32, kWave));
+    // phase 3: probabilities to LDS, each lane's sums
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      mn[rt] = fmaxf(m[rt], mt[rt]);
+      ps[rt] = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         float4 pv;
-        pv.x = mn > -INFINITY && sv[kt][0] > -INFINITY ? __expf(sv[kt][0] - mn) : 0.f;
-        pv.y = mn > -INFINITY && sv[kt][1] > -INFINITY ? __expf(sv[kt][1] - mn) : 0.f;
-        pv.z = mn > -INFINITY && sv[kt][2] > -INFINITY ? __expf(sv[kt][2] - mn) : 0.f;
-        pv.w = mn > -INFINITY && sv[kt][3] > -INFINITY ? __expf(sv[kt][3] - mn) : 0.f;
-        ps += (pv.x + pv.y) + (pv.z + pv.w);
+        pv.x = mn[rt] > -INFINITY && acc_s[rt][kt][0] > -INFINITY ? __expf(acc_s[rt][kt][0] - mn[rt]) : 0.f;
+        pv.y = mn[rt] > -INFINITY && acc_s[rt][kt][1] > -INFINITY ? __expf(acc_s[rt][kt][1] - mn[rt]) : 0.f;
+        pv.z = mn[rt] > -INFINITY && acc_s[rt][kt][2] > -INFINITY ? __expf(acc_s[rt][kt][2] - mn[rt]) : 0.f;
+        pv.w = mn[rt] > -INFINITY && acc_s[rt][kt][3] > -INFINITY ? __expf(acc_s[rt][kt][3] - mn[rt]) : 0.f;
+        ps[rt] += (pv.x + pv.y) + (pv.z + pv.w);
         *reinterpret_cast<float4*>(&pbuf[wave][rt * 16 + c][16 * kt + 4 * g]) = pv;
       }
-      ps += __shfl_xor(ps, 16, kWave);
-      ps += __shfl_xor(ps, 32, kWave);
+    }
+    // phase 4: row sums, the running state
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) ps[rt] += __shfl_xor(ps[rt], 16, kWave);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) ps[rt] += __shfl_xor(ps[rt], 32, kWave);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
       float cr = 1.f;
-      if (mn > m[rt]) {
-        cr = m[rt] > -INFINITY ? __expf(m[rt] - mn) : 0.f;
+      if (mn[rt] > m[rt]) {
+        cr = m[rt] > -INFINITY ? __expf(m[rt] - mn[rt]) : 0.f;
         moved = true;
       }
       corr[rt] = cr;
-      l[rt] = l[rt] * cr + ps;
-      m[rt] = mn;
+      l[rt] = l[rt] * cr + ps[rt];
+      m[rt] = mn[rt];
     }
     // rescale the output accumulators only when some row's max rose (the
     // accumulators live in the MFMA registers, so a rescale is a round trip)
@@ -340,6 +357,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the wave's last tile: values of keys past w1 are zeroed (memory past
+    // the visible keys may hold anything, even non-finite bits)
+    if (t + kAttnTile > w1) {
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vf[kv][dt] = zero_past(vf[kv][dt], v_first(t, kv), w1);
+    }
     // O^T += V^T P^T: P's B fragments (row 16 rt + c, keys 32 kv + 8 g ..
     // + 7), split into two bf16 terms (probabilities to 2^-16 relative)
 #pragma unroll
@@ -387,24 +412,39 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   const size_t unit = (((size_t)b * a.Hkv + kvh) * a.RG + rg) * (size_t)a.S + split;
   float* po = a.part_o + unit * ROWS * HD;
   float* pml = a.part_ml + unit * ROWS * 2;
-  for (int x = tid; x < nr * HD; x += kAttnThreads) {
-    const int r = x / HD, d = x - r * HD;
+  // per row: the merged max and sum, and each wave's weight exp(m_w - M)
+  // (0 for a wave that saw none of the row's keys), once per row
+  float* ew = mlbuf + kAttnWaves * ROWS * 2;                    // [ROWS][waves]
+  for (int r = tid; r < nr; r += kAttnThreads) {
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mlbuf[(w * ROWS + r) * 2]);
-    float o = 0.f, lsum = 0.f;
-    if (M > -INFINITY) {
+    float lsum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float mw = mlbuf[(w * ROWS + r) * 2];
-        if (mw == -INFINITY) continue;
-        const float e = __expf(mw - M);
-        o += obuf[((size_t)w * ROWS + r) * HD + d] * e;
-        lsum += mlbuf[(w * ROWS + r) * 2 + 1] * e;
-      }
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float mw = mlbuf[(w * ROWS + r) * 2];
+      const float e = M > -INFINITY && mw > -INFINITY ? __expf(mw - M) : 0.f;
+      ew[r * kAttnWaves + w] = e;
+      lsum += mlbuf[(w * ROWS + r) * 2 + 1] * e;
     }
-    po[r * HD + d] = o;
-    if (d == 0) { pml[2 * r] = M; pml[2 * r + 1] = lsum; }
+    pml[2 * r] = M;
+    pml[2 * r + 1] = lsum;
+  }
+  __syncthreads();
+  // the merged rows, four dimensions per thread
+  constexpr int HD4 = HD / 4;
+  const float4* ob4 = reinterpret_cast<const float4*>(obuf);
+  float4* po4 = reinterpret_cast<float4*>(po);
+  for (int x = tid; x < nr * HD4; x += kAttnThreads) {
+    const int r = x / HD4, d4 = x - r * HD4;
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float e = ew[r * kAttnWaves + w];
+      const float4 v = ob4[((size_t)w * ROWS + r) * HD4 + d4];
+      o.x += v.x * e; o.y += v.y * e; o.z += v.z * e; o.w += v.w * e;
+    }
+    po4[r * HD4 + d4] = o;
   }
 }
 
