@@ -1018,6 +1018,90 @@ __global__ __launch_bounds__(kEpiThreads) void k_epi_wide(WideArgs a, EpiArgs e0
   run_epilogue(e, M, c0, 4, res, ldr, sh_inv, kEpiThreads / kWave, pv);
 }
 
+// The UP and DOWN epilogues after K slices with each thread owning 8
+// consecutive columns of one row: the slices' partial sums as 16-byte loads
+// (summed in slice order), and the split activations for the next GEMM as
+// one 16-byte store per term.  Work group: 16 rows x 128 columns.  The same
+// arithmetic as run_epilogue's, except that a 16-column subtile's sum of
+// squares adds its two halves of 8 (a different rounding order).
+constexpr int kEpi8Cols = 128;
+__global__ __launch_bounds__(kEpiThreads) void k_epi_wide8(WideArgs a, EpiArgs e0) {
+  const int tid = threadIdx.x, r = tid >> 4, cgp = tid & 15;
+  const int m0 = blockIdx.y * 16;
+  const int n0 = blockIdx.x * kEpi8Cols + 8 * cgp;
+  const int M = min(16, a.M - m0);
+  const bool live = r < M && n0 < a.ldp;
+  const EpiArgs e = epi_rows(e0, m0);
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  if (live) {
+    const float* p = a.P + (size_t)(m0 + r) * a.ldp + n0;
+    for (int sl = 0; sl < a.S; sl += 4) {
+      float4 x[4][2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool in = sl + q < a.S;
+        const float4* pq = reinterpret_cast<const float4*>(p + (size_t)(in ? sl + q : 0) * a.slice_stride);
+        x[q][0] = in ? pq[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[q][1] = in ? pq[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[0] += x[q][0].x; v[1] += x[q][0].y; v[2] += x[q][0].z; v[3] += x[q][0].w;
+        v[4] += x[q][1].x; v[5] += x[q][1].y; v[6] += x[q][1].z; v[7] += x[q][1].w;
+      }
+    }
+  }
+  float y[8];
+  if (e.kind == EPI_UP) {
+    const float inv = live ? e.rms[e.row0 + r] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = live && n0 + j < e.N ? silu(v[j] * inv) : 0.f;
+    if (live && !e.xs)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e.out[(size_t)r * e.ldo + n0 + j] = y[j];
+  } else {
+    float hn[8];
+    float* hrow = e.out + (size_t)r * e.ldo + n0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hn[j] = live && n0 + j < e.N ? hrow[j] + v[j] : 0.f;
+    if (live)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hrow[j] = hn[j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = hn[j];
+    if (e.gain_next) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = live && n0 + j < e.N ? hn[j] * e.gain_next[n0 + j] : 0.f;
+      if (live && !e.xs)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e.xg[(size_t)r * e.ldo + n0 + j] = y[j];
+      float sq = ((hn[0] * hn[0] + hn[1] * hn[1]) + (hn[2] * hn[2] + hn[3] * hn[3])) +
+                 ((hn[4] * hn[4] + hn[5] * hn[5]) + (hn[6] * hn[6] + hn[7] * hn[7]));
+      sq += __shfl_xor(sq, 1, kWave);                 // the subtile's other 8 columns
+      if (live && (cgp & 1) == 0) e.ss_out[(size_t)r * e.ss_ld + n0 / kSub] = sq;
+    }
+  }
+  if (live && e.xs && n0 < kKStep * e.xs_ks) {
+    uint32_t t[3][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t a0, b0, c0 = 0, a1, b1, c1 = 0;
+      if (e.xs_two) { split2_bf16(y[2 * j], a0, b0); split2_bf16(y[2 * j + 1], a1, b1); }
+      else { split3_bf16(y[2 * j], a0, b0, c0); split3_bf16(y[2 * j + 1], a1, b1, c1); }
+      t[0][j] = a0 | (a1 << 16);
+      t[1][j] = b0 | (b1 << 16);
+      t[2][j] = c0 | (c1 << 16);
+    }
+    uint16_t* base = e.xs + xs_index(r, n0, e.xs_ks, false);
+    const int st = xs_term_step(false);
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      if (q < 2 || !e.xs_two) *reinterpret_cast<uint4*>(base + q * st) = make_uint4(t[q][0], t[q][1], t[q][2], t[q][3]);
+  }
+}
+
 // ---------------------------------------------------------------- vector-FMA GEMM
 // Row-major weights (fp32 or bf16), kFmaWaves waves, 4 column tiles (64
 // columns) per work group.  Lane = (row r = lane / 8 of an 8-row step, 8
@@ -1286,7 +1370,11 @@ hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.fuse_lm) return err;
-  hipLaunchKernelGGL(k_epi_wide, dim3(a.tiles / 4, (a.M + 15) / 16), dim3(kEpiThreads), 0, st, a, e);
+  if (e.kind == EPI_LM)
+    hipLaunchKernelGGL(k_epi_wide, dim3(a.tiles / 4, (a.M + 15) / 16), dim3(kEpiThreads), 0, st, a, e);
+  else
+    hipLaunchKernelGGL(k_epi_wide8, dim3((a.ldp + kEpi8Cols - 1) / kEpi8Cols, (a.M + 15) / 16),
+                       dim3(kEpiThreads), 0, st, a, e);
   return hipGetLastError();
 }
 

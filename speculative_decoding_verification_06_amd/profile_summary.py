@@ -2,6 +2,9 @@
 
     python -m speculative_decoding_verification_06_amd.profile_summary trace DIR
         per-kernel call counts and durations from DIR/*kernel_trace.csv
+    python -m speculative_decoding_verification_06_amd.profile_summary counters DIR [SUBSTRING]
+        per-dispatch averages of every counter of a --pmc run, per kernel
+        (kernels whose name contains SUBSTRING)
     python -m speculative_decoding_verification_06_amd.profile_summary traffic \\
         WORKLOAD FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR COPY_MIB OUT_JSON
         HBM bytes per weight-streaming GEMM launch from FETCH_SIZE and
@@ -71,6 +74,21 @@ def counter_per_dispatch(directory, counter):
     return out
 
 
+def counter_table(directory, substring="sv::"):
+    """{kernel: {counter: per-dispatch average}} and the dispatch counts."""
+    names = set()
+    for r in _rows(directory, "counter_collection.csv"):
+        names.add(r["Counter_Name"])
+    out, counts = {}, {}
+    for cname in sorted(names):
+        for kern, vals in counter_per_dispatch(directory, cname).items():
+            if substring not in kern:
+                continue
+            out.setdefault(kern, {})[cname] = sum(vals) / len(vals)
+            counts[kern] = len(vals)
+    return out, counts
+
+
 def _copy_scale(directory, counter, mib):
     vals = [v for name, vs in counter_per_dispatch(directory, counter).items()
             if "elementwise" in name or "mul" in name.lower() for v in vs]
@@ -110,6 +128,12 @@ def traffic(workload, fetch_dir, write_dir, copy_fetch, copy_write, copy_mib, ou
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "trace":
         print(trace_table(sys.argv[2]))
+    elif len(sys.argv) in (3, 4) and sys.argv[1] == "counters":
+        tab, counts = counter_table(sys.argv[2], sys.argv[3] if len(sys.argv) == 4 else "sv::")
+        for kern, cs in tab.items():
+            print(f"{kern} ({counts[kern]} dispatches)")
+            for cname, v in cs.items():
+                print(f"  {cname}: {v:.6g}")
     elif len(sys.argv) == 9 and sys.argv[1] == "traffic":
         rec = traffic(sys.argv[2], *sys.argv[3:7], float(sys.argv[7]), sys.argv[8])
         print(json.dumps({k: v for k, v in rec.items() if k != "per_kernel"}))
