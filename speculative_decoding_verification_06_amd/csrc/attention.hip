@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   // of probabilities), reused after the loop to merge the four waves' states
   constexpr size_t kLoopBytes = sizeof(bf16x8) * RT * KS * 3 * kWave +
                                 sizeof(float) * kAttnWaves * ROWS * (kAttnTile + 4);
-  constexpr size_t kMergeBytes = sizeof(float) * kAttnWaves * ROWS * (HD + 3);
+  constexpr int OLD = HD + 4;                      // merge rows padded a float4: rows c and c + 1 in other banks
+  constexpr size_t kMergeBytes = sizeof(float) * kAttnWaves * ROWS * (OLD + 3);
   __shared__ __align__(16) unsigned char smem[kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes];
   auto& qf = *reinterpret_cast<bf16x8 (*)[RT][KS][3][kWave]>(smem);
   auto& pbuf = *reinterpret_cast<float (*)[kAttnWaves][ROWS][kAttnTile + 4]>(
@@ -316,13 +317,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
     for (int rt = 0; rt < RT; ++rt) {
       mn[rt] = fmaxf(m[rt], mt[rt]);
       ps[rt] = 0.f;
+      // exp(-inf - M) = 0 for a masked key; a row with nothing visible yet
+      // subtracts 0 instead of -inf, so its masked keys also give 0
+      const float mref = mn[rt] > -INFINITY ? mn[rt] : 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         float4 pv;
-        pv.x = mn[rt] > -INFINITY && acc_s[rt][kt][0] > -INFINITY ? __expf(acc_s[rt][kt][0] - mn[rt]) : 0.f;
-        pv.y = mn[rt] > -INFINITY && acc_s[rt][kt][1] > -INFINITY ? __expf(acc_s[rt][kt][1] - mn[rt]) : 0.f;
-        pv.z = mn[rt] > -INFINITY && acc_s[rt][kt][2] > -INFINITY ? __expf(acc_s[rt][kt][2] - mn[rt]) : 0.f;
-        pv.w = mn[rt] > -INFINITY && acc_s[rt][kt][3] > -INFINITY ? __expf(acc_s[rt][kt][3] - mn[rt]) : 0.f;
+        pv.x = __expf(acc_s[rt][kt][0] - mref);
+        pv.y = __expf(acc_s[rt][kt][1] - mref);
+        pv.z = __expf(acc_s[rt][kt][2] - mref);
+        pv.w = __expf(acc_s[rt][kt][3] - mref);
         ps[rt] += (pv.x + pv.y) + (pv.z + pv.w);
         *reinterpret_cast<float4*>(&pbuf[wave][rt * 16 + c][16 * kt + 4 * g]) = pv;
       }
@@ -344,8 +348,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
       m[rt] = mn[rt];
     }
     // rescale the output accumulators only when some row's max rose (the
-    // accumulators live in the MFMA registers, so a rescale is a round trip)
-    if (__any(moved)) {
+    // accumulators live in the MFMA registers, so a rescale is a round trip);
+    // never after a wave's first tile, whose accumulators are still zero
+    if (t != w0 && __any(moved)) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -393,15 +398,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   // in wave order, and write one partial per work group: row 16 rt + c,
   // dimensions 16 dt + 4 g + j
   __syncthreads();
-  float* obuf = reinterpret_cast<float*>(smem);                 // [waves][ROWS][HD]
-  float* mlbuf = obuf + (size_t)kAttnWaves * ROWS * HD;         // [waves][ROWS][2]
+  float* obuf = reinterpret_cast<float*>(smem);                 // [waves][ROWS][OLD]
+  float* mlbuf = obuf + (size_t)kAttnWaves * ROWS * OLD;        // [waves][ROWS][2]
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int r = rt * 16 + c;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const float4 o = {acc_o[rt][dt][0], acc_o[rt][dt][1], acc_o[rt][dt][2], acc_o[rt][dt][3]};
-      *reinterpret_cast<float4*>(&obuf[((size_t)wave * ROWS + r) * HD + 16 * dt + 4 * g]) = o;
+      *reinterpret_cast<float4*>(&obuf[((size_t)wave * ROWS + r) * OLD + 16 * dt + 4 * g]) = o;
     }
     if (g == 0) {
       mlbuf[(wave * ROWS + r) * 2] = m[rt];
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
       const float e = ew[r * kAttnWaves + w];
-      const float4 v = ob4[((size_t)w * ROWS + r) * HD4 + d4];
+      const float4 v = ob4[((size_t)w * ROWS + r) * (OLD / 4) + d4];
       o.x += v.x * e; o.y += v.y * e; o.z += v.z * e; o.w += v.w * e;
     }
     po4[r * HD4 + d4] = o;
