@@ -49,6 +49,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kAttnMaxRT = 4;      // 16-row MFMA tiles of query rows per work group (at most)
 constexpr int kAttnTile = 64;      // keys per wave tile: four 16-key MFMA tiles
+constexpr float kAttnSlack = 8.f;  // a row's reference max moves when passed by more (e^8 ~ 3e3)
 #ifndef SV_ATTN_WAVES
 #define SV_ATTN_WAVES 1024         // waves a launch aims for (splits of the keys)
 #endif
@@ -312,10 +313,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
     for (int rt = 0; rt < RT; ++rt) mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 16, kWave));
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 32, kWave));
-    // phase 3: probabilities to LDS, each lane's sums
+    // phase 3: probabilities to LDS, each lane's sums.  The reference max of
+    // a row moves only when the tile's max passes it by more than
+    // kAttnSlack (or on its first visible key): probabilities up to
+    // e^kAttnSlack are exact enough in fp32 and bf16 pairs, and the
+    // accumulators are rescaled far less often.
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      mn[rt] = fmaxf(m[rt], mt[rt]);
+      mn[rt] = m[rt] == -INFINITY || mt[rt] > m[rt] + kAttnSlack ? fmaxf(m[rt], mt[rt]) : m[rt];
       ps[rt] = 0.f;
       // exp(-inf - M) = 0 for a masked key; a row with nothing visible yet
       // subtracts 0 instead of -inf, so its masked keys also give 0
