@@ -129,11 +129,12 @@ def read_ceiling(torch, sv, nbytes, launches=40):
             "kernel": "spec_stream_read (16-byte non-temporal loads, one launch, fresh data)"}
 
 
-def roofline_of(wl, M, per_launch_bytes, per_launch_s, traffic, ceiling):
+def roofline_of(wl, M, per_launch_bytes, per_launch_s, traffic, ceiling, terms):
     """Roofline of the weight-streaming GEMMs: the method's own flops
     (2 M K N per launch), the bound from its intensity against the bf16
-    ridge, and, as a side field, the MFMA rate the kernels execute (three
-    bf16 terms per fp32 activation: 6 M K N)."""
+    ridge, and, as a side field, the MFMA rate the kernels execute (terms
+    bf16 MFMA products per fp32 activation: 2 terms M K N; terms = 0 for
+    the vector-FMA path)."""
     wbytes = 4 if wl.wdtype == "f32" else 2
     kn = per_launch_bytes / wbytes
     intensity = 2.0 * M * kn / per_launch_bytes
@@ -148,10 +149,10 @@ def roofline_of(wl, M, per_launch_bytes, per_launch_s, traffic, ceiling):
                     "unit": "TFLOP/s", "frac": method_tflops / MFMA_BF16_PEAK_TFLOPS})
     out["traffic"] = traffic
     out["method_tflops"] = method_tflops
-    if wl.wdtype == "bf16":
-        ex = 3.0 * method_tflops
+    if wl.wdtype == "bf16" and terms:
+        ex = terms * method_tflops
         out["mfma_executed"] = {"tflops": ex, "frac_of_bf16_peak": ex / MFMA_BF16_PEAK_TFLOPS,
-                                "note": "three bf16 MFMA terms per fp32 activation"}
+                                "note": f"{terms} bf16 MFMA terms per fp32 activation"}
     if ceiling:
         out["read_ceiling_gbs"] = ceiling["gbs"]
         out["frac_of_read_ceiling"] = gbs / ceiling["gbs"]
@@ -492,6 +493,13 @@ def main():
     step_gbs = (weight_bytes + other) / (ms / K / 1e3) / 1e9
     traffic = stored_traffic(wl.name)
 
+    # bf16 terms per fp32 activation on the MFMA path: two for the wide passes
+    # of 113 to 224 rows unless the exact split is asked for, else three; the
+    # vector-FMA path and fp32 weights take the activations as they are.
+    if args.gemm == "fma" or wl.wdtype != "bf16":
+        terms = 0
+    else:
+        terms = 2 if (not args.exact_split and 113 <= M <= 224) else 3
     out = {
         "metric": METRIC, "value": passes_s, "unit": "verify passes/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": ms / K, "higher_is_better": True,
@@ -502,14 +510,13 @@ def main():
                    "B": B, "gamma": gamma, "d": wl.d, "ffn": wl.ffn, "blocks": wl.n_blocks,
                    "V": wl.V, "temperature": T, "top_p": top_p,
                    "gemm_path": "vector FMA" if args.gemm == "fma" else "library default",
-                   "activation_terms": 2 if (not args.exact_split and wl.wdtype == "bf16"
-                                             and 113 <= B * G1 <= 224 and args.gemm == "auto") else 3},
+                   "activation_terms": terms},
         "accepted_tokens_per_s": tokens / (ms / 1e3),
         "mean_tokens_per_pass": tokens / (K * B),
         "hbm_gbs_whole_step": step_gbs,
         "hbm_frac_whole_step": step_gbs / HBM_PEAK_GBS,
         "algorithmic_bytes_per_step": weight_bytes + other,
-        "roofline": roofline_of(wl, M, per_launch_bytes, per_launch_s, traffic, ceiling),
+        "roofline": roofline_of(wl, M, per_launch_bytes, per_launch_s, traffic, ceiling, terms),
         "gemm": {"kernel": "weight-streaming GEMMs (MLP up/down, LM head)",
                  "bytes_per_launch": per_launch_bytes, "launches": launches,
                  "avg_launch_us": per_launch_s * 1e6, "hbm_gbs": achieved,

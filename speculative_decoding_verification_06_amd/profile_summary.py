@@ -46,13 +46,14 @@ def kernel_trace(directory):
 def trace_table(directory, prefix="sv::"):
     d = kernel_trace(directory)
     total = sum(sum(v) for v in d.values())
-    lines = ["| kernel | calls | avg us | min us | max us | % of GPU time |",
-             "|---|---|---|---|---|---|"]
+    lines = ["| kernel | calls | avg us | median us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|---|"]
     for name, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
         if prefix not in name:
             continue
         short = name if len(name) <= 90 else name[:87] + "..."
-        lines.append(f"| `{short}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | "
+        med = sorted(v)[len(v) // 2]
+        lines.append(f"| `{short}` | {len(v)} | {sum(v) / len(v):.1f} | {med:.1f} | {min(v):.1f} | "
                      f"{max(v):.1f} | {100 * sum(v) / total:.2f} |")
     return "\n".join(lines)
 
