@@ -56,6 +56,7 @@ constexpr float kAttnSlack = 8.f;  // a row's reference max moves when passed by
 #ifndef SV_ATTN_MIN_TILES
 #define SV_ATTN_MIN_TILES 2        // fewest 64-key tiles per wave
 #endif
+constexpr int kAttnMaxSplits = 256;  // splits of the keys (LDS of the combine)
 
 struct AttnArgs {
   int B, n_new, H, Hkv, G, max_seq, R, RG, S;   // R = n_new * G rows, RG row groups, S splits
@@ -437,11 +438,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
       ew[r * kAttnWaves + w] = e;
       lsum += mlbuf[(w * ROWS + r) * 2 + 1] * e;
     }
-    pml[2 * r] = M;
-    pml[2 * r + 1] = lsum;
+    if (a.S == 1) {
+      mlbuf[2 * r + 1] = lsum;                 // wave 0's slot of the row: read below
+    } else {
+      pml[2 * r] = M;
+      pml[2 * r + 1] = lsum;
+    }
   }
   __syncthreads();
-  // the merged rows, four dimensions per thread
+  // the merged rows, four dimensions per thread; with one split the merged
+  // row is the output itself, o / l (the combine's weight would be exactly 1)
   constexpr int HD4 = HD / 4;
   const float4* ob4 = reinterpret_cast<const float4*>(obuf);
   float4* po4 = reinterpret_cast<float4*>(po);
@@ -454,32 +460,73 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
       const float4 v = ob4[((size_t)w * ROWS + r) * (OLD / 4) + d4];
       o.x += v.x * e; o.y += v.y * e; o.z += v.z * e; o.w += v.w * e;
     }
-    po4[r * HD4 + d4] = o;
+    if (a.S == 1) {
+      const float den = mlbuf[2 * r + 1];
+      const int rr = r0 + r, i = rr / a.G, h = kvh * a.G + rr % a.G;
+      float* out = a.out + (((size_t)b * a.n_new + i) * a.H + h) * HD + 4 * d4;
+      out[0] = den > 0.f ? o.x / den : 0.f;
+      out[1] = den > 0.f ? o.y / den : 0.f;
+      out[2] = den > 0.f ? o.z / den : 0.f;
+      out[3] = den > 0.f ? o.w / den : 0.f;
+    } else {
+      po4[r * HD4 + d4] = o;
+    }
   }
 }
 
 // Merge the S partial states of every query row in order: out =
 // sum_p o_p exp(m_p - M) / sum_p l_p exp(m_p - M), M the largest m_p.
+// kCombineRows rows per work group, one thread per (row, dimension).  The
+// splits' (m, l) pairs are read once, in parallel, into LDS, and their
+// weights computed there, so the loads of a row's S partial outputs do not
+// depend on one another and stay in flight together; the sums still run in
+// split order.  Every split writes its partial (an empty one: o = 0,
+// m = -inf, l = 0), so a weight of 0 adds exactly 0.  Launched only when
+// S > 1; with one split the attention writes the output itself.
+constexpr int kCombineRows = 4;
 template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, int rows) {
-  const int d = threadIdx.x, r = blockIdx.x, rg = blockIdx.y % a.RG, kvh = blockIdx.y / a.RG,
+__global__ __launch_bounds__(HD * kCombineRows) void k_attn_combine(AttnArgs a, int rows) {
+  __shared__ float wsh[kCombineRows][kAttnMaxSplits], lsh[kCombineRows][kAttnMaxSplits];
+  const int d = threadIdx.x % HD, cr = threadIdx.x / HD;
+  const int r = blockIdx.x * kCombineRows + cr, rg = blockIdx.y % a.RG, kvh = blockIdx.y / a.RG,
             b = blockIdx.z;
   const int rr = rg * rows + r;
-  if (rr >= a.R) return;
+  const bool live = r < rows && rr < a.R;        // every thread reaches the barriers
   const int P = a.S;
   const size_t unit0 = (((size_t)b * a.Hkv + kvh) * a.RG + rg) * (size_t)P;
-  float M = -INFINITY;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, a.part_ml[((unit0 + p) * rows + r) * 2]);
-  float num = 0.f, den = 0.f;
-  if (M > -INFINITY) {
-    for (int p = 0; p < P; ++p) {
-      const float mp = a.part_ml[((unit0 + p) * rows + r) * 2];
-      if (mp == -INFINITY) continue;
-      const float w = expf(mp - M);
-      den += a.part_ml[((unit0 + p) * rows + r) * 2 + 1] * w;
-      num += a.part_o[((unit0 + p) * rows + r) * HD + d] * w;
+  if (live) {
+    for (int p = d; p < P; p += HD) {
+      wsh[cr][p] = a.part_ml[((unit0 + p) * rows + r) * 2];
+      lsh[cr][p] = a.part_ml[((unit0 + p) * rows + r) * 2 + 1];
     }
   }
+  __syncthreads();
+  float M = -INFINITY;
+  if (live)
+    for (int p = 0; p < P; ++p) M = fmaxf(M, wsh[cr][p]);
+  __syncthreads();
+  if (live) {
+    for (int p = d; p < P; p += HD) {
+      const float mp = wsh[cr][p];
+      wsh[cr][p] = M > -INFINITY && mp > -INFINITY ? expf(mp - M) : 0.f;
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  float den = 0.f;
+  for (int p = 0; p < P; ++p) den += lsh[cr][p] * wsh[cr][p];
+  const float* po = a.part_o + unit0 * rows * HD + (size_t)r * HD + d;
+  const size_t step = (size_t)rows * HD;
+  float num = 0.f;
+  int p = 0;
+  for (; p + 8 <= P; p += 8) {
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = po[(p + j) * step];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) num += o[j] * wsh[cr][p + j];
+  }
+  for (; p < P; ++p) num += po[p * step] * wsh[cr][p];
   const int i = rr / a.G, h = kvh * a.G + rr % a.G;
   a.out[(((size_t)b * a.n_new + i) * a.H + h) * HD + d] = den > 0.f ? num / den : 0.f;
 }
@@ -559,7 +606,7 @@ AttnShape attn_shape(int B, int n_new, int H, int Hkv, int hd, int max_seq) {
   const int tiles = (max_seq + kAttnTile - 1) / kAttnTile;
   const int want = (SV_ATTN_WAVES + groups * kAttnWaves - 1) / (groups * kAttnWaves);
   const int most = std::max(1, tiles / (SV_ATTN_MIN_TILES * kAttnWaves));
-  s.S = std::max(1, std::min(want, most));
+  s.S = std::max(1, std::min(std::min(want, most), kAttnMaxSplits));
   const size_t units = (size_t)groups * s.S;
   const size_t rows = (size_t)16 * s.RT;
   s.o_off = 0;
@@ -606,11 +653,12 @@ spec_status spec_decode_attention(int32_t B, int32_t n_new, int32_t H, int32_t H
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.ml_off);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const dim3 grid(s.S, Hkv * s.RG, B), cgrid(16 * s.RT, Hkv * s.RG, B);
+  const dim3 grid(s.S, Hkv * s.RG, B), cgrid(16 * s.RT / kCombineRows, Hkv * s.RG, B);
   auto go = [&](auto hd_tag, auto rt_tag) {
     constexpr int HDc = decltype(hd_tag)::value, RTc = decltype(rt_tag)::value;
     hipLaunchKernelGGL((k_decode_attn<HDc, RTc>), grid, dim3(kAttnThreads), 0, st, a);
-    hipLaunchKernelGGL(k_attn_combine<HDc>, cgrid, dim3(HDc), 0, st, a, 16 * RTc);
+    if (s.S > 1)
+      hipLaunchKernelGGL(k_attn_combine<HDc>, cgrid, dim3(HDc * kCombineRows), 0, st, a, 16 * RTc);
   };
   auto by_rt = [&](auto hd_tag) {
     switch (s.RT) {
