@@ -391,7 +391,7 @@ def bench_attention(progress, steps=200, warmup=20):
             "us_per_call": us, "bytes_per_call": kv_bytes + io_bytes, "hbm_gbs": gbs,
             "hbm_frac": gbs / HBM_PEAK_GBS, "read_ceiling_gbs": ceiling["gbs"],
             "frac_of_read_ceiling": gbs / ceiling["gbs"],
-            "note": "one call = the attention launch plus the split-combine launch"}), flush=True)
+            "note": "one call = the attention launch plus, when the keys are split, the split-combine launch"}), flush=True)
         progress(f"attention {name}: {us:.1f} us/call, {gbs:.0f} GB/s")
         del kc, vc
         torch.cuda.empty_cache()
