@@ -28,9 +28,14 @@
 // from the head-dimension-major value cache.  Online softmax per row; the four
 // waves' states are merged in LDS and every work group writes one partial
 // (max, sum, unnormalised output); a second kernel merges the splits'
-// partials in a fixed order, so results are run-to-run identical.  The softmax uses the hardware exp (relative error about
-// |x| 2^-23 for an argument x, far below the score error of an fp32
-// 128-term dot product that bounds the output).
+// partials in a fixed order, so results are run-to-run identical.  The
+// softmax runs in base 2: the queries are multiplied by scale * log2(e)
+// (one fp32 rounding) before they are split, so the accumulators hold
+// scores in log2 units and a probability is the hardware exp2 of a
+// difference (about one ulp), with no multiply per score; the running
+// maxima and the partials' maxima are in the same units.  Both errors are
+// far below the score error of an fp32 128-term dot product that bounds
+// the output.
 
 #include <algorithm>
 #include <climits>
@@ -49,7 +54,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = kAttnWaves * kWave;
 constexpr int kAttnMaxRT = 4;      // 16-row MFMA tiles of query rows per work group (at most)
 constexpr int kAttnTile = 64;      // keys per wave tile: four 16-key MFMA tiles
-constexpr float kAttnSlack = 8.f;  // a row's reference max moves when passed by more (e^8 ~ 3e3)
+constexpr float kAttnSlack = 11.5f;  // a row's reference max moves when passed by more (2^11.5 ~ 3e3)
 #ifndef SV_ATTN_WAVES
 #define SV_ATTN_WAVES 1024         // waves a launch aims for (splits of the keys)
 #endif
@@ -175,8 +180,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
       const float4* qp = reinterpret_cast<const float4*>(
           a.q + (((size_t)b * a.n_new + i) * a.H + h) * HD + ks * 32 + 8 * (l >> 4));
       const float4 u0 = qp[0], u1 = qp[1];
-      v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
-      v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+      const float qs = a.scale * 1.44269504088896341f;   // scale * log2(e)
+      v[0] = u0.x * qs; v[1] = u0.y * qs; v[2] = u0.z * qs; v[3] = u0.w * qs;
+      v[4] = u1.x * qs; v[5] = u1.y * qs; v[6] = u1.z * qs; v[7] = u1.w * qs;
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = 0.f;
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
             const int key = t + 16 * kt + 4 * g + j, jn = key - L;
             vis = vis && key < w1 && (jn < 0 || ((vis_new >> jn) & 1ull));
           }
-          acc_s[rt][kt][j] = vis ? acc_s[rt][kt][j] * a.scale : -INFINITY;
+          acc_s[rt][kt][j] = vis ? acc_s[rt][kt][j] : -INFINITY;
           mt[rt] = fmaxf(mt[rt], acc_s[rt][kt][j]);
         }
     }
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
     // phase 3: probabilities to LDS, each lane's sums.  The reference max of
     // a row moves only when the tile's max passes it by more than
     // kAttnSlack (or on its first visible key): probabilities up to
-    // e^kAttnSlack are exact enough in fp32 and bf16 pairs, and the
+    // 2^kAttnSlack are exact enough in fp32 and bf16 pairs, and the
     // accumulators are rescaled far less often.
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -329,10 +335,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         float4 pv;
-        pv.x = __expf(acc_s[rt][kt][0] - mref);
-        pv.y = __expf(acc_s[rt][kt][1] - mref);
-        pv.z = __expf(acc_s[rt][kt][2] - mref);
-        pv.w = __expf(acc_s[rt][kt][3] - mref);
+        pv.x = __builtin_amdgcn_exp2f(acc_s[rt][kt][0] - mref);
+        pv.y = __builtin_amdgcn_exp2f(acc_s[rt][kt][1] - mref);
+        pv.z = __builtin_amdgcn_exp2f(acc_s[rt][kt][2] - mref);
+        pv.w = __builtin_amdgcn_exp2f(acc_s[rt][kt][3] - mref);
         ps[rt] += (pv.x + pv.y) + (pv.z + pv.w);
         *reinterpret_cast<float4*>(&pbuf[wave][rt * 16 + c][16 * kt + 4 * g]) = pv;
       }
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
     for (int rt = 0; rt < RT; ++rt) {
       float cr = 1.f;
       if (mn[rt] > m[rt]) {
-        cr = m[rt] > -INFINITY ? __expf(m[rt] - mn[rt]) : 0.f;
+        cr = m[rt] > -INFINITY ? __builtin_amdgcn_exp2f(m[rt] - mn[rt]) : 0.f;
         moved = true;
       }
       corr[rt] = cr;
@@ -423,7 +429,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
   const size_t unit = (((size_t)b * a.Hkv + kvh) * a.RG + rg) * (size_t)a.S + split;
   float* po = a.part_o + unit * ROWS * HD;
   float* pml = a.part_ml + unit * ROWS * 2;
-  // per row: the merged max and sum, and each wave's weight exp(m_w - M)
+  // per row: the merged max and sum, and each wave's weight 2^(m_w - M)
   // (0 for a wave that saw none of the row's keys), once per row
   float* ew = mlbuf + kAttnWaves * ROWS * 2;                    // [ROWS][waves]
   for (int r = tid; r < nr; r += kAttnThreads) {
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
       const float mw = mlbuf[(w * ROWS + r) * 2];
-      const float e = M > -INFINITY && mw > -INFINITY ? __expf(mw - M) : 0.f;
+      const float e = M > -INFINITY && mw > -INFINITY ? __builtin_amdgcn_exp2f(mw - M) : 0.f;
       ew[r * kAttnWaves + w] = e;
       lsum += mlbuf[(w * ROWS + r) * 2 + 1] * e;
     }
@@ -475,7 +481,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
 }
 
 // Merge the S partial states of every query row in order: out =
-// sum_p o_p exp(m_p - M) / sum_p l_p exp(m_p - M), M the largest m_p.
+// sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), M the largest m_p (maxima
+// in log2 units).
 // kCombineRows rows per work group, one thread per (row, dimension).  The
 // splits' (m, l) pairs are read once, in parallel, into LDS, and their
 // weights computed there, so the loads of a row's S partial outputs do not
@@ -508,7 +515,7 @@ __global__ __launch_bounds__(HD * kCombineRows) void k_attn_combine(AttnArgs a, 
   if (live) {
     for (int p = d; p < P; p += HD) {
       const float mp = wsh[cr][p];
-      wsh[cr][p] = M > -INFINITY && mp > -INFINITY ? expf(mp - M) : 0.f;
+      wsh[cr][p] = M > -INFINITY && mp > -INFINITY ? __builtin_amdgcn_exp2f(mp - M) : 0.f;
     }
   }
   __syncthreads();

@@ -3,17 +3,19 @@ prefix (spec_decode_attention) and of the KV commit (spec_kv_commit)
 against the float64 oracle (oracle/attention.py).
 
 Tolerance, from the arithmetic: a score is a float32 sum of hd products of
-a float32 query (split exactly into three bf16 terms) and an exact bf16 key,
-so |delta s| <= hd 2^-24 sum_d |q_d k_d| scale; the hardware exp adds a
-relative error of about 2^-23 |x| + 2^-22 for an argument x, the score less
-the row's reference max (at least minus twice the largest |score|, at most
-the kernel's slack of 8 above it); the probabilities enter P V as two bf16
-terms, 2^-16 relative.  The softmax weights then move by at most 2 |delta s|
-+ the exp error + 2^-16, and the output (a convex combination of value rows)
-by that times max |v|.  The test bounds every output row by
+a float32 query, multiplied by scale log2(e) (one rounding, 2^-24 relative)
+and split exactly into three bf16 terms, and an exact bf16 key, so in
+natural units |delta s| <= (hd + 1) 2^-24 sum_d |q_d k_d| scale; the
+hardware exp2 of the score less the row's reference max adds about one ulp
+(2^-23 relative) plus 2^-22 for the denormal range; the probabilities enter
+P V as two bf16 terms, 2^-16 relative.  The softmax weights then move by at
+most 2 |delta s| + the exp error + 2^-16, and the output (a convex
+combination of value rows) by that times max |v|.  The test bounds every
+output row by
     max|v| (2 hd 2^-24 S1 + 2^-23 max(2 S0, 8) + 2^-22 + 2^-16),
 S1 = max_t sum_d |q_d k_d| scale, S0 = max_t |q . k_t| scale, computed
-from the oracle's inputs."""
+from the oracle's inputs; its exp term also covers a natural-base exp
+whose argument is rounded (2^-23 |x| for an argument x)."""
 
 import numpy as np
 import pytest
