@@ -395,7 +395,7 @@ spec_status verify_impl(spec_weights_t w, int32_t B, int32_t gamma, const float*
 // k-step that reach the lowest and highest element of each buffer), for the
 // launch plans verify_impl would choose.  The address formulas are the
 // kernels' own (xs_index is shared with them; the rest restate gemm.hip's
-// k_gemm_mfma, k_gemm_wide, k_epi_wide, k_gemm_fma, run_epilogue and
+// k_gemm_mfma, k_gemm_wide, k_epi_wide, k_epi_wide8, k_gemm_fma, run_epilogue and
 // sample.hip's k_prep line for line).  Nothing is launched.
 struct AccessCheck {
   char* msg = nullptr;
@@ -588,7 +588,8 @@ void check_wide(AccessCheck& C, const char* what, const WidePlan& p, const Mat& 
     check_epilogue(C, what, e, c, L, 0, M, tiles - 4, tiles);
     return;
   }
-  // partial sums P[slice][row][col], then k_epi_wide per (4 tiles, 16 rows)
+  // partial sums P[slice][row][col], then the slice-sum epilogue per 16 rows
+  // (k_epi_wide8: 128 columns for UP and DOWN; k_epi_wide: 4 tiles for LM)
   const int64_t ss = (int64_t)M * W.Np;
   C.range(what, "partial sums (write)", 0, (int64_t)(p.S - 1) * ss + (int64_t)(M - 1) * W.Np + (tiles - 1) * kSub + 15, c.part);
   for (int by = 0; by * 16 < M; by += std::max(1, ((M + 15) / 16) - 1)) {

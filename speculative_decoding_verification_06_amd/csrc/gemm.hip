@@ -769,7 +769,8 @@ __device__ __forceinline__ void wide_lm_epilogue2(const EpiArgs& e, const f32x4 
 // into registers, written to a double-buffered LDS tile, and read back one
 // row tile at a time with ds_read_b128; weights stream into a register
 // ring.  When the column blocks cannot fill the chip, K is split over
-// blockIdx.y and the slices are summed, in slice order, by k_epi_wide.
+// blockIdx.y and the slices are summed, in slice order, by k_epi_wide8 (UP,
+// DOWN) or k_epi_wide (an LM head in slices).
 // TERMS: the bf16 terms of each activation read (3, or 2 with the
 // two-term split, whose third fragment is skipped).
 // Output: fp32 partial sums P[slice][row][col].
@@ -804,7 +805,7 @@ __global__ __launch_bounds__(64 * MG * CG) void k_gemm_wide(WideArgs a, EpiArgs 
   const int nfr = MT * TERMS * 64;
   const bf16x8* XS = reinterpret_cast<const bf16x8*>(a.XS);
   const bf16x8* W = reinterpret_cast<const bf16x8*>(a.W);
-  // UP: 1 / rms of every row once per pass, for k_epi_wide (slice 0's work
+  // UP: 1 / rms of every row once per pass, for the epilogue (slice 0's work
   // groups take 16-row blocks in turn), instead of once per epilogue group
   if (e.kind == EPI_UP && e.rms && blockIdx.y == 0) {
     for (int rb = blockIdx.x; rb * 16 < M; rb += gridDim.x)
