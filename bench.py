@@ -80,8 +80,9 @@ def source_hash():
 
 
 def stored_traffic(workload):
-    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or
-    None when absent or taken on other kernel sources."""
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs (taken
+    with the default GEMM path and activation terms), or None when absent or
+    taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.json")
     try:
         with open(path) as f:
@@ -491,7 +492,9 @@ def main():
     weight_bytes = wbytes / kp
     other = 4 * (B * G1 * wl.d + (B * gamma * wl.V if T > 0 else 0) + B * gamma)
     step_gbs = (weight_bytes + other) / (ms / K / 1e3) / 1e9
-    traffic = stored_traffic(wl.name)
+    # the committed counter runs use the library's default GEMM path and
+    # activation terms; another configuration has no stored reading
+    traffic = stored_traffic(wl.name) if args.gemm == "auto" and not args.exact_split else None
 
     # bf16 terms per fp32 activation on the MFMA path: two for the wide passes
     # of 113 to 224 rows unless the exact split is asked for, else three; the
