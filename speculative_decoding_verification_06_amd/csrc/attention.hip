@@ -12,30 +12,30 @@
 // q[b][i][h][:] (fp32); its key and value sit at slot L_b + i.  Row i sees
 // slots 0 .. L_b - 1 and the new slots of itself and its ancestors.
 //
-// Work decomposition: a work group of 4 waves owns (sequence, KV head, group
-// of up to 64 query rows: new rows x the H / Hkv query heads sharing the KV
-// head, split of the keys); each wave streams its own tiles of 64 keys, so
-// every key and value byte of a split is read once for all query rows of
-// the group (the weight-streaming idea of the GEMMs, applied to the cache).
-// Both products run on bf16 MFMA (16x16x32): the queries are split once
-// into three bf16 terms (exact) and staged in LDS as fragments; the key
-// fragments are loaded straight from the cache; the products are taken
-// transposed (S^T = K Q^T, O^T = V^T P^T), so the scores' softmax runs on
-// the accumulators with each lane owning one query row per row tile (16 of
-// its 64 scores of a key tile in registers, the rest in three other
+// Work decomposition: a work group owns (sequence, KV head, group of up to
+// 128 query rows: new rows x the H / Hkv query heads sharing the KV head,
+// split of the keys); each of its waves owns one 16-row tile of those rows,
+// and the group stages each 64-key tile of keys and values in LDS once for
+// all of them, so every key and value byte of a split is read from memory
+// once for all query rows of the group (the weight-streaming idea of the
+// GEMMs, applied to the cache).  Both products run on bf16 MFMA (16x16x32):
+// a wave's queries are split once into three bf16 terms (exact) and held as
+// B fragments in registers; the products are taken transposed (S^T = K Q^T,
+// O^T = V^T P^T, keys and values as A operands from LDS), so the scores'
+// softmax runs on the accumulators with each lane owning one query row (16
+// of its 64 scores of a key tile in registers, the rest in three other
 // lanes); the probabilities go through LDS into the operand layout, split
-// into two terms (2^-16 relative), against value fragments loaded straight
-// from the head-dimension-major value cache.  Online softmax per row; the four
-// waves' states are merged in LDS and every work group writes one partial
-// (max, sum, unnormalised output); a second kernel merges the splits'
-// partials in a fixed order, so results are run-to-run identical.  The
-// softmax runs in base 2: the queries are multiplied by scale * log2(e)
-// (one fp32 rounding) before they are split, so the accumulators hold
-// scores in log2 units and a probability is the hardware exp2 of a
-// difference (about one ulp), with no multiply per score; the running
-// maxima and the partials' maxima are in the same units.  Both errors are
-// far below the score error of an fp32 128-term dot product that bounds
-// the output.
+// into two terms (2^-16 relative).  Online softmax per row; every wave
+// writes its rows' partial (max, sum, unnormalised output) for the split,
+// and a second kernel merges the splits' partials in a fixed order, so
+// results are run-to-run identical (with one split the output is written
+// directly).  The softmax runs in base 2: the queries are multiplied by
+// scale * log2(e) (one fp32 rounding) before they are split, so the
+// accumulators hold scores in log2 units and a probability is the hardware
+// exp2 of a difference (about one ulp), with no multiply per score; the
+// running maxima and the partials' maxima are in the same units.  Both
+// errors are far below the score error of an fp32 128-term dot product that
+// bounds the output.
 
 #include <algorithm>
 #include <climits>
@@ -50,16 +50,14 @@
 
 namespace sv {
 
-constexpr int kAttnWaves = 4;
-constexpr int kAttnThreads = kAttnWaves * kWave;
-constexpr int kAttnMaxRT = 4;      // 16-row MFMA tiles of query rows per work group (at most)
-constexpr int kAttnTile = 64;      // keys per wave tile: four 16-key MFMA tiles
+constexpr int kAttnMaxRT = 8;      // 16-row tiles of query rows per work group (at most)
+constexpr int kAttnTile = 64;      // keys per tile: four 16-key MFMA tiles
 constexpr float kAttnSlack = 11.5f;  // a row's reference max moves when passed by more (2^11.5 ~ 3e3)
 #ifndef SV_ATTN_WAVES
-#define SV_ATTN_WAVES 1024         // waves a launch aims for (splits of the keys)
+#define SV_ATTN_WAVES 2048         // waves a launch aims for (splits of the keys): two per SIMD
 #endif
 #ifndef SV_ATTN_MIN_TILES
-#define SV_ATTN_MIN_TILES 1        // fewest 64-key tiles per wave
+#define SV_ATTN_MIN_TILES 1        // fewest 64-key tiles per split
 #endif
 constexpr int kAttnMaxSplits = 256;  // splits of the keys (LDS of the combine)
 
@@ -137,27 +135,40 @@ __device__ __forceinline__ bf16x8 zero_past(bf16x8 f, int k0, int end) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Each wave owns one 16-row tile of the group's query rows and streams every
+// key tile of the split; the group stages each 64-key tile of keys and
+// values in LDS once for all its waves (loaded through registers a tile
+// ahead, stored between two barriers).  A wave holds one row tile's
+// accumulators (under 190 registers), so two waves share a SIMD: two
+// four-wave groups per CU up to 64 rows, one eight-wave group up to 128.
+// Each wave's state is final for its rows over the split: no merge across
+// waves.  Tiles in LDS are padded (keys HD + 8, values 64 + 8 bf16 per row)
+// so the 16-byte operand reads of a wave fall in distinct bank groups.
+template <int RT>
+struct AttnGroupWaves { static constexpr int value = RT <= 4 ? 4 : 8; };
+
 template <int HD, int RT>
-__global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
+__global__ __launch_bounds__(64 * AttnGroupWaves<RT>::value) void k_decode_attn(AttnArgs a) {
+  constexpr int NW = AttnGroupWaves<RT>::value, THREADS = 64 * NW;
   constexpr int KS = HD / 32;                      // 32-dimension k-steps of a score
   constexpr int DT = HD / 16;                      // 16-dimension output tiles
-  constexpr int ROWS = 16 * RT;                    // query rows of the work group
-  __shared__ uint64_t anc[64];                     // visible new rows of each new row
-  // the loop's buffers (query A fragments in three terms; each wave's tile
-  // of probabilities), reused after the loop to merge the four waves' states
-  constexpr size_t kLoopBytes = sizeof(bf16x8) * RT * KS * 3 * kWave +
-                                sizeof(float) * kAttnWaves * ROWS * (kAttnTile + 4);
-  constexpr int OLD = HD + 4;                      // merge rows padded a float4: rows c and c + 1 in other banks
-  constexpr size_t kMergeBytes = sizeof(float) * kAttnWaves * ROWS * (OLD + 3);
-  __shared__ __align__(16) unsigned char smem[kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes];
-  auto& qf = *reinterpret_cast<bf16x8 (*)[RT][KS][3][kWave]>(smem);
-  auto& pbuf = *reinterpret_cast<float (*)[kAttnWaves][ROWS][kAttnTile + 4]>(
-      smem + sizeof(bf16x8) * RT * KS * 3 * kWave);
+  constexpr int ROWS = 16 * RT;
+  constexpr int KLD = HD + 8, VLD = kAttnTile + 8; // LDS row strides (bf16)
+  constexpr int KPR = HD / 8, VPR = kAttnTile / 8; // 16-byte chunks per key / value row
+  constexpr int KPT = kAttnTile * KPR / THREADS, VPT = HD * VPR / THREADS;
+  static_assert(KPT * THREADS == kAttnTile * KPR && VPT * THREADS == HD * VPR,
+                "whole 16-byte chunks per thread");
+  __shared__ uint64_t anc[64];
+  __shared__ __align__(16) uint16_t kl[kAttnTile * KLD];
+  __shared__ __align__(16) uint16_t vl[HD * VLD];
+  __shared__ __align__(16) float pbuf[NW][16][kAttnTile + 4];
   const int lane = threadIdx.x & 63, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = blockIdx.x, rg = blockIdx.y % a.RG, kvh = blockIdx.y / a.RG, b = blockIdx.z;
   const int L = attn_len(a, b), T = L + a.n_new;
   const int r0 = rg * ROWS, nr = min(ROWS, a.R - r0);
+  const int g = lane >> 4, c = lane & 15;          // C layout: rows 4 g + j, column c
+  const bool live = wave < RT;                     // waves past the row tiles only load
 
   if (tid == 0) {
     uint64_t m = 0;
@@ -168,17 +179,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
       anc[i] = m;
     }
   }
-  // query fragments: lane L of tile rt, k-step ks holds row rt*16 + L%16 at
-  // dimensions 32 ks + 8 (L/16) .. + 7, as three bf16 terms (rows past the
-  // group are zero)
-  for (int x = tid; x < RT * KS * kWave; x += kAttnThreads) {
-    const int l = x % kWave, ks = (x / kWave) % KS, rt = x / (kWave * KS);
-    const int r = rt * 16 + (l & 15);
+  // this lane's query row (16 wave + c) as B fragments: dimensions
+  // 32 ks + 8 g .. + 7, times scale * log2(e), in three exact bf16 terms
+  const int r = wave * 16 + c;
+  const int rowi = live && r < nr ? (r0 + r) / a.G : -1;
+  bf16x8 qf[KS][3];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
     float v[8];
-    if (r < nr) {
-      const int rr = r0 + r, i = rr / a.G, h = kvh * a.G + rr % a.G;
+    if (rowi >= 0) {
+      const int rr = r0 + r, h = kvh * a.G + rr % a.G;
       const float4* qp = reinterpret_cast<const float4*>(
-          a.q + (((size_t)b * a.n_new + i) * a.H + h) * HD + ks * 32 + 8 * (l >> 4));
+          a.q + (((size_t)b * a.n_new + rowi) * a.H + h) * HD + ks * 32 + 8 * g);
       const float4 u0 = qp[0], u1 = qp[1];
       const float qs = a.scale * 1.44269504088896341f;   // scale * log2(e)
       v[0] = u0.x * qs; v[1] = u0.y * qs; v[2] = u0.z * qs; v[3] = u0.w * qs;
@@ -187,296 +199,165 @@ __global__ __launch_bounds__(kAttnThreads) void k_decode_attn(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = 0.f;
     }
-    bf16x8 f[3];
-    split8(v, f);
-#pragma unroll
-    for (int p = 0; p < 3; ++p) qf[rt][ks][p][l] = f[p];
+    split8(v, qf[ks]);
   }
   __syncthreads();
 
-  // this wave's keys: split `split` of S, quarter `wave` of it, in tiles
+  // this group's keys: split `split` of S, in 64-key tiles
   const int per_split = (((T + a.S - 1) / a.S) + kAttnTile - 1) / kAttnTile * kAttnTile;
   const int s0 = min(T, split * per_split), s1 = min(T, s0 + per_split);
-  const int per_wave = (((s1 - s0) + kAttnWaves - 1) / kAttnWaves + kAttnTile - 1) / kAttnTile * kAttnTile;
-  const int w0 = min(s1, s0 + wave * per_wave), w1 = min(s1, w0 + per_wave);
-
   const uint16_t* K = a.k + ((size_t)b * a.Hkv + kvh) * a.max_seq * HD;
   const uint16_t* Vt = a.vt + ((size_t)b * a.Hkv + kvh) * (size_t)HD * a.max_seq;
-  const int g = lane >> 4, c = lane & 15;          // C layout: rows 4 g + j, column c
 
-  // Both products are taken transposed, S^T = K Q^T and O^T = V^T P^T, so
-  // that in the MFMA output layout (lane (g, c) holds rows 4 g + j of column
-  // c) a lane owns one query row per row tile: query 16 rt + c, at keys
-  // 4 g + j of each 16-key tile (scores) and dimensions 16 dt + 4 g + j
-  // (output).  A row's 64 scores of a tile are then 16 values in a lane and
-  // one value in each of the four lanes c, c + 16, c + 32, c + 48: its max
-  // and sum take two cross-lane steps, and its rescale of the output is the
-  // lane's own factor.  The fragments are the same registers either way:
-  // the key and value fragments serve as A operands, the query and
-  // probability fragments as B operands.
-  float m[RT], l[RT];
-  int rowi[RT];
+  // tile loads: chunk x of the keys is key x / KPR, dimensions 8 (x % KPR);
+  // of the values, dimension x / VPR, keys 8 (x % VPR).  Keys past the
+  // split read its last key; values past it are zeroed when stored.
+  bf16x8 kr[KPT], vr[VPT];
+  auto load_tile = [&](int t) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m[rt] = -INFINITY;
-    l[rt] = 0.f;
-    const int r = rt * 16 + c;
-    rowi[rt] = r < nr ? (r0 + r) / a.G : -1;
-  }
-  f32x4 acc_o[RT][DT];
+    for (int i = 0; i < KPT; ++i) {
+      const int x = tid + i * THREADS, key = min(t + x / KPR, s1 - 1);
+      kr[i] = *reinterpret_cast<const bf16x8*>(K + (size_t)key * HD + 8 * (x % KPR));
+    }
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+    for (int i = 0; i < VPT; ++i) {
+      const int x = tid + i * THREADS;
+      const int k0 = min(t + 8 * (x % VPR), a.max_seq - 8);   // in bounds: max_seq % 8 == 0
+      vr[i] = *reinterpret_cast<const bf16x8*>(Vt + (size_t)(x / VPR) * a.max_seq + k0);
+    }
+  };
+  auto store_tile = [&](int t) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc_o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < KPT; ++i) {
+      const int x = tid + i * THREADS;
+      *reinterpret_cast<bf16x8*>(&kl[(x / KPR) * KLD + 8 * (x % KPR)]) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int x = tid + i * THREADS;
+      *reinterpret_cast<bf16x8*>(&vl[(x / VPR) * VLD + 8 * (x % VPR)]) =
+          zero_past(vr[i], t + 8 * (x % VPR), s1);
+    }
+  };
 
-  // key fragments: key tile kt, k-step ks: lane holds key t + 16 kt + c at
-  // dimensions 32 ks + 8 g .. + 7 (one 16-byte load from the key row)
-  bf16x8 kf[4][KS];
-  auto load_k = [&](int t) {
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc_o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint64_t vis_new = rowi >= 0 ? anc[rowi] : 0ull;
+  if (s0 < s1) load_tile(s0);
+  for (int t = s0; t < s1; t += kAttnTile) {
+    __syncthreads();                                 // the last tile's reads are done
+    store_tile(t);
+    __syncthreads();                                 // this tile is in LDS
+    if (t + kAttnTile < s1) load_tile(t + kAttnTile);
+    if (!live) continue;
+    // scores S^T[key][row] of the four 16-key tiles
+    f32x4 acc_s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) acc_s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 kf[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        kf[kt] = *reinterpret_cast<const bf16x8*>(&kl[(16 * kt + c) * KLD + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          acc_s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt], qf[ks][p], acc_s[kt], 0, 0, 0);
+    }
+    // mask and online softmax of the lane's row (as in k_decode_attn)
+    const bool plain = t + kAttnTile <= min(L, s1);
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bool vis = rowi >= 0;
+        if (!plain) {
+          const int key = t + 16 * kt + 4 * g + j, jn = key - L;
+          vis = vis && key < s1 && (jn < 0 || ((vis_new >> jn) & 1ull));
+        }
+        acc_s[kt][j] = vis ? acc_s[kt][j] : -INFINITY;
+        mt = fmaxf(mt, acc_s[kt][j]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, kWave));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
+    const float mn = m == -INFINITY || mt > m + kAttnSlack ? fmaxf(m, mt) : m;
+    const float mref = mn > -INFINITY ? mn : 0.f;
+    float ps = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const int key = min(t + 16 * kt + c, w1 - 1);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[kt][ks] = *reinterpret_cast<const bf16x8*>(K + (size_t)key * HD + 32 * ks + 8 * g);
+      float4 pv;
+      pv.x = __builtin_amdgcn_exp2f(acc_s[kt][0] - mref);
+      pv.y = __builtin_amdgcn_exp2f(acc_s[kt][1] - mref);
+      pv.z = __builtin_amdgcn_exp2f(acc_s[kt][2] - mref);
+      pv.w = __builtin_amdgcn_exp2f(acc_s[kt][3] - mref);
+      ps += (pv.x + pv.y) + (pv.z + pv.w);
+      *reinterpret_cast<float4*>(&pbuf[wave][c][16 * kt + 4 * g]) = pv;
     }
-  };
-  // value fragments: k-step kv (32 keys), dimension tile dt: lane holds
-  // dimension 16 dt + c at keys t + 32 kv + 8 g .. + 7 (16 bytes of the
-  // head-dimension-major value row).  Plain loads, so they stay in flight
-  // under the next tile's scores; in the wave's last tile the keys past w1
-  // are zeroed where the values are used.
-  bf16x8 vf[2][DT];
-  auto v_first = [&](int t, int kv) { return min(t + 32 * kv + 8 * g, a.max_seq - 8); };
-  auto load_v = [&](int t) {
-#pragma unroll
-    for (int kv = 0; kv < 2; ++kv) {
-      const int kl = v_first(t, kv);               // in bounds (max_seq is a multiple of 8)
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    float cr = 1.f;
+    bool moved = false;
+    if (mn > m) {
+      cr = m > -INFINITY ? __builtin_amdgcn_exp2f(m - mn) : 0.f;
+      moved = true;
+    }
+    l = l * cr + ps;
+    m = mn;
+    if (t != s0 && __any(moved)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        vf[kv][dt] = *reinterpret_cast<const bf16x8*>(Vt + (size_t)(16 * dt + c) * a.max_seq + kl);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc_o[dt][j] *= cr;
     }
-  };
-  // The loads rotate through the tiles: a tile's keys are consumed by the
-  // score MFMAs, after which the next tile's keys are requested; its values
-  // by the P V MFMAs, after which the next tile's values are; so each load
-  // is in flight while the other half of the tile computes.
-  if (w0 < w1) {
-    load_k(w0);
-    load_v(w0);
-  }
-  for (int t = w0; t < w1; t += kAttnTile) {
-    const bool more = t + kAttnTile < w1;
-    // scores S^T[key][row] for the four key tiles and RT row tiles
-    f32x4 acc_s[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) acc_s[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // query fragments stream from LDS two fragments ahead of the MFMAs that
-    // use them (a rolling buffer over (k-step, term, row tile)); the four-
-    // tile kernel has no registers for the buffer and reads each as it goes
-    constexpr int NQ = KS * 3 * RT, QA = RT >= 4 ? 1 : 3;
-    auto qfrag = [&](int n) { return qf[n % RT][n / (3 * RT)][(n / RT) % 3][lane]; };
-    bf16x8 qb[QA];
-#pragma unroll
-    for (int n = 0; n < QA - 1; ++n) qb[n] = qfrag(n);
-#pragma unroll
-    for (int n = 0; n < NQ; ++n) {
-      if (n + QA - 1 < NQ) qb[(n + QA - 1) % QA] = qfrag(n + QA - 1);
-      const int rt = n % RT, ks = n / (3 * RT);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        acc_s[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][ks], qb[n % QA], acc_s[rt][kt], 0, 0, 0);
-    }
-    if (more) load_k(t + kAttnTile);
-    // mask and online softmax per row.  A tile wholly inside this wave's
-    // committed keys is visible to every row (no mask work).
-    const bool plain = t + kAttnTile <= min(L, w1);
-    bool moved = false;                              // some row's running max rose
-    float corr[RT], mt[RT], mn[RT], ps[RT];
-    // phase 1: scaled, masked scores (in place) and each lane's max
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int i = rowi[rt];
-      const uint64_t vis_new = i >= 0 ? anc[i] : 0ull;
-      mt[rt] = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bool vis = i >= 0;
-          if (!plain) {
-            const int key = t + 16 * kt + 4 * g + j, jn = key - L;
-            vis = vis && key < w1 && (jn < 0 || ((vis_new >> jn) & 1ull));
-          }
-          acc_s[rt][kt][j] = vis ? acc_s[rt][kt][j] : -INFINITY;
-          mt[rt] = fmaxf(mt[rt], acc_s[rt][kt][j]);
-        }
-    }
-    // phase 2: row maxima over the four lanes of a row, every row tile's
-    // exchange in flight together
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 16, kWave));
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) mt[rt] = fmaxf(mt[rt], __shfl_xor(mt[rt], 32, kWave));
-    // phase 3: probabilities to LDS, each lane's sums.  The reference max of
-    // a row moves only when the tile's max passes it by more than
-    // kAttnSlack (or on its first visible key): probabilities up to
-    // 2^kAttnSlack are exact enough in fp32 and bf16 pairs, and the
-    // accumulators are rescaled far less often.
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      mn[rt] = m[rt] == -INFINITY || mt[rt] > m[rt] + kAttnSlack ? fmaxf(m[rt], mt[rt]) : m[rt];
-      ps[rt] = 0.f;
-      // exp(-inf - M) = 0 for a masked key; a row with nothing visible yet
-      // subtracts 0 instead of -inf, so its masked keys also give 0
-      const float mref = mn[rt] > -INFINITY ? mn[rt] : 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        float4 pv;
-        pv.x = __builtin_amdgcn_exp2f(acc_s[rt][kt][0] - mref);
-        pv.y = __builtin_amdgcn_exp2f(acc_s[rt][kt][1] - mref);
-        pv.z = __builtin_amdgcn_exp2f(acc_s[rt][kt][2] - mref);
-        pv.w = __builtin_amdgcn_exp2f(acc_s[rt][kt][3] - mref);
-        ps[rt] += (pv.x + pv.y) + (pv.z + pv.w);
-        *reinterpret_cast<float4*>(&pbuf[wave][rt * 16 + c][16 * kt + 4 * g]) = pv;
-      }
-    }
-    // phase 4: row sums, the running state
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) ps[rt] += __shfl_xor(ps[rt], 16, kWave);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) ps[rt] += __shfl_xor(ps[rt], 32, kWave);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float cr = 1.f;
-      if (mn[rt] > m[rt]) {
-        cr = m[rt] > -INFINITY ? __builtin_amdgcn_exp2f(m[rt] - mn[rt]) : 0.f;
-        moved = true;
-      }
-      corr[rt] = cr;
-      l[rt] = l[rt] * cr + ps[rt];
-      m[rt] = mn[rt];
-    }
-    // rescale the output accumulators only when some row's max rose (the
-    // accumulators live in the MFMA registers, so a rescale is a round trip);
-    // never after a wave's first tile, whose accumulators are still zero
-    if (t != w0 && __any(moved)) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc_o[rt][dt][j] *= corr[rt];
-    }
-    // the tile's probabilities are read back below in the operand layout
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // the wave's last tile: values of keys past w1 are zeroed (memory past
-    // the visible keys may hold anything, even non-finite bits)
-    if (t + kAttnTile > w1) {
+    // O^T += V^T P^T, P in two bf16 terms (2^-16 relative)
 #pragma unroll
-      for (int kv = 0; kv < 2; ++kv)
+    for (int kv = 0; kv < 2; ++kv) {
+      const float4* pp = reinterpret_cast<const float4*>(&pbuf[wave][c][32 * kv + 8 * g]);
+      const float4 u0 = pp[0], u1 = pp[1];
+      const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      bf16x8 pf[2];
+      split8_2(x, pf);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vf[kv][dt] = zero_past(vf[kv][dt], v_first(t, kv), w1);
-    }
-    // O^T += V^T P^T: P's B fragments (row 16 rt + c, keys 32 kv + 8 g ..
-    // + 7), split into two bf16 terms (probabilities to 2^-16 relative)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int kv = 0; kv < 2; ++kv) {
-        const float4* pp = reinterpret_cast<const float4*>(&pbuf[wave][rt * 16 + c][32 * kv + 8 * g]);
-        const float4 u0 = pp[0], u1 = pp[1];
-        const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        bf16x8 pf[2];
-        split8_2(x, pf);
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vl[(16 * dt + c) * VLD + 32 * kv + 8 * g]);
 #pragma unroll
         for (int p = 0; p < 2; ++p)
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            acc_o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kv][dt], pf[p], acc_o[rt][dt], 0, 0, 0);
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[p], acc_o[dt], 0, 0, 0);
       }
-    if (more) load_v(t + kAttnTile);
-    // every lane has read the tile's probabilities before the next tile's
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-
-  // merge the four waves' states in LDS (the loop buffers are free now),
-  // in wave order, and write one partial per work group: row 16 rt + c,
-  // dimensions 16 dt + 4 g + j
-  __syncthreads();
-  float* obuf = reinterpret_cast<float*>(smem);                 // [waves][ROWS][OLD]
-  float* mlbuf = obuf + (size_t)kAttnWaves * ROWS * OLD;        // [waves][ROWS][2]
+  // the rows' states over this split: lane (g, c) holds row r at dimensions
+  // 16 dt + 4 g + j; with one split, the output o / l itself
+  if (!live || r >= nr) return;
+  if (a.S == 1) {
+    const int rr = r0 + r, h = kvh * a.G + rr % a.G;
+    float* out = a.out + (((size_t)b * a.n_new + rowi) * a.H + h) * HD;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = rt * 16 + c;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const float4 o = {acc_o[rt][dt][0], acc_o[rt][dt][1], acc_o[rt][dt][2], acc_o[rt][dt][3]};
-      *reinterpret_cast<float4*>(&obuf[((size_t)wave * ROWS + r) * OLD + 16 * dt + 4 * g]) = o;
-    }
-    if (g == 0) {
-      mlbuf[(wave * ROWS + r) * 2] = m[rt];
-      mlbuf[(wave * ROWS + r) * 2 + 1] = l[rt];
-    }
+      for (int j = 0; j < 4; ++j) out[16 * dt + 4 * g + j] = l > 0.f ? acc_o[dt][j] / l : 0.f;
+    return;
   }
-  __syncthreads();
   const size_t unit = (((size_t)b * a.Hkv + kvh) * a.RG + rg) * (size_t)a.S + split;
-  float* po = a.part_o + unit * ROWS * HD;
-  float* pml = a.part_ml + unit * ROWS * 2;
-  // per row: the merged max and sum, and each wave's weight 2^(m_w - M)
-  // (0 for a wave that saw none of the row's keys), once per row
-  float* ew = mlbuf + kAttnWaves * ROWS * 2;                    // [ROWS][waves]
-  for (int r = tid; r < nr; r += kAttnThreads) {
-    float M = -INFINITY;
+  float* po = a.part_o + (unit * ROWS + r) * HD;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mlbuf[(w * ROWS + r) * 2]);
-    float lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
-      const float mw = mlbuf[(w * ROWS + r) * 2];
-      const float e = M > -INFINITY && mw > -INFINITY ? __builtin_amdgcn_exp2f(mw - M) : 0.f;
-      ew[r * kAttnWaves + w] = e;
-      lsum += mlbuf[(w * ROWS + r) * 2 + 1] * e;
-    }
-    if (a.S == 1) {
-      mlbuf[2 * r + 1] = lsum;                 // wave 0's slot of the row: read below
-    } else {
-      pml[2 * r] = M;
-      pml[2 * r + 1] = lsum;
-    }
-  }
-  __syncthreads();
-  // the merged rows, four dimensions per thread; with one split the merged
-  // row is the output itself, o / l (the combine's weight would be exactly 1)
-  constexpr int HD4 = HD / 4;
-  const float4* ob4 = reinterpret_cast<const float4*>(obuf);
-  float4* po4 = reinterpret_cast<float4*>(po);
-  for (int x = tid; x < nr * HD4; x += kAttnThreads) {
-    const int r = x / HD4, d4 = x - r * HD4;
-    float4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
-      const float e = ew[r * kAttnWaves + w];
-      const float4 v = ob4[((size_t)w * ROWS + r) * (OLD / 4) + d4];
-      o.x += v.x * e; o.y += v.y * e; o.z += v.z * e; o.w += v.w * e;
-    }
-    if (a.S == 1) {
-      const float den = mlbuf[2 * r + 1];
-      const int rr = r0 + r, i = rr / a.G, h = kvh * a.G + rr % a.G;
-      float* out = a.out + (((size_t)b * a.n_new + i) * a.H + h) * HD + 4 * d4;
-      out[0] = den > 0.f ? o.x / den : 0.f;
-      out[1] = den > 0.f ? o.y / den : 0.f;
-      out[2] = den > 0.f ? o.z / den : 0.f;
-      out[3] = den > 0.f ? o.w / den : 0.f;
-    } else {
-      po4[r * HD4 + d4] = o;
-    }
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<float4*>(&po[16 * dt + 4 * g]) =
+        make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+  if (g == 0) {
+    a.part_ml[(unit * ROWS + r) * 2] = m;
+    a.part_ml[(unit * ROWS + r) * 2 + 1] = l;
   }
 }
 
@@ -602,19 +483,18 @@ AttnShape attn_shape(int B, int n_new, int H, int Hkv, int hd, int max_seq) {
   AttnShape s;
   const int G = H / Hkv;
   s.R = n_new * G;
-  // row tiles per work group: all rows in one group up to 64 (every key and
-  // value byte read once for them), else groups of 64
+  // row tiles per work group: all rows in one group up to 128 (every key and
+  // value byte read once for them), else groups of 128
   s.RT = std::min(kAttnMaxRT, (s.R + 15) / 16);
   s.RG = (s.R + 16 * s.RT - 1) / (16 * s.RT);
-  // splits of the keys: about SV_ATTN_WAVES waves over the chip, but at
-  // least SV_ATTN_MIN_TILES 64-key tiles per wave (a wave's partial state,
-  // 16 RT x hd floats, against the keys and values it streams; one tile per
-  // wave measured faster than two once the combine read its splits'
-  // partials in parallel: B = 1, 8192 keys, 27.8 -> 23.5 us)
+  // splits of the keys: about SV_ATTN_WAVES waves over the chip (two per
+  // SIMD: 1024 and 4096 measured slower, and 1536 and 3072 as well, on
+  // B = 4 tree rows), but at least SV_ATTN_MIN_TILES 64-key tiles per split
   const int groups = B * Hkv * s.RG;
   const int tiles = (max_seq + kAttnTile - 1) / kAttnTile;
-  const int want = (SV_ATTN_WAVES + groups * kAttnWaves - 1) / (groups * kAttnWaves);
-  const int most = std::max(1, tiles / (SV_ATTN_MIN_TILES * kAttnWaves));
+  const int nw = s.RT <= 4 ? 4 : 8;                 // waves of a group (AttnGroupWaves)
+  const int want = (SV_ATTN_WAVES + groups * nw - 1) / (groups * nw);
+  const int most = std::max(1, tiles / SV_ATTN_MIN_TILES);
   s.S = std::max(1, std::min(std::min(want, most), kAttnMaxSplits));
   const size_t units = (size_t)groups * s.S;
   const size_t rows = (size_t)16 * s.RT;
@@ -665,7 +545,7 @@ spec_status spec_decode_attention(int32_t B, int32_t n_new, int32_t H, int32_t H
   const dim3 grid(s.S, Hkv * s.RG, B), cgrid(16 * s.RT / kCombineRows, Hkv * s.RG, B);
   auto go = [&](auto hd_tag, auto rt_tag) {
     constexpr int HDc = decltype(hd_tag)::value, RTc = decltype(rt_tag)::value;
-    hipLaunchKernelGGL((k_decode_attn<HDc, RTc>), grid, dim3(kAttnThreads), 0, st, a);
+    hipLaunchKernelGGL((k_decode_attn<HDc, RTc>), grid, dim3(64 * AttnGroupWaves<RTc>::value), 0, st, a);
     if (s.S > 1)
       hipLaunchKernelGGL(k_attn_combine<HDc>, cgrid, dim3(HDc * kCombineRows), 0, st, a, 16 * RTc);
   };
@@ -674,7 +554,11 @@ spec_status spec_decode_attention(int32_t B, int32_t n_new, int32_t H, int32_t H
       case 1: go(hd_tag, std::integral_constant<int, 1>{}); break;
       case 2: go(hd_tag, std::integral_constant<int, 2>{}); break;
       case 3: go(hd_tag, std::integral_constant<int, 3>{}); break;
-      default: go(hd_tag, std::integral_constant<int, 4>{}); break;
+      case 4: go(hd_tag, std::integral_constant<int, 4>{}); break;
+      case 5: go(hd_tag, std::integral_constant<int, 5>{}); break;
+      case 6: go(hd_tag, std::integral_constant<int, 6>{}); break;
+      case 7: go(hd_tag, std::integral_constant<int, 7>{}); break;
+      default: go(hd_tag, std::integral_constant<int, 8>{}); break;
     }
   };
   if (head_dim == 128) by_rt(std::integral_constant<int, 128>{});
