@@ -364,7 +364,8 @@ __global__ __launch_bounds__(64 * AttnGroupWaves<RT>::value) void k_decode_attn(
 // Merge the S partial states of every query row in order: out =
 // sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), M the largest m_p (maxima
 // in log2 units).
-// kCombineRows rows per work group, one thread per (row, dimension).  The
+// kCombineRows rows per work group, one thread per (row, dimension) or per
+// (row, four dimensions).  The
 // splits' (m, l) pairs are read once, in parallel, into LDS, and their
 // weights computed there, so the loads of a row's S partial outputs do not
 // depend on one another and stay in flight together; the sums still run in
@@ -372,10 +373,12 @@ __global__ __launch_bounds__(64 * AttnGroupWaves<RT>::value) void k_decode_attn(
 // m = -inf, l = 0), so a weight of 0 adds exactly 0.  Launched only when
 // S > 1; with one split the attention writes the output itself.
 constexpr int kCombineRows = 4;
-template <int HD>
-__global__ __launch_bounds__(HD * kCombineRows) void k_attn_combine(AttnArgs a, int rows) {
+template <int HD, int DPT>
+__global__ __launch_bounds__(HD / DPT * kCombineRows) void k_attn_combine(AttnArgs a, int rows) {
+  static_assert(DPT == 1 || DPT == 4, "one or four dimensions per thread");
+  constexpr int TR = HD / DPT;                   // threads per row
   __shared__ float wsh[kCombineRows][kAttnMaxSplits], lsh[kCombineRows][kAttnMaxSplits];
-  const int d = threadIdx.x % HD, cr = threadIdx.x / HD;
+  const int dq = threadIdx.x % TR, cr = threadIdx.x / TR;
   const int r = blockIdx.x * kCombineRows + cr, rg = blockIdx.y % a.RG, kvh = blockIdx.y / a.RG,
             b = blockIdx.z;
   const int rr = rg * rows + r;
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(HD * kCombineRows) void k_attn_combine(AttnArgs a, 
   const int P = a.S;
   const size_t unit0 = (((size_t)b * a.Hkv + kvh) * a.RG + rg) * (size_t)P;
   if (live) {
-    for (int p = d; p < P; p += HD) {
+    for (int p = dq; p < P; p += TR) {
       wsh[cr][p] = a.part_ml[((unit0 + p) * rows + r) * 2];
       lsh[cr][p] = a.part_ml[((unit0 + p) * rows + r) * 2 + 1];
     }
@@ -394,7 +397,7 @@ __global__ __launch_bounds__(HD * kCombineRows) void k_attn_combine(AttnArgs a, 
     for (int p = 0; p < P; ++p) M = fmaxf(M, wsh[cr][p]);
   __syncthreads();
   if (live) {
-    for (int p = d; p < P; p += HD) {
+    for (int p = dq; p < P; p += TR) {
       const float mp = wsh[cr][p];
       wsh[cr][p] = M > -INFINITY && mp > -INFINITY ? __builtin_amdgcn_exp2f(mp - M) : 0.f;
     }
@@ -403,20 +406,34 @@ __global__ __launch_bounds__(HD * kCombineRows) void k_attn_combine(AttnArgs a, 
   if (!live) return;
   float den = 0.f;
   for (int p = 0; p < P; ++p) den += lsh[cr][p] * wsh[cr][p];
-  const float* po = a.part_o + unit0 * rows * HD + (size_t)r * HD + d;
-  const size_t step = (size_t)rows * HD;
-  float num = 0.f;
+  // the partial rows sit in the workspace (256-byte aligned): with four
+  // dimensions per thread, 16-byte loads
+  using V = typename std::conditional<DPT == 4, float4, float>::type;
+  const V* po = reinterpret_cast<const V*>(a.part_o + unit0 * rows * HD + (size_t)r * HD) + dq;
+  const size_t step = (size_t)rows * TR;
+  float num[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) num[e] = 0.f;
+  auto add = [&](const V& o, float w) {
+    if constexpr (DPT == 4) {
+      num[0] += o.x * w; num[1] += o.y * w; num[2] += o.z * w; num[3] += o.w * w;
+    } else {
+      num[0] += o * w;
+    }
+  };
   int p = 0;
   for (; p + 8 <= P; p += 8) {
-    float o[8];
+    V o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = po[(p + j) * step];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) num += o[j] * wsh[cr][p + j];
+    for (int j = 0; j < 8; ++j) add(o[j], wsh[cr][p + j]);
   }
-  for (; p < P; ++p) num += po[p * step] * wsh[cr][p];
+  for (; p < P; ++p) add(po[p * step], wsh[cr][p]);
   const int i = rr / a.G, h = kvh * a.G + rr % a.G;
-  a.out[(((size_t)b * a.n_new + i) * a.H + h) * HD + d] = den > 0.f ? num / den : 0.f;
+  float* out = a.out + (((size_t)b * a.n_new + i) * a.H + h) * HD + DPT * dq;
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) out[e] = den > 0.f ? num[e] / den : 0.f;
 }
 
 // ---------------------------------------------------------------- commit
@@ -546,8 +563,12 @@ spec_status spec_decode_attention(int32_t B, int32_t n_new, int32_t H, int32_t H
   auto go = [&](auto hd_tag, auto rt_tag) {
     constexpr int HDc = decltype(hd_tag)::value, RTc = decltype(rt_tag)::value;
     hipLaunchKernelGGL((k_decode_attn<HDc, RTc>), grid, dim3(64 * AttnGroupWaves<RTc>::value), 0, st, a);
-    if (s.S > 1)
-      hipLaunchKernelGGL(k_attn_combine<HDc>, cgrid, dim3(HDc * kCombineRows), 0, st, a, 16 * RTc);
+    // few splits: four dimensions per thread (fewer, fuller work groups);
+    // many: one, so more loads of a row's partials are in flight at once
+    if (s.S > 16)
+      hipLaunchKernelGGL((k_attn_combine<HDc, 1>), cgrid, dim3(HDc * kCombineRows), 0, st, a, 16 * RTc);
+    else if (s.S > 1)
+      hipLaunchKernelGGL((k_attn_combine<HDc, 4>), cgrid, dim3(HDc / 4 * kCombineRows), 0, st, a, 16 * RTc);
   };
   auto by_rt = [&](auto hd_tag) {
     switch (s.RT) {
