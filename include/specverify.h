@@ -348,8 +348,9 @@ size_t spec_attention_workspace_size(int32_t B, int32_t n_new, int32_t H, int32_
  *   workspace  spec_attention_workspace_size bytes, 256-byte aligned
  * Shapes: 1 <= n_new <= 64, H a multiple of Hkv, hd 64 or 128, max_seq a
  * multiple of 8, caches 16-byte aligned; SPEC_EINVAL / SPEC_EWORKSPACE
- * otherwise.  Both products run on bf16 MFMA with the queries and the
- * probabilities split into three bf16 terms (exact).  Results are
+ * otherwise.  Both products run on bf16 MFMA: the queries (times
+ * scale * log2(e), the softmax running in base 2) split into three bf16
+ * terms (exact), the probabilities into two (2^-16 relative).  Results are
  * run-to-run identical (no atomics; partials merged in a fixed order). */
 spec_status spec_decode_attention(int32_t B, int32_t n_new, int32_t H, int32_t Hkv,
                                   int32_t head_dim, int32_t max_seq, const float* q,
