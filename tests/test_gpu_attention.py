@@ -64,7 +64,7 @@ CASES = [
     ("rows-over-32-tree", 3, 40, 8, 2, 128, 1200, [1000, 5, 300], True),
     ("mha-g1", 2, 3, 4, 4, 64, 96, [93, 40], True),
     ("one-row-cache-end", 2, 1, 8, 8, 128, 72, [71, 70], False),
-    ("splits-13", 1, 5, 64, 8, 128, 832, [800], False),
+    ("splits-13", 1, 5, 64, 8, 128, 3328, [3300], False),
     ("splits-256-hd64", 1, 5, 4, 1, 64, 131072, [131000], False),
     ("rt3-chain-hd64", 2, 6, 32, 4, 64, 2048, [1500, 2040], False),
     ("rt4-tree-padded", 3, 9, 48, 8, 128, 1024, [0, 500, 1015], True),
@@ -72,16 +72,18 @@ CASES = [
     ("one-tile-cache", 2, 3, 8, 4, 128, 64, [60, 10], False),
     ("rt5-chain", 2, 10, 64, 8, 128, 640, [600, 3], False),
 ]
-# The launch splits each row's keys S ways and merges the splits in a second
-# launch when S > 1 (S = 1 writes the output directly: one-tile-cache).  A
-# work group holds 16-row tiles of rows, one per wave (four waves up to 64
+# The launch splits each row's keys S ways (at least four 64-key tiles per
+# split) and merges the splits in a second launch when S > 1; S = 1 writes the
+# output directly (chain-g4-short, mha-g1, one-row-cache-end, one-tile-cache).
+# A work group holds 16-row tiles of rows, one per wave (four waves up to 64
 # rows, eight up to 128): one tile in mha-g1, one-row-cache-end, rt1-g2 and
 # one-tile-cache, two in chain-g4-short, batch-hd64 and splits-256-hd64,
 # three in chain-g8-8k, splits-13 and rt3-chain-hd64, four in rt4-tree-padded
 # (padding rows), five in rt5-chain (three waves that only load), eight in
-# tree-15-g8 and in rows-over-32-tree (two row groups).  S = 13 in splits-13
-# (the merge's groups of eight plus a tail), 256 in splits-256-hd64 (more
-# splits than the merge has threads per row).
+# tree-15-g8 and in rows-over-32-tree (two row groups).  The merge takes four
+# dimensions per thread up to 16 splits (2 to 11 here) and one above (32 in
+# chain-g8-8k, 256 in splits-256-hd64: more splits than threads per row);
+# S = 13 in splits-13 (its groups of eight loads plus a tail).
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
