@@ -82,13 +82,15 @@ int gemm_path(const spec_weights* w, int M) {
   return (M >= w->mfma_min_rows || !have_rm) ? PATH_MFMA : PATH_FMA_BF16;
 }
 
-// Whether a pass of M rows carries its activations as two bf16 terms:
-// passes the wide GEMM serves from kTwoTermMinRows rows on, unless the
-// weights were registered with SPEC_FLAG_EXACT_SPLIT.  Every producer of
-// the pass splits alike.
+// Whether a pass of M rows carries its activations as two bf16 terms: every
+// pass the wide GEMM serves, unless the weights were registered with
+// SPEC_FLAG_EXACT_SPLIT.  The wide k-loop's chain of activation loads, LDS
+// reads and matrix operations per k-step then shrinks by a third (measured
+// 10.6% of a 72-row top-p pass and 14-21% of B = 1 passes of 65 to 97 rows);
+// the stacked passes of up to 10 rows keep three exact terms, which cost no
+// extra matrix operation there.  Every producer of the pass splits alike.
 bool two_term(const spec_weights* w, int M, int path) {
-  return !(w->flags & SPEC_FLAG_EXACT_SPLIT) && path == PATH_MFMA && wide_rows(M) &&
-         M >= kTwoTermMinRows;
+  return !(w->flags & SPEC_FLAG_EXACT_SPLIT) && path == PATH_MFMA && wide_rows(M);
 }
 
 // Statistics units per logits row: one per LM-head work group (nt tiles of

@@ -6,9 +6,11 @@
 // lattice-ai-eng.pages.dev: the single target call over k+1 positions is one
 // weight read; "Speculative Decoding: Speeding Sequential Generation",
 // aicomputerinstitute.com, Why Generation Is Slow: A Roofline View).  Each
-// weight byte is read from HBM once; activations stay fp32-exact (MFMA
-// path: three bf16 terms per value, split once by the kernel that produces
-// them) so the logits track a float64 reference.
+// weight byte is read from HBM once; activations are split once, by the
+// kernel that produces them, into bf16 terms for the MFMA path: three exact
+// terms in the stacked passes of up to 10 rows, two rounded ones (2^-16
+// relative) in the wide passes unless the exact split is asked for, so the
+// logits track a float64 reference.
 //
 // Work decomposition: a work group owns NT MFMA column tiles (16 columns
 // each) over the whole K range.  Its waves are MG row groups x KG k-groups;
@@ -1259,7 +1261,7 @@ GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack) {
 WidePlan plan_wide(int M, const Mat& m, bool two_term) {
   WidePlan p;
   p.MT = (M + 15) / 16;
-  p.terms = two_term && M >= kTwoTermMinRows ? 2 : 3;
+  p.terms = two_term ? 2 : 3;
   // two row groups x 4 column groups of 4 tiles = 16 column tiles, 8 waves
   p.mtw = (p.MT + 1) / 2;
   p.mg = 2; p.ntc = 4; p.cg = 4;
@@ -1314,7 +1316,7 @@ WidePlan plan_wide(int M, const Mat& m, bool two_term) {
   return p;
 }
 
-template <int MTW, int NTC, int MG, int CG, int RING = (MTW >= 5 ? 2 : 4), int TERMS = 3>
+template <int MTW, int NTC, int MG, int CG, int RING, int TERMS>
 static void launch_wide_t(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
                           hipEvent_t e0, hipEvent_t e1) {
   // the double-buffered activation tile can exceed the default 64 KiB
@@ -1326,49 +1328,49 @@ static void launch_wide_t(const WidePlan& p, const WideArgs& a, const EpiArgs& e
                         dim3(64 * MG * CG), p.lds, st, e0, e1, 0, a, e);
 }
 
+template <int TERMS>
+static void launch_wide_terms(const WidePlan& p, const WideArgs& a, const EpiArgs& e, hipStream_t st,
+                              hipEvent_t e0, hipEvent_t e1) {
+  if (p.mg == 1 && p.cg == 16) {
+    switch (p.mtw) {
+      case 1: launch_wide_t<1, 2, 1, 16, 4, TERMS>(p, a, e, st, e0, e1); break;
+      case 2: launch_wide_t<2, 2, 1, 16, 4, TERMS>(p, a, e, st, e0, e1); break;
+      case 3: launch_wide_t<3, 2, 1, 16, 4, TERMS>(p, a, e, st, e0, e1); break;
+      case 4: launch_wide_t<4, 2, 1, 16, 4, TERMS>(p, a, e, st, e0, e1); break;
+      default: launch_wide_t<5, 2, 1, 16, 2, TERMS>(p, a, e, st, e0, e1); break;
+    }
+  } else if (p.mg == 1) {
+    switch (p.mtw) {
+      case 1: launch_wide_t<1, 2, 1, 8, 4, TERMS>(p, a, e, st, e0, e1); break;
+      case 2: launch_wide_t<2, 2, 1, 8, 4, TERMS>(p, a, e, st, e0, e1); break;
+      case 3: launch_wide_t<3, 2, 1, 8, 4, TERMS>(p, a, e, st, e0, e1); break;
+      case 4: launch_wide_t<4, 2, 1, 8, 4, TERMS>(p, a, e, st, e0, e1); break;
+      default:
+        // a 4-deep ring takes 137 registers with three terms: one group per
+        // CU.  Where more groups than CUs are launched, two groups per CU
+        // with a 2-deep ring stream faster (measured on a 501-group LM
+        // head, now launched in the 1024-thread shape above).
+        if (p.colblocks * p.S > SV_MIN_BLOCKS) launch_wide_t<5, 2, 1, 8, 2, TERMS>(p, a, e, st, e0, e1);
+        else launch_wide_t<5, 2, 1, 8, 4, TERMS>(p, a, e, st, e0, e1);
+        break;
+    }
+  } else {
+    switch (p.mtw) {   // 6 to 14 row tiles in two row groups: mtw = 3 .. 7
+      case 3: launch_wide_t<3, 4, 2, 4, 4, TERMS>(p, a, e, st, e0, e1); break;
+      case 4: launch_wide_t<4, 4, 2, 4, 4, TERMS>(p, a, e, st, e0, e1); break;
+      case 5: launch_wide_t<5, 4, 2, 4, 2, TERMS>(p, a, e, st, e0, e1); break;
+      case 6: launch_wide_t<6, 4, 2, 4, 2, TERMS>(p, a, e, st, e0, e1); break;
+      default: launch_wide_t<7, 4, 2, 4, 2, TERMS>(p, a, e, st, e0, e1); break;
+    }
+  }
+}
+
 hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e, hipStream_t st,
                        hipEvent_t e0, hipEvent_t e1) {
   WideArgs a = a_in;
   a.fuse_lm = p.S == 1 && e.kind == EPI_LM;
-  if (p.mg == 1 && p.cg == 16) {
-    switch (p.mtw) {
-      case 1: launch_wide_t<1, 2, 1, 16>(p, a, e, st, e0, e1); break;
-      case 2: launch_wide_t<2, 2, 1, 16>(p, a, e, st, e0, e1); break;
-      case 3: launch_wide_t<3, 2, 1, 16>(p, a, e, st, e0, e1); break;
-      case 4: launch_wide_t<4, 2, 1, 16>(p, a, e, st, e0, e1); break;
-      default: launch_wide_t<5, 2, 1, 16, 2>(p, a, e, st, e0, e1); break;
-    }
-  } else if (p.mg == 1) {
-    switch (p.mtw) {
-      case 1: launch_wide_t<1, 2, 1, 8>(p, a, e, st, e0, e1); break;
-      case 2: launch_wide_t<2, 2, 1, 8>(p, a, e, st, e0, e1); break;
-      case 3: launch_wide_t<3, 2, 1, 8>(p, a, e, st, e0, e1); break;
-      case 4: launch_wide_t<4, 2, 1, 8>(p, a, e, st, e0, e1); break;
-      default:
-        // a 4-deep ring takes 137 registers: one group per CU.  Where
-        // more groups than CUs are launched, two groups per CU with a
-        // 2-deep ring stream faster (measured on a 501-group LM head, now
-        // launched in the 1024-thread shape above).
-        if (p.colblocks * p.S > SV_MIN_BLOCKS) launch_wide_t<5, 2, 1, 8, 2>(p, a, e, st, e0, e1);
-        else launch_wide_t<5, 2, 1, 8, 4>(p, a, e, st, e0, e1);
-        break;
-    }
-  } else if (p.terms == 2) {
-    switch (p.mtw) {   // 113 to 224 rows: 8 to 14 row tiles, mtw = 4 .. 7
-    case 4: launch_wide_t<4, 4, 2, 4, 4, 2>(p, a, e, st, e0, e1); break;
-    case 5: launch_wide_t<5, 4, 2, 4, 2, 2>(p, a, e, st, e0, e1); break;
-    case 6: launch_wide_t<6, 4, 2, 4, 2, 2>(p, a, e, st, e0, e1); break;
-    default: launch_wide_t<7, 4, 2, 4, 2, 2>(p, a, e, st, e0, e1); break;
-    }
-  } else {
-    switch (p.mtw) {   // 6 to 14 row tiles: mtw = 3 .. 7
-    case 3: launch_wide_t<3, 4, 2, 4>(p, a, e, st, e0, e1); break;
-    case 4: launch_wide_t<4, 4, 2, 4>(p, a, e, st, e0, e1); break;
-    case 5: launch_wide_t<5, 4, 2, 4>(p, a, e, st, e0, e1); break;
-    case 6: launch_wide_t<6, 4, 2, 4>(p, a, e, st, e0, e1); break;
-    default: launch_wide_t<7, 4, 2, 4>(p, a, e, st, e0, e1); break;
-    }
-  }
+  if (p.terms == 2) launch_wide_terms<2>(p, a, e, st, e0, e1);
+  else launch_wide_terms<3>(p, a, e, st, e0, e1);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.fuse_lm) return err;
   if (e.kind == EPI_LM)

@@ -133,9 +133,6 @@ struct WideArgs {
                               // logits and unit statistics, P is unused
 };
 WidePlan plan_wide(int M, const Mat& m, bool two_term);
-// Wide passes of at least this many rows take the two-term split unless
-// SPEC_FLAG_EXACT_SPLIT: the wide GEMM is bound by its matrix operations there.
-constexpr int kTwoTermMinRows = 113;
 // Row counts the wide GEMM serves: the plain packing up to one 224-row chunk.
 inline bool wide_rows(int M) { return !xs_stacked(M) && M <= 224; }
 // The GEMM (timed by e0 / e1 when given) and then its epilogue kernel; an

@@ -5,9 +5,9 @@ spec_diag_access_check evaluates the kernels' address formulas at the
 extremes of their index ranges for the launch plans spec_verify would take
 and checks them against the buffers spec_workspace_size lays out and the
 registered weight layouts.  It covers every row count the GEMM paths serve
-(1 .. 448 rows: stacked MFMA up to 10, wide MFMA 11 .. 224 with three or,
-from 113 rows unless the exact split is asked for, two activation terms,
-chunked plain MFMA beyond; and the vector-FMA paths), the five workload shapes, and the
+(1 .. 448 rows: stacked MFMA up to 10, wide MFMA 11 .. 224 with two
+activation terms, or three when the exact split is asked for, chunked plain
+MFMA beyond; and the vector-FMA paths), the five workload shapes, and the
 shapes the GPU parity tests run.  A planted inconsistency (workspace
 buffers one fragment short) must be caught, so the check is not vacuous."""
 
@@ -75,17 +75,18 @@ def test_parity_test_shapes():
 
 def test_exact_split_row_counts():
     """The row counts where the default reads two of the three fragments of
-    each row tile (113 .. 224), with the exact three-term split kept
-    instead, and a short workspace caught either way."""
+    each row tile (the wide GEMM's 11 .. 224), with the exact three-term
+    split kept instead, and a short workspace caught either way."""
     for (d, ffn, nb, V) in [(8192, 28672, 1, 128256), (200, 300, 2, 1000), (160, 288, 1, 700)]:
-        for M in range(100, 229):
+        for M in range(1, 229):
             check(d, ffn, nb, V, BF16, M, 0, exact_split=True)
-    g = synth.WORKLOADS["greedy"]
-    check(g.d, g.ffn, g.n_blocks, g.V, BF16, g.B, g.gamma, exact_split=True)
-    for exact in (False, True):
-        st, msg, _ = sv.access_check(g.d, g.ffn, g.n_blocks, g.V, BF16, g.B, g.gamma,
-                                     shrink_bytes=16, exact_split=exact)
-        assert st == sv.SPEC_EINVAL and "outside" in msg
+    for name in ("topp", "greedy"):
+        g = synth.WORKLOADS[name]
+        check(g.d, g.ffn, g.n_blocks, g.V, BF16, g.B, g.gamma, exact_split=True)
+        for exact in (False, True):
+            st, msg, _ = sv.access_check(g.d, g.ffn, g.n_blocks, g.V, BF16, g.B, g.gamma,
+                                         shrink_bytes=16, exact_split=exact)
+            assert st == sv.SPEC_EINVAL and "outside" in msg
 
 
 @pytest.mark.parametrize("wl", ["tiny", "mid", "topp", "greedy"])

@@ -77,7 +77,8 @@ def test_full_size_parity(name):
     torch.cuda.empty_cache()
     T, top_p = wl.temperature, wl.top_p
     # the tolerance of the pass as the library runs it (two activation
-    # terms from 113 rows on: the greedy workload's 224)
+    # terms in the wide passes: the top-p workload's 72 rows and the greedy
+    # workload's 224)
     M = wl.B * (wl.gamma + 1)
     tol, two = logit_tol_for(M, wl.wdtype), two_term_pass(M, wl.wdtype)
     d_dev = torch.from_numpy(draft).to(DEV)

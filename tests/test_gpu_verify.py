@@ -97,14 +97,22 @@ CASES = [
     # row groups of 5 and of 6 row tiles (129 and 161 rows)
     ("bf16-wide-129-rows", 1, 128, 192, 320, 650, 2, "bf16", 0.8, 0.9, True, {}),
     ("bf16-wide-161-rows", 1, 160, 128, 256, 700, 1, "bf16", 1.0, 1.0, False, {}),
-    # the exact three-term split kept from 113 rows on (SPEC_FLAG_EXACT_SPLIT;
-    # the two cases above take two terms): 224 rows greedy, 129 rows sampled
-    # with top-p, and 90 rows, where the flag changes nothing
+    # the exact three-term split kept in wide passes (SPEC_FLAG_EXACT_SPLIT;
+    # without it every wide pass takes two terms): two row groups at 224
+    # rows greedy, 129 rows sampled with top-p and 90 rows; one row group at
+    # 72 rows (the top-p workload's shape) and in the 1024-thread LM head;
+    # and 5 rows, a stacked pass, where the flag changes nothing
     ("bf16-wide-224-greedy-exact", 32, 6, 160, 288, 700, 1, "bf16", 0.0, 1.0, False,
      {"exact_split": True}),
     ("bf16-wide-129-rows-exact", 1, 128, 192, 320, 650, 2, "bf16", 0.8, 0.9, True,
      {"exact_split": True}),
-    ("bf16-wide-90-rows-exact-flag", 10, 8, 128, 256, 600, 1, "bf16", 1.0, 1.0, False,
+    ("bf16-wide-90-rows-exact", 10, 8, 128, 256, 600, 1, "bf16", 1.0, 1.0, False,
+     {"exact_split": True}),
+    ("bf16-wide-72-rows-exact", 8, 8, 256, 14336, 700, 1, "bf16", 0.7, 0.9, False,
+     {"exact_split": True}),
+    ("bf16-wide-lm-1024-exact", 3, 5, 128, 192, 70000, 1, "bf16", 0.9, 0.95, False,
+     {"exact_split": True}),
+    ("bf16-stacked-exact-flag", 1, 4, 128, 256, 600, 1, "bf16", 1.0, 1.0, False,
      {"exact_split": True}),
     # LM heads of more than 4096 tiles at up to 80 rows: the 1024-thread
     # one-row-group shape (18 rows, sampling with top-p; 16 rows, greedy)
