@@ -326,7 +326,10 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
   };
 
   // Visits every token once, with the loads of the next batch in flight
-  // while a batch is processed; only the last batch checks bounds.  Rows
+  // while a batch is processed; only the last batch checks bounds.  The
+  // loads are unconditional (a load past the row's end re-reads its last
+  // element, whose token is skipped), so no branch separates a load from
+  // its use and each wait covers only the batch being processed.  Rows
   // that allow it are read 16 bytes per lane (tokens 4 i .. 4 i + 3 of
   // float4 i), else 4 bytes per lane.
   const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (V & 3) == 0;
@@ -335,23 +338,15 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
       constexpr int B4 = kToppBatch4;
       constexpr int stride = B4 * kToppThreads;
       const float4* s4 = reinterpret_cast<const float4*>(src);
-      const int V4 = V >> 2;
+      const int V4 = V >> 2, last = V4 - 1;
       const int nbt = (V4 + stride - 1) / stride, nfull = V4 / stride;
       float4 cur[B4], nxt[B4];
 #pragma unroll
-      for (int u = 0; u < B4; ++u) {
-        const int i = tid + u * kToppThreads;
-        cur[u] = i < V4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int u = 0; u < B4; ++u) cur[u] = s4[min(tid + u * kToppThreads, last)];
       for (int bt = 0; bt < nbt; ++bt) {
         const int i0 = tid + bt * stride;
-        if (bt + 1 < nbt) {
 #pragma unroll
-          for (int u = 0; u < B4; ++u) {
-            const int i = i0 + stride + u * kToppThreads;
-            nxt[u] = i < V4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
+        for (int u = 0; u < B4; ++u) nxt[u] = s4[min(i0 + stride + u * kToppThreads, last)];
         const bool full = bt < nfull;
 #pragma unroll
         for (int u = 0; u < B4; ++u) {
@@ -366,22 +361,14 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
       return;
     }
     constexpr int stride = kToppBatch1 * kToppThreads;
-    const int nbt = (V + stride - 1) / stride, nfull = V / stride;
+    const int nbt = (V + stride - 1) / stride, nfull = V / stride, last = V - 1;
     float cur[kToppBatch1], nxt[kToppBatch1];
 #pragma unroll
-    for (int u = 0; u < kToppBatch1; ++u) {
-      const int v = tid + u * kToppThreads;
-      cur[u] = v < V ? src[v] : 0.f;
-    }
+    for (int u = 0; u < kToppBatch1; ++u) cur[u] = src[min(tid + u * kToppThreads, last)];
     for (int bt = 0; bt < nbt; ++bt) {
       const int v0 = tid + bt * stride;
-      if (bt + 1 < nbt) {
 #pragma unroll
-        for (int u = 0; u < kToppBatch1; ++u) {
-          const int v = v0 + stride + u * kToppThreads;
-          nxt[u] = v < V ? src[v] : 0.f;
-        }
-      }
+      for (int u = 0; u < kToppBatch1; ++u) nxt[u] = src[min(v0 + stride + u * kToppThreads, last)];
       if (bt < nfull) {
 #pragma unroll
         for (int u = 0; u < kToppBatch1; ++u) f(v0 + u * kToppThreads, cur[u]);
@@ -413,15 +400,16 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
     if (pass == 0) {
       for_each_token([&](int, float x) { atomicAdd(&myhist[key_of(x) >> 21], mass_of(x)); });
     } else if (pass == 1) {
-      // histogram of the second digit within the first digit's crossing
-      // bucket, whose tokens are appended to the wave's segment (a
-      // wave-uniform count, no atomics)
+      // The first digit's crossing bucket: its tokens are appended to the
+      // wave's segment (a wave-uniform count, no atomics) in one pass over
+      // the row that computes no mass, then the second digit's histogram
+      // is taken over the candidates, every lane busy.  If any wave's
+      // segment overflowed, the histogram takes a second pass over the row
+      // instead (the same masses, so the same integer sums).
       const uint32_t p0 = prefix >> 21;
       int wn = 0;
       for_each_token([&](int v, float x) {
-        const uint32_t k = key_of(x);
-        const bool hit = (k >> 21) == p0;
-        if (hit) atomicAdd(&myhist[(k >> 10) & 2047u], mass_of(x));
+        const bool hit = (key_of(x) >> 21) == p0;
         const u64 mask = __ballot(hit);
         const int slot = wn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -431,6 +419,19 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
       if (lane == 0) {
         sh.ncw[wave] = min(wn, kCandPerWave);
         if (wn > kCandPerWave) sh.overflow = 1;
+      }
+      __syncthreads();
+      if (sh.overflow == 0) {
+        const int n = min(wn, kCandPerWave);
+        for (int i = lane; i < n; i += kWave) {
+          const float x = __uint_as_float(wcand[i].x);
+          atomicAdd(&myhist[(key_of(x) >> 10) & 2047u], mass_of(x));
+        }
+      } else {
+        for_each_token([&](int, float x) {
+          const uint32_t k = key_of(x);
+          if ((k >> 21) == p0) atomicAdd(&myhist[(k >> 10) & 2047u], mass_of(x));
+        });
       }
     } else if (compact) {
       const int n = sh.ncw[wave];
