@@ -204,7 +204,7 @@ constexpr int kMaxBins = 2048;           // digits of 11, 11 and 10 bits
 // copies falls in four different LDS banks (a stride of nb alone is a
 // multiple of the bank count, and the copies' lanes would conflict).
 constexpr int kHistPad = 4;
-constexpr int kToppBatch4 = 4;           // 16-byte loads of one batch (the next batch is in flight meanwhile)
+constexpr int kToppBatch4 = 4;           // 16-byte loads of one batch (one or two batches in flight)
 constexpr int kToppBatch1 = 8;           // 4-byte loads of one batch, rows that are not 16-byte aligned
 constexpr int kTieCap = 64;              // tied keys ordered by one thread
 constexpr int kCandPerWave = 512;        // candidate slots of each wave
@@ -325,13 +325,15 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
     return fixed_mass(p);
   };
 
-  // Visits every token once, with the loads of the next batch in flight
-  // while a batch is processed; only the last batch checks bounds.  The
-  // loads are unconditional (a load past the row's end re-reads its last
-  // element, whose token is skipped), so no branch separates a load from
-  // its use and each wait covers only the batch being processed.  Rows
-  // that allow it are read 16 bytes per lane (tokens 4 i .. 4 i + 3 of
-  // float4 i), else 4 bytes per lane.
+  // Visits every token once.  Batches alternate between two register
+  // buffers: batch k + 1 is issued into one before batch k is processed
+  // from the other, and batch k + 2 before the wait for batch k + 1, so up
+  // to two batches are in flight and no register copy waits on a load.
+  // The loads are unconditional (a load past the row's end re-reads its
+  // last element, whose token is skipped), so no branch separates a load
+  // from its use; only the last batch checks bounds.  Rows that allow it
+  // are read 16 bytes per lane (tokens 4 i .. 4 i + 3 of float4 i), else
+  // 4 bytes per lane.
   const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (V & 3) == 0;
   auto for_each_token = [&](auto&& f) {
     if (vec) {
@@ -340,45 +342,64 @@ __device__ __forceinline__ void topp_row(const SampleArgs& a, int row, ToppShare
       const float4* s4 = reinterpret_cast<const float4*>(src);
       const int V4 = V >> 2, last = V4 - 1;
       const int nbt = (V4 + stride - 1) / stride, nfull = V4 / stride;
-      float4 cur[B4], nxt[B4];
-#pragma unroll
-      for (int u = 0; u < B4; ++u) cur[u] = s4[min(tid + u * kToppThreads, last)];
-      for (int bt = 0; bt < nbt; ++bt) {
+      float4 ba[B4], bb[B4];
+      auto issue = [&](float4 (&d)[B4], int bt) {
         const int i0 = tid + bt * stride;
 #pragma unroll
-        for (int u = 0; u < B4; ++u) nxt[u] = s4[min(i0 + stride + u * kToppThreads, last)];
+        for (int u = 0; u < B4; ++u) d[u] = s4[min(i0 + u * kToppThreads, last)];
+      };
+      auto run = [&](const float4 (&d)[B4], int bt) {
+        const int i0 = tid + bt * stride;
         const bool full = bt < nfull;
 #pragma unroll
         for (int u = 0; u < B4; ++u) {
           const int i = i0 + u * kToppThreads;
           if (full || i < V4) {
-            f(4 * i, cur[u].x); f(4 * i + 1, cur[u].y); f(4 * i + 2, cur[u].z); f(4 * i + 3, cur[u].w);
+            f(4 * i, d[u].x); f(4 * i + 1, d[u].y); f(4 * i + 2, d[u].z); f(4 * i + 3, d[u].w);
           }
         }
-#pragma unroll
-        for (int u = 0; u < B4; ++u) cur[u] = nxt[u];
+      };
+      issue(ba, 0);
+      for (int bt = 0; bt < nbt; bt += 2) {
+        issue(bb, bt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        run(ba, bt);
+        if (bt + 1 >= nbt) break;
+        issue(ba, bt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        run(bb, bt + 1);
       }
       return;
     }
-    constexpr int stride = kToppBatch1 * kToppThreads;
+    constexpr int B1 = kToppBatch1;
+    constexpr int stride = B1 * kToppThreads;
     const int nbt = (V + stride - 1) / stride, nfull = V / stride, last = V - 1;
-    float cur[kToppBatch1], nxt[kToppBatch1];
-#pragma unroll
-    for (int u = 0; u < kToppBatch1; ++u) cur[u] = src[min(tid + u * kToppThreads, last)];
-    for (int bt = 0; bt < nbt; ++bt) {
+    float ba[B1], bb[B1];
+    auto issue = [&](float (&d)[B1], int bt) {
       const int v0 = tid + bt * stride;
 #pragma unroll
-      for (int u = 0; u < kToppBatch1; ++u) nxt[u] = src[min(v0 + stride + u * kToppThreads, last)];
+      for (int u = 0; u < B1; ++u) d[u] = src[min(v0 + u * kToppThreads, last)];
+    };
+    auto run = [&](const float (&d)[B1], int bt) {
+      const int v0 = tid + bt * stride;
       if (bt < nfull) {
 #pragma unroll
-        for (int u = 0; u < kToppBatch1; ++u) f(v0 + u * kToppThreads, cur[u]);
+        for (int u = 0; u < B1; ++u) f(v0 + u * kToppThreads, d[u]);
       } else {
 #pragma unroll
-        for (int u = 0; u < kToppBatch1; ++u)
-          if (v0 + u * kToppThreads < V) f(v0 + u * kToppThreads, cur[u]);
+        for (int u = 0; u < B1; ++u)
+          if (v0 + u * kToppThreads < V) f(v0 + u * kToppThreads, d[u]);
       }
-#pragma unroll
-      for (int u = 0; u < kToppBatch1; ++u) cur[u] = nxt[u];
+    };
+    issue(ba, 0);
+    for (int bt = 0; bt < nbt; bt += 2) {
+      issue(bb, bt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      run(ba, bt);
+      if (bt + 1 >= nbt) break;
+      issue(ba, bt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      run(bb, bt + 1);
     }
   };
   // Candidates of this wave: segment cand[wave * kCandPerWave ...].
