@@ -1337,7 +1337,8 @@ static void launch_wide_terms(const WidePlan& p, const WideArgs& a, const EpiArg
       case 2: launch_wide_t<2, 2, 1, 16, 4, TERMS>(p, a, e, st, e0, e1); break;
       case 3: launch_wide_t<3, 2, 1, 16, 4, TERMS>(p, a, e, st, e0, e1); break;
       case 4: launch_wide_t<4, 2, 1, 16, 4, TERMS>(p, a, e, st, e0, e1); break;
-      default: launch_wide_t<5, 2, 1, 16, 2, TERMS>(p, a, e, st, e0, e1); break;
+      // four waves per SIMD: 128 VGPRs hold a 4-deep ring with two terms
+      default: launch_wide_t<5, 2, 1, 16, TERMS == 2 ? 4 : 2, TERMS>(p, a, e, st, e0, e1); break;
     }
   } else if (p.mg == 1) {
     switch (p.mtw) {
