@@ -15,6 +15,11 @@ GEMM kernels (algorithmic weight bytes / their event-timed duration vs
     python bench.py [--steps K] [--warmup W] [--workload mid]
     python bench.py --sweep-gamma      (verify cost per pass against gamma)
     python bench.py --attention        (decode attention over a KV-cached prefix)
+    python bench.py --tree             (greedy tree verification on the mid model)
+    python bench.py --repack           (ragged repacking and the host gamma controller)
+
+The last four print one JSON line per point or workload, each with the
+oracle timed beside it, and are not the headline line.
 """
 
 import argparse
@@ -62,6 +67,12 @@ def parse():
     ap.add_argument("--sweep-gamma", action="store_true",
                     help="only print the verify cost per pass for gamma = 0..8, 16 .. 160 at B = 1 "
                          "on the mid and large models (one JSON line per point)")
+    ap.add_argument("--tree", action="store_true",
+                    help="only time greedy tree verification on the mid model (the 14-node "
+                         "binary tree at B = 1 and 8, and a 14-node chain at B = 1)")
+    ap.add_argument("--repack", action="store_true",
+                    help="only time the ragged repacking after a step and the host gamma "
+                         "controller (one JSON line per batch size)")
     return ap.parse_args()
 
 
@@ -348,7 +359,7 @@ ATTN_WORKLOADS = [
 ]
 
 
-def bench_attention(progress, steps=200, warmup=20):
+def bench_attention(progress, steps=200, warmup=20, cpu_seconds=3.0):
     """Decode attention: per call, the keys and values of every visible
     position are read once (2 * Hkv * hd * 2 bytes per position) plus the
     queries and outputs; GB/s against 8 TB/s and the measured read ceiling."""
@@ -392,10 +403,242 @@ def bench_attention(progress, steps=200, warmup=20):
             "us_per_call": us, "bytes_per_call": kv_bytes + io_bytes, "hbm_gbs": gbs,
             "hbm_frac": gbs / HBM_PEAK_GBS, "read_ceiling_gbs": ceiling["gbs"],
             "frac_of_read_ceiling": gbs / ceiling["gbs"],
-            "note": "one call = the attention launch plus, when the keys are split, the split-combine launch"}), flush=True)
+            "note": "one call = the attention launch plus, when the keys are split, the split-combine launch",
+            "cpu_baseline": attention_oracle(name, q, kc, vc, cl, parent, cpu_seconds) if cpu_seconds > 0 else None}),
+            flush=True)
         progress(f"attention {name}: {us:.1f} us/call, {gbs:.0f} GB/s")
         del kc, vc
         torch.cuda.empty_cache()
+
+
+def oracle_cores():
+    """Threads the host BLAS uses (the oracle's matrix products)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def attention_oracle(name, q, kc, vc, cl, parent, seconds):
+    """The float64 oracle's decode attention timed on whole sequences of the
+    same inputs until `seconds` pass; calls/s scales by the batch."""
+    import numpy as np
+    import torch
+    import oracle
+    B = q.shape[0]
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    qh, kh = q.cpu().numpy(), bits(kc)
+    vh = np.ascontiguousarray(bits(vc).transpose(0, 1, 3, 2))   # the oracle's [B][Hkv][max_seq][hd]
+    clh = cl.cpu().numpy()
+    par = parent.cpu().numpy() if parent is not None else None
+    done, t0 = 0, time.perf_counter()
+    while True:
+        b = done % B
+        oracle.attention.decode_attention(qh[b:b + 1], kh[b:b + 1], vh[b:b + 1], clh[b:b + 1],
+                                None if par is None else par[b:b + 1])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / B / el, "unit": "attention calls/s", "cores": int(oracle_cores()),
+            "kind": "oracle", "sample": f"{done} sequences of {name} ({B} per call) in {el:.1f} s"}
+
+
+# ---------------------------------------------------------------- tree verification
+
+# (name, B, tree): the 14-node full binary tree of depth 3 (two children per
+# node, the aicomputerinstitute.com tree chapter's example shape) at B = 1 and
+# 8, and a 14-node chain at B = 1 (the same rows scored as a chain).
+TREE_WORKLOADS = [("tree-mid-b1", 1, "binary"), ("chain14-mid-b1", 1, "chain"),
+                  ("tree-mid-b8", 8, "binary")]
+
+
+def tree_parents(kind, n=14):
+    """Parent of each node (-1: the root), nodes in level order."""
+    if kind == "chain":
+        return [-1] + list(range(n - 1))
+    par = [-1, -1]                   # the root's two children
+    level = [0, 1]
+    while len(par) < n:
+        nxt = []
+        for node in level:
+            for _ in range(2):
+                if len(par) < n:
+                    nxt.append(len(par))
+                    par.append(node)
+        level = nxt
+    return par
+
+
+def bench_tree(progress, steps=200, warmup=20, cpu_seconds=10.0):
+    """Greedy tree verification on the mid model: the pass over the root and
+    node rows, then the walk, cycling through POOL input sets.  Node tokens
+    copy their parent row's argmax with probability 0.65, else a random id
+    (expected 3.4 tokens per binary-tree pass and 2.7 per chain pass).  Per pass the weights are read
+    once; GB/s of the GEMM launches against 8 TB/s and the read ceiling,
+    and the float64 oracle (forward plus walk) timed beside it."""
+    import numpy as np
+    import torch
+    import synth
+    import oracle
+    import speculative_decoding_verification_06_amd as sv
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS["mid"]
+    key = (300 + list(synth.WORKLOADS).index("mid"),)
+    model = synth.model_torch(key, wl.d, wl.ffn, wl.n_blocks, wl.V, wl.wdtype, "cuda")
+    w = sv.Weights(model["blocks"], model["lm_head"])
+    host = None
+    if cpu_seconds > 0:
+        f64 = lambda t: t.detach().to("cpu").to(torch.float64).numpy()
+        host = {"blocks": [{"w_up": f64(b["w_up"]), "w_down": f64(b["w_down"]), "gain": None}
+                           for b in model["blocks"]], "lm_head": f64(model["lm_head"])}
+    del model
+    torch.cuda.empty_cache()
+    for idx, (name, B, kind) in enumerate(TREE_WORKLOADS):
+        par = tree_parents(kind)
+        n = len(par)
+        parent = torch.tensor([par] * B, dtype=torch.int32, device="cuda")
+        hids, toks = [], []
+        for k in range(POOL):
+            hid = synth.normal_torch((*key, synth.T_HIDDEN, 500 + idx, k), (B, n + 1, wl.d), 1.0, "cuda")
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(synth.torch_seed(*key, synth.T_DRAFT, 500 + idx, k))
+            tok0 = torch.randint(0, wl.V, (B, n), generator=gen, device="cuda", dtype=torch.int32)
+            _, _, _, logits = sv.verify_tree_greedy(w, hid, parent, tok0, want_logits=True)
+            amax = logits.argmax(-1)
+            from_parent = torch.gather(amax, 1, (parent + 1).long()).to(torch.int32)
+            keep = torch.rand((B, n), generator=gen, device="cuda") < 0.65
+            hids.append(hid)
+            toks.append(torch.where(keep, from_parent, tok0).contiguous())
+            del logits
+        ws = w.workspace(B, n)
+        accepted = 0
+        for k in range(POOL):
+            n_acc, _, _, _ = sv.verify_tree_greedy(w, hids[k], parent, toks[k], workspace=ws)
+            accepted += int((n_acc.cpu() + 1).sum())
+        tokens_per_pass = accepted / (POOL * B)
+        for k in range(warmup):
+            sv.verify_tree_greedy(w, hids[k % POOL], parent, toks[k % POOL], workspace=ws)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for k in range(steps):
+            sv.verify_tree_greedy(w, hids[k % POOL], parent, toks[k % POOL], workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        w.profile(True)
+        kp = min(steps, 50)
+        for k in range(kp):
+            sv.verify_tree_greedy(w, hids[k % POOL], parent, toks[k % POOL], workspace=ws)
+        gemm_ms, launches, wbytes = w.profile_read()
+        w.profile(False)
+        per_launch_bytes, per_launch_us = wbytes / launches, gemm_ms * 1e3 / launches
+        gbs = per_launch_bytes / per_launch_us / 1e3
+        ceiling = read_ceiling(torch, sv, per_launch_bytes)
+        cpu = None
+        if host is not None:
+            h = hids[0].cpu().numpy()
+            parh, tokh = parent.cpu().numpy(), toks[0].cpu().numpy()
+            done, t0 = 0, time.perf_counter()
+            while True:
+                ell = oracle.forward(h, host["blocks"], host["lm_head"], 1e-6)
+                oracle.tree.spec_verify_tree_greedy(ell, parh, tokh)
+                done += 1
+                el = time.perf_counter() - t0
+                if el >= cpu_seconds:
+                    break
+            cpu = {"value": done / el, "unit": "tree verify passes/s", "cores": int(oracle_cores()),
+                   "kind": "oracle", "sample": f"{done} oracle passes (forward and walk) of {name}, "
+                                                f"one input set, in {el:.1f} s"}
+        M = B * (n + 1)
+        print(json.dumps({
+            "bench": "tree_verify_greedy", "workload": name, "B": B, "nodes": n, "rows": M,
+            "tree": kind, "model": f"mid: d={wl.d} ffn={wl.ffn} blocks={wl.n_blocks} V={wl.V} bf16",
+            "us_per_pass": us, "passes_per_s": 1e6 / us,
+            "mean_tokens_per_pass": tokens_per_pass, "accepted_tokens_per_s": tokens_per_pass * B * 1e6 / us,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "weight-streaming GEMMs of the pass",
+                         "bytes_per_launch": per_launch_bytes, "avg_launch_us": per_launch_us,
+                         "read_ceiling_gbs": ceiling["gbs"], "frac_of_read_ceiling": gbs / ceiling["gbs"],
+                         "method_flop_per_byte": float(M)},
+            "cpu_baseline": cpu}), flush=True)
+        progress(f"tree {name}: {us:.1f} us/pass, {tokens_per_pass:.2f} tokens per sequence and pass")
+    w.close()
+
+
+# ---------------------------------------------------------------- repacking and gamma control
+
+REPACK_BATCHES = [32, 1024, 16384]
+
+
+def bench_repack(progress, steps=200, warmup=20, cpu_seconds=3.0):
+    """spec_repack after a step of B sequences at gamma = 6 (accept counts
+    drawn uniformly, about 1% refused rows), and one host update of the gamma
+    controller for the whole batch; the oracle's repack timed beside."""
+    import numpy as np
+    import torch
+    import synth
+    import ctypes
+    import oracle
+    import speculative_decoding_verification_06_amd as sv
+    torch.cuda.set_device(0)
+    gamma = 6
+    G1 = gamma + 1
+    for B in REPACK_BATCHES:
+        rng = synth.generator(600, B)
+        n_acc = rng.integers(0, G1, size=B).astype(np.int32)
+        n_acc[rng.random(B) < 0.01] = -1
+        emitted = rng.integers(0, 128256, size=(B, G1)).astype(np.int32)
+        for b in range(B):
+            emitted[b, max(n_acc[b], -1) + 1:] = -1
+        committed = rng.integers(0, 8192, size=B).astype(np.int32)
+        nd, ed = torch.from_numpy(n_acc).cuda(), torch.from_numpy(emitted).cuda()
+        cd = torch.from_numpy(committed).cuda()
+        for _ in range(warmup):
+            sv.repack(nd, ed, cd)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            sv.repack(nd, ed, cd)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        nbytes = 4 * (B + B * G1 + B) + 4 * (B * G1 + (B + 1) + B + (G1 + 2) + 2 + B)
+        # host controller: one update of all B sequences per step (the C call
+        # on prebuilt host arrays, so no marshalling is timed)
+        ctl = sv.GammaController(B, 1, 8, gamma, 0.9, [1.0 + 0.05 * g for g in range(9)])
+        c_n = (ctypes.c_int32 * B)(*[int(x) for x in n_acc])
+        c_g = (ctypes.c_int32 * B)(*([gamma] * B))
+        c_out = (ctypes.c_int32 * B)()
+        lib = sv.load()
+        t0, reps = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 0.5:
+            if lib.spec_gamma_ctl_update(ctl.handle, c_n, c_g, c_out) != 0:
+                raise RuntimeError("spec_gamma_ctl_update failed")
+            reps += 1
+        ctl_us = (time.perf_counter() - t0) / reps * 1e6
+        ctl.close()
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.control.repack(n_acc, emitted, committed)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= cpu_seconds:
+                break
+        print(json.dumps({
+            "bench": "repack", "B": B, "gamma": gamma, "us_per_call": us,
+            "bytes_per_call": nbytes, "gbs": nbytes / us / 1e3,
+            "roofline": {"bound": "latency", "note": "one work group; a few KB to a few hundred KB "
+                         "per call, so the launch and its dependent steps bound it"},
+            "gamma_controller_us_per_step": ctl_us,
+            "cpu_baseline": {"value": done / el, "unit": "repack calls/s", "cores": 1, "kind": "oracle",
+                             "sample": f"{done} oracle repack calls of B={B} in {el:.1f} s"}}), flush=True)
+        progress(f"repack B={B}: {us:.1f} us/call, controller {ctl_us:.2f} us/step")
 
 
 # ---------------------------------------------------------------- main
@@ -418,7 +661,13 @@ def main():
         sweep_gamma(progress)
         return
     if args.attention:
-        bench_attention(progress)
+        bench_attention(progress, cpu_seconds=0.0 if args.no_cpu_baseline else 3.0)
+        return
+    if args.tree:
+        bench_tree(progress, cpu_seconds=0.0 if args.no_cpu_baseline else 10.0)
+        return
+    if args.repack:
+        bench_repack(progress)
         return
 
     progress("importing torch")
