@@ -598,13 +598,21 @@ def bench_repack(progress, steps=200, warmup=20, cpu_seconds=3.0):
         committed = rng.integers(0, 8192, size=B).astype(np.int32)
         nd, ed = torch.from_numpy(n_acc).cuda(), torch.from_numpy(emitted).cuda()
         cd = torch.from_numpy(committed).cuda()
+        sv.repack(nd, ed, cd)                     # checked call through the binding
+        # the C call on preallocated outputs, so the loop times the device
+        z = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")
+        outs = [z(B * G1), z(B + 1), z(B), z(G1 + 2), z(2)]
+        lib = sv.load()
+        args = [ctypes.c_void_p(t.data_ptr()) for t in [nd, ed, cd] + outs]
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         for _ in range(warmup):
-            sv.repack(nd, ed, cd)
+            lib.spec_repack(B, gamma, *args, st)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
-            sv.repack(nd, ed, cd)
+            if lib.spec_repack(B, gamma, *args, st) != 0:
+                raise RuntimeError("spec_repack failed")
         b.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b) / steps * 1e3
