@@ -1280,6 +1280,14 @@ WidePlan plan_wide(int M, const Mat& m, bool two_term) {
   if (p.MT <= 5 || (two_term && p.MT <= 10 && tiles / 16 <= SV_MIN_BLOCKS)) {
     p.mtw = p.MT; p.mg = 1; p.ntc = 2;
     p.cg = (p.MT <= 5 && tiles / 16 > SV_MIN_BLOCKS) ? 16 : 8;
+  } else if (two_term && p.MT >= 11) {
+    // 161 to 224 rows with two terms: two row groups of 16 waves, 8 column
+    // groups of 2 tiles (123 VGPRs, four waves per SIMD), so a SIMD holds
+    // four waves to alternate on the MFMA pipe; each k-step's activations
+    // are read from LDS twice as often as with 4 column groups of 4 tiles
+    // (measured: greedy pass 4032 -> 3940 and 4094 -> 4017 us in two
+    // calls, B = 1 passes of 176 to 224 rows 0.5-3% faster)
+    p.ntc = 2; p.cg = 8;
   }
   const int ntw = p.ntc * p.cg;
   p.colblocks = (tiles + ntw - 1) / ntw;
@@ -1364,6 +1372,11 @@ static void launch_wide_terms(const WidePlan& p, const WideArgs& a, const EpiArg
         if (p.colblocks * p.S > SV_MIN_BLOCKS) launch_wide_t<5, 2, 1, 8, 2, TERMS>(p, a, e, st, e0, e1);
         else launch_wide_t<5, 2, 1, 8, 4, TERMS>(p, a, e, st, e0, e1);
         break;
+    }
+  } else if (p.ntc == 2) {
+    if constexpr (TERMS == 2) {   // 11 to 14 row tiles in two row groups of 8 column groups
+      if (p.mtw == 6) launch_wide_t<6, 2, 2, 8, 2, TERMS>(p, a, e, st, e0, e1);
+      else launch_wide_t<7, 2, 2, 8, 2, TERMS>(p, a, e, st, e0, e1);
     }
   } else {
     switch (p.mtw) {   // 6 to 14 row tiles in two row groups: mtw = 3 .. 7
