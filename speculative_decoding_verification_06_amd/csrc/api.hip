@@ -82,15 +82,19 @@ int gemm_path(const spec_weights* w, int M) {
   return (M >= w->mfma_min_rows || !have_rm) ? PATH_MFMA : PATH_FMA_BF16;
 }
 
-// Whether a pass of M rows carries its activations as two bf16 terms: every
-// pass the wide GEMM serves, unless the weights were registered with
-// SPEC_FLAG_EXACT_SPLIT.  The wide k-loop's chain of activation loads, LDS
-// reads and matrix operations per k-step then shrinks by a third (measured
-// 10.6% of a 72-row top-p pass and 14-21% of B = 1 passes of 65 to 97 rows);
-// the stacked passes of up to 10 rows keep three exact terms, which cost no
-// extra matrix operation there.  Every producer of the pass splits alike.
+// Whether a pass of M rows carries its activations as two bf16 terms, unless
+// the weights were registered with SPEC_FLAG_EXACT_SPLIT: every pass the
+// wide GEMM serves, whose k-loop chain of activation loads, LDS reads and
+// matrix operations per k-step then shrinks by a third (measured 10.6% of a
+// 72-row top-p pass and 14-21% of B = 1 passes of 65 to 97 rows), and the
+// stacked passes of 6 to 8 rows, whose eight rows of two terms fit one
+// fragment where five rows of three do not.  Stacked passes of up to 5 rows
+// keep three exact terms, which cost no extra matrix operation there, and so
+// do those of 9 and 10 rows (two tiles either way).  Every producer of the
+// pass splits alike.
 bool two_term(const spec_weights* w, int M, int path) {
-  return !(w->flags & SPEC_FLAG_EXACT_SPLIT) && path == PATH_MFMA && wide_rows(M);
+  return !(w->flags & SPEC_FLAG_EXACT_SPLIT) && path == PATH_MFMA &&
+         (wide_rows(M) || (M >= 6 && M <= kStackRows2));
 }
 
 // Statistics units per logits row: one per LM-head work group (nt tiles of
@@ -273,7 +277,7 @@ hipError_t run_gemm(spec_weights* w, bool prof, int path, const Mat& W, const fl
       wa.P = part; wa.ldp = W.Np; wa.slice_stride = (size_t)a.M * W.Np;
       err = launch_wide(wp, wa, a.e, st, e0, e1);
     } else {
-      err = launch_gemm(plan_gemm(path, a.M, W, stack), a, st, e0, e1);
+      err = launch_gemm(plan_gemm(path, a.M, W, stack, two), a, st, e0, e1);
     }
     if (err != hipSuccess) return err;
     if (prof) {
@@ -449,20 +453,20 @@ PassBufs pass_bufs(const spec_weights* w, const Layout& L, int B, int gamma, int
 // rows, which for the plain packing (16-row tiles, chunks on tile bounds)
 // is xs_index of the pass row.
 void check_xs_store(AccessCheck& C, const char* what, const char* buf, int64_t cap, int row0,
-                    int rows, int cols, int ks, bool stacked) {
+                    int rows, int cols, int ks, bool stacked, bool two) {
   const int ncol = std::min(cols, kKStep * ks);
   if (rows <= 0 || ncol <= 0) return;
   int64_t lo = INT64_MAX, hi = -1;
-  const int st = xs_term_step(stacked);
+  const int st = xs_term_step(stacked, two), last_term = two ? 1 : 2;
   const int last = (ncol - 1) / kKStep;   // columns of the first and last k-step
   for (int r = row0; r < row0 + rows; ++r)
     for (int s = 0; s <= last; s += std::max(1, last))
       for (int j = 0; j < kKStep; ++j) {
         const int col = s * kKStep + j;
         if (col >= ncol) break;
-        const int64_t i = (int64_t)xs_index(r, col, ks, stacked);
+        const int64_t i = (int64_t)xs_index(r, col, ks, stacked, two);
         lo = std::min(lo, i);
-        hi = std::max(hi, i + 2 * st);
+        hi = std::max(hi, i + last_term * st);
       }
   C.range(what, buf, lo, hi, cap);
 }
@@ -471,7 +475,7 @@ void check_xs_store(AccessCheck& C, const char* what, const char* buf, int64_t c
 // tiles [t0, t1) of the GEMM's output.
 struct EpiCheck {
   int kind, N, Np, ldo, nt;                // nt: tiles of one statistics unit
-  bool to_xs, stacked;
+  bool to_xs, stacked, two;
   int xs_ks;
   const char* xs_name;
   int64_t xs_cap;                          // next GEMM's split buffer (bf16 elements)
@@ -507,14 +511,15 @@ void check_epilogue(AccessCheck& C, const char* what, const EpiCheck& e, const P
     }
     if (q_hi >= 0) C.range(what, "qst", 2 * (q_lo * e.G + u0), 2 * (q_hi * e.G + u1) + 1, c.qst);
   }
-  if (e.to_xs) check_xs_store(C, what, e.xs_name, e.xs_cap, row0, rows, t1 * kSub, e.xs_ks, e.stacked);
+  if (e.to_xs) check_xs_store(C, what, e.xs_name, e.xs_cap, row0, rows, t1 * kSub, e.xs_ks, e.stacked, e.two);
 }
 
 void check_mfma(AccessCheck& C, const char* what, const GemmPlan& p, const Mat& W, int M,
                 const char* xs_name, int64_t xs_cap, int64_t xs_off_units, const EpiCheck& e,
                 const PassBufs& c, const Layout& L, int row0) {
   const int KS = W.Kp / kKStep, NT = p.nt;
-  const int FPT = p.stack ? 1 : 3, RPT = p.stack ? kStackRows : 16, TERMS = p.stack ? 3 : 1;
+  const int FPT = p.stack ? 1 : 3, RPT = p.stack ? xs_stack_rows(p.two) : 16;
+  const int TERMS = p.stack ? (p.two ? 2 : 3) : 1;
   const int MT = (M + RPT - 1) / RPT, MG = p.mg, KG = p.kg, nwaves = MG * KG;
   const int64_t wcap = (int64_t)W.Kp * W.Np / 8;     // bf16x8 fragments
   if ((int64_t)p.blocks * NT * kSub != W.Np) { C.range(what, "column blocks", 0, p.blocks * NT * kSub, W.Np + 1); }
@@ -532,8 +537,8 @@ void check_mfma(AccessCheck& C, const char* what, const GemmPlan& p, const Mat& 
           const int ar = lane & 15;
           int al;
           if (p.stack) {
-            const int pp = std::min(ar / kStackRows, 2);
-            al = (lane & 48) + pp * kStackRows + std::min(ar - pp * kStackRows, rows - 1);
+            const int pp = std::min(ar / RPT, TERMS - 1);
+            al = (lane & 48) + pp * RPT + std::min(ar - pp * RPT, rows - 1);
           } else {
             al = (lane & 48) + std::min(ar, rows - 1);
           }
@@ -624,13 +629,16 @@ spec_status access_check_pass(const spec_weights* w, int B, int gamma, int shrin
   const int M = L.M, path = gemm_path(w, M);
   const bool stack = path == PATH_MFMA && xs_stacked(M);
   const bool wide = path == PATH_MFMA && wide_rows(M);
+  const bool two = two_term(w, M, path);
   // k_prep
   {
     const char* what = "k_prep";
     C.range(what, "h", 0, (int64_t)(M - 1) * L.ldd + L.ldd - 1, c.h);
     C.range(what, "ss (sums of squares)", 0, (int64_t)(M - 1) * (L.ldd / kSub) + L.ldd / kSub - 1, c.ss);
     if (path == PATH_MFMA) {
-      check_xs_store(C, what, "xs (d-wide)", c.xsd, 0, M, L.ldd, L.ksd, stack);
+      check_xs_store(C, what, "xs (d-wide)", c.xsd, 0, M, L.ldd, L.ksd, stack, two);
+      // the zero steps of five-row stacked tiles, as k_prep clears them (the
+      // eight-row tiles of the two-term packing are a subset)
       const int rpt = stack ? kStackRows : 16, fpt = stack ? 1 : 3;
       const int mtn = (M + rpt - 1) / rpt;
       for (int pass = 0; pass < 2; ++pass) {
@@ -650,6 +658,7 @@ spec_status access_check_pass(const spec_weights* w, int B, int gamma, int shrin
     e.N = W.N; e.Np = W.Np;
     e.ldo = kind == EPI_UP ? L.ldf : (kind == EPI_DOWN ? L.ldd : L.Vs);
     e.stacked = stack;
+    e.two = two;
     e.to_xs = path == PATH_MFMA && kind != EPI_LM;
     e.xs_ks = kind == EPI_UP ? L.ksf : L.ksd;
     e.xs_name = kind == EPI_UP ? "xs (ffn-wide, next input)" : "xs (d-wide, next input)";
@@ -665,14 +674,13 @@ spec_status access_check_pass(const spec_weights* w, int B, int gamma, int shrin
         const int ldx = in_ffn ? L.ldf : L.ldd;
         const int64_t x_cap = in_ffn ? c.act : (kind == EPI_LM ? c.h : c.xg);
         e.nt = 4;
-        check_fma(C, what, plan_gemm(path, Mc, W, false), W, Mc, ldx, x_cap,
+        check_fma(C, what, plan_gemm(path, Mc, W, false, false), W, Mc, ldx, x_cap,
                   in_ffn ? "act" : (kind == EPI_LM ? "h" : "xg"), (int64_t)m0 * ldx, e, c, L, m0);
       } else if (wide) {
         e.nt = kGroupCols / kSub;
-        check_wide(C, what, plan_wide(Mc, W, two_term(w, M, path)), W, Mc, xs_name, xs_cap / 8, e, c,
-                   L);
+        check_wide(C, what, plan_wide(Mc, W, two), W, Mc, xs_name, xs_cap / 8, e, c, L);
       } else {
-        const GemmPlan p = plan_gemm(path, Mc, W, stack);
+        const GemmPlan p = plan_gemm(path, Mc, W, stack, two);
         e.nt = p.nt;
         check_mfma(C, what, p, W, Mc, xs_name, xs_cap / 8, xs_off, e, c, L, m0);
       }

@@ -59,26 +59,32 @@ __device__ __forceinline__ void split2_bf16(float x, uint32_t& hi, uint32_t& lo)
 // Split activations in MFMA A-operand order.  For a GEMM input X[M][K]
 // with KS k-steps of 32 (step KS is all zero), one 1 KiB fragment holds 64
 // lanes x 8 bf16, lane L holding A-rows L % 16 at columns
-// 32 s + 8 (L / 16) + j of k-step s.  Two packings of the three terms:
+// 32 s + 8 (L / 16) + j of k-step s.  Packings:
 //   plain   : row tile mt = 16 rows; k-step s of the tile is three
-//             fragments (hi, mid, lo), all multiplied into one accumulator
-//   stacked : row tile mt = kStackRows rows; one fragment per k-step whose
-//             A-row 5 p + r holds term p of row 5 mt + r (A-row 15 unused),
-//             so a single MFMA covers every term of five rows and the
-//             terms are summed after the k-loop
-// With the two-term split (plain packing only) the third fragment is not
-// written: every GEMM of such a pass reads two fragments per row tile (the
-// all-zero k-step past the end holds zeros in all three).
+//             fragments (hi, mid, lo), all multiplied into one accumulator;
+//             with the two-term split the third fragment is not written, and
+//             every GEMM of such a pass reads two fragments per row tile (the
+//             all-zero k-step past the end holds zeros in all three)
+//   stacked : one fragment per k-step whose A-row R p + r holds term p of
+//             row R mt + r, so a single MFMA covers every term of R rows and
+//             the terms are summed after the k-loop: R = kStackRows = 5 rows
+//             of three terms (A-row 15 unused), or, with the two-term split,
+//             R = kStackRows2 = 8 rows of two terms
 // xs_index returns the bf16 index of term 0 of (row, col); term p sits at
-// +p * xs_term_step(stacked).  Both are host functions too, so the host-side
-// access check evaluates the very formulas the kernels use.
+// +p * xs_term_step(stacked, two).  Both are host functions too, so the
+// host-side access check evaluates the very formulas the kernels use.
 constexpr int kStackRows = 5;
-__host__ __device__ __forceinline__ int xs_term_step(bool stacked) { return stacked ? 8 * kStackRows : 512; }
-__host__ __device__ __forceinline__ size_t xs_index(int row, int col, int ks, bool stacked) {
+constexpr int kStackRows2 = 8;
+__host__ __device__ __forceinline__ int xs_stack_rows(bool two) { return two ? kStackRows2 : kStackRows; }
+__host__ __device__ __forceinline__ int xs_term_step(bool stacked, bool two) {
+  return stacked ? 8 * xs_stack_rows(two) : 512;
+}
+__host__ __device__ __forceinline__ size_t xs_index(int row, int col, int ks, bool stacked, bool two) {
   const int lane_hi = 16 * ((col & 31) >> 3), s = col >> 5, j = col & 7;
   if (stacked) {
-    const size_t frag = (size_t)(row / kStackRows) * (ks + 1) + s;
-    return (frag * 64 + lane_hi + row % kStackRows) * 8 + j;
+    const int R = xs_stack_rows(two);
+    const size_t frag = (size_t)(row / R) * (ks + 1) + s;
+    return (frag * 64 + lane_hi + row % R) * 8 + j;
   }
   const size_t frag = ((size_t)(row >> 4) * (ks + 1) + s) * 3;
   return (frag * 64 + lane_hi + (row & 15)) * 8 + j;
@@ -88,8 +94,8 @@ __device__ __forceinline__ void xs_store(uint16_t* xs, int row, int col, int ks,
   uint32_t a, b, c = 0;
   if (two) split2_bf16(x, a, b);
   else split3_bf16(x, a, b, c);
-  const size_t i = xs_index(row, col, ks, stacked);
-  const int st = xs_term_step(stacked);
+  const size_t i = xs_index(row, col, ks, stacked, two);
+  const int st = xs_term_step(stacked, two);
   xs[i] = (uint16_t)a;
   xs[i + st] = (uint16_t)b;
   if (!two) xs[i + 2 * st] = (uint16_t)c;

@@ -278,12 +278,13 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
 
 // ---------------------------------------------------------------- MFMA GEMM
 // bf16 weights in MFMA tiles (layout in internal.h); the activations come
-// already split into three bf16 terms in A-fragment order (xs_index), so a
-// k-step is NT weight fragments + FPT activation fragments per row tile and
-// FPT * NT MFMAs, with no vector ALU work.  STACK selects the stacked
-// packing (five rows, all three terms in one fragment), which cuts the
-// activation loads and MFMAs of a B = 1 pass by three; the plain packing
-// (16 rows, three fragments) serves many rows.  MTW = row tiles per wave,
+// already split into bf16 terms in A-fragment order (xs_index), so a k-step
+// is NT weight fragments + FPT activation fragments per row tile and
+// FPT * NT MFMAs, with no vector ALU work.  The stacked packings (SK 3: five
+// rows, all three terms in one fragment; SK 2: eight rows, both terms of the
+// two-term split in one fragment) cut the activation loads and MFMAs of a
+// B = 1 pass by three; the plain packing (16 rows, three fragments) serves
+// many rows.  MTW = row tiles per wave,
 // MG row groups, NT column tiles per work group; the number of k-groups
 // KG = waves / MG is a launch parameter.
 // The weight stream is latency bound unless each CU keeps well over 100 KiB
@@ -296,12 +297,15 @@ struct MfmaPipe {
   static constexpr int value = (!STACK && MTW >= 3) ? 2 : (SV_PIPE_VGPRS / stage < 2 ? 2 : SV_PIPE_VGPRS / stage);
 };
 
-template <int MTW, int MG, int NT, bool STACK>
+// SK: the activation packing, 0 plain, 3 stacked with three terms of five
+// rows, 2 stacked with two terms of eight rows.
+template <int MTW, int MG, int NT, int SK>
 __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
+  constexpr bool STACK = SK != 0;
   constexpr int PIPE = MfmaPipe<MTW, NT, STACK>::value;
   constexpr int FPT = STACK ? 1 : 3;            // A fragments per row tile and k-step
-  constexpr int RPT = STACK ? kStackRows : 16;  // rows per row tile
-  constexpr int TERMS = STACK ? 3 : 1;          // LDS planes per row before the term sum
+  constexpr int RPT = SK == 2 ? kStackRows2 : (STACK ? kStackRows : 16);   // rows per row tile
+  constexpr int TERMS = STACK ? SK : 1;         // LDS planes per row before the term sum
   extern __shared__ float smem[];
   __shared__ float sh_inv[256];
   const int lane = threadIdx.x & 63;
@@ -335,8 +339,8 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
     const int ar = lane & 15;
     int al;
     if (STACK) {
-      const int p = min(ar / kStackRows, 2);
-      al = (lane & 48) + p * kStackRows + min(ar - p * kStackRows, rows - 1);
+      const int p = min(ar / RPT, TERMS - 1);
+      al = (lane & 48) + p * RPT + min(ar - p * RPT, rows - 1);
     } else {
       al = (lane & 48) + min(ar, rows - 1);
     }
@@ -415,8 +419,8 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 #undef SV_COMPUTE
 
   // Partial tiles into LDS red[KG][M][TERMS][ldr] (k-group, row, term),
-  // then summed in a fixed order (terms lo + mid + hi, then k-groups in
-  // order) into res[M][ldr].  C layout of 16x16 MFMA: lane holds A-rows
+  // then summed in a fixed order (terms from the last to the first, lo +
+  // mid + hi or lo + hi, then k-groups in order) into res[M][ldr].  C layout of 16x16 MFMA: lane holds A-rows
   // 4*(lane/16)+j of column lane%16.
   constexpr int NCOL = NT * kSub;
   constexpr int ldr = NCOL + 1;
@@ -431,9 +435,9 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
         const int ar = crow + j;
         int row, p = 0;
         if (STACK) {
-          p = ar / kStackRows;
-          row = (mt0 + i) * kStackRows + (ar - p * kStackRows);
-          if (p > 2) row = M;                     // A-row 15: no row
+          p = ar / RPT;
+          row = (mt0 + i) * RPT + (ar - p * RPT);
+          if (p >= TERMS) row = M;                // A-row 15 of five-row tiles: no row
         } else {
           row = (mt0 + i) * 16 + ar;
         }
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
       float v = 0.f;
       for (int q = 0; q < KG; ++q) {
         const float* pr = red + (((size_t)q * M + r) * TERMS) * ldr + col;
-        v += (pr[2 * ldr] + pr[ldr]) + pr[0];
+        v += SK == 2 ? pr[ldr] + pr[0] : (pr[2 * ldr] + pr[ldr]) + pr[0];
       }
       res[r * ldr + col] = v;
     }
@@ -1097,8 +1101,8 @@ __global__ __launch_bounds__(kEpiThreads) void k_epi_wide8(WideArgs a, EpiArgs e
       t[1][j] = b0 | (b1 << 16);
       t[2][j] = c0 | (c1 << 16);
     }
-    uint16_t* base = e.xs + xs_index(r, n0, e.xs_ks, false);
-    const int st = xs_term_step(false);
+    uint16_t* base = e.xs + xs_index(r, n0, e.xs_ks, false, e.xs_two);
+    const int st = xs_term_step(false, e.xs_two);
 #pragma unroll
     for (int q = 0; q < 3; ++q)
       if (q < 2 || !e.xs_two) *reinterpret_cast<uint4*>(base + q * st) = make_uint4(t[q][0], t[q][1], t[q][2], t[q][3]);
@@ -1215,7 +1219,7 @@ int mfma_block_tiles(int Np) {
   return nt;
 }
 
-GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack) {
+GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack, bool two) {
   GemmPlan p;
   p.path = path;
   const int tiles = m.Np / kSub;
@@ -1227,8 +1231,10 @@ GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack) {
     return p;
   }
   p.stack = stack;
+  p.two = stack && two;
   if (p.stack) {
-    p.mtw = (M + kStackRows - 1) / kStackRows;
+    const int R = xs_stack_rows(p.two);
+    p.mtw = (M + R - 1) / R;
     p.mg = 1;
   } else {
     const int MT = (M + 15) / 16;
@@ -1408,14 +1414,14 @@ hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e
 // Launches go through hipExtLaunchKernelGGL so that, when timing is on, the
 // two events take the kernel's own start and end timestamps (no extra
 // packets between kernels).
-template <int MTW, int MG, bool STACK>
+template <int MTW, int MG, int SK>
 static hipError_t launch_mfma_mg(const GemmPlan& p, const GemmArgs& a, hipStream_t st,
                                  hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(p.blocks), block(64 * p.mg * p.kg);
   switch (p.nt) {
-    case 1: hipExtLaunchKernelGGL((k_gemm_mfma<MTW, MG, 1, STACK>), grid, block, p.lds, st, e0, e1, 0, a); break;
-    case 2: hipExtLaunchKernelGGL((k_gemm_mfma<MTW, MG, 2, STACK>), grid, block, p.lds, st, e0, e1, 0, a); break;
-    default: hipExtLaunchKernelGGL((k_gemm_mfma<MTW, MG, 4, STACK>), grid, block, p.lds, st, e0, e1, 0, a); break;
+    case 1: hipExtLaunchKernelGGL((k_gemm_mfma<MTW, MG, 1, SK>), grid, block, p.lds, st, e0, e1, 0, a); break;
+    case 2: hipExtLaunchKernelGGL((k_gemm_mfma<MTW, MG, 2, SK>), grid, block, p.lds, st, e0, e1, 0, a); break;
+    default: hipExtLaunchKernelGGL((k_gemm_mfma<MTW, MG, 4, SK>), grid, block, p.lds, st, e0, e1, 0, a); break;
   }
   return hipGetLastError();
 }
@@ -1430,19 +1436,20 @@ hipError_t launch_gemm(const GemmPlan& p, const GemmArgs& a, hipStream_t st, hip
       hipExtLaunchKernelGGL((k_gemm_fma<uint16_t>), grid, block, p.lds, st, e0, e1, 0, a);
     return hipGetLastError();
   }
+  if (p.stack && p.two) return launch_mfma_mg<1, 1, 2>(p, a, st, e0, e1);   // 6 to 8 rows
   if (p.stack)
-    return p.mtw == 1 ? launch_mfma_mg<1, 1, true>(p, a, st, e0, e1)
-                      : launch_mfma_mg<2, 1, true>(p, a, st, e0, e1);
+    return p.mtw == 1 ? launch_mfma_mg<1, 1, 3>(p, a, st, e0, e1)
+                      : launch_mfma_mg<2, 1, 3>(p, a, st, e0, e1);
   if (p.mg == 1)
-    return p.mtw == 1 ? launch_mfma_mg<1, 1, false>(p, a, st, e0, e1)
-                      : launch_mfma_mg<2, 1, false>(p, a, st, e0, e1);
+    return p.mtw == 1 ? launch_mfma_mg<1, 1, 0>(p, a, st, e0, e1)
+                      : launch_mfma_mg<2, 1, 0>(p, a, st, e0, e1);
   if (p.mg == 2) {
-    if (p.mtw == 2) return launch_mfma_mg<2, 2, false>(p, a, st, e0, e1);
-    if (p.mtw == 3) return launch_mfma_mg<3, 2, false>(p, a, st, e0, e1);
-    return launch_mfma_mg<4, 2, false>(p, a, st, e0, e1);
+    if (p.mtw == 2) return launch_mfma_mg<2, 2, 0>(p, a, st, e0, e1);
+    if (p.mtw == 3) return launch_mfma_mg<3, 2, 0>(p, a, st, e0, e1);
+    return launch_mfma_mg<4, 2, 0>(p, a, st, e0, e1);
   }
-  return p.mtw == 3 ? launch_mfma_mg<3, 4, false>(p, a, st, e0, e1)
-                    : launch_mfma_mg<4, 4, false>(p, a, st, e0, e1);
+  return p.mtw == 3 ? launch_mfma_mg<3, 4, 0>(p, a, st, e0, e1)
+                    : launch_mfma_mg<4, 4, 0>(p, a, st, e0, e1);
 }
 
 }  // namespace sv

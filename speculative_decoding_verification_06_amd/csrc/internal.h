@@ -69,7 +69,7 @@ struct EpiArgs {
   uint16_t* xs = nullptr;
   int xs_ks = 0;
   bool xs_stack = false;      // stacked packing (xs_index)
-  bool xs_two = false;        // two-term split (split2_bf16), plain packing
+  bool xs_two = false;        // two-term split (split2_bf16)
 };
 
 struct GemmArgs {
@@ -92,24 +92,26 @@ struct GemmPlan {
   int mtw = 1, mg = 1, kg = 1;   // M tiles per wave, row groups, k-groups
   int nt = 4;                    // 16-column tiles per work group
   bool stack = false;            // stacked activation packing (MFMA)
+  bool two = false;              // stacked: two terms of eight rows per tile
   int blocks = 0;                // work groups
   size_t lds = 0;                // dynamic LDS bytes
 };
 
-// The MFMA path packs the split activations of up to 10 rows stacked (two
-// five-row tiles, one fragment per k-step each); more rows use the plain
+// The MFMA path packs the split activations of up to 10 rows stacked (up to
+// two five-row tiles of three terms, or one eight-row tile of two terms for
+// 6 to 8 rows, one fragment per k-step each); more rows use the plain
 // packing, which needs no more fragments from 11 rows on.
 inline bool xs_stacked(int M) { return M <= 10; }
 
 // Bytes of one split-activation buffer of M rows and ks k-steps (plus the
-// all-zero step): one 1 KiB fragment per row tile and k-step stacked, three
-// plain.
+// all-zero step): one 1 KiB fragment per row tile and k-step stacked (sized
+// for five-row tiles, which the eight-row tiles never exceed), three plain.
 inline size_t xs_bytes(int M, int ks) {
   return xs_stacked(M) ? (size_t)((M + kStackRows - 1) / kStackRows) * (ks + 1) * 1024
                        : (size_t)((M + 15) / 16) * (ks + 1) * 3 * 1024;
 }
 
-GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack);
+GemmPlan plan_gemm(int path, int M, const Mat& m, bool stack, bool two);
 
 // Wide MFMA GEMM (plain packing): work groups of 8 column tiles with the
 // activations staged in LDS, K split over S slices when the column blocks

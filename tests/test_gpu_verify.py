@@ -114,6 +114,14 @@ CASES = [
      {"exact_split": True}),
     ("bf16-stacked-exact-flag", 1, 4, 128, 256, 600, 1, "bf16", 1.0, 1.0, False,
      {"exact_split": True}),
+    # stacked passes of 6 to 8 rows: one eight-row tile of two terms (the
+    # large workload's B = 1, gamma = 5 shape), sampled, with top-p and
+    # greedy; and 6 rows with the exact split, two five-row tiles of three
+    ("bf16-stacked-two-6", 1, 5, 128, 256, 600, 2, "bf16", 1.0, 1.0, True, {}),
+    ("bf16-stacked-two-8-topp", 2, 3, 192, 320, 700, 1, "bf16", 0.8, 0.9, False, {}),
+    ("bf16-stacked-two-7-greedy", 1, 6, 160, 288, 650, 1, "bf16", 0.0, 1.0, False, {}),
+    ("bf16-stacked-6-exact", 1, 5, 128, 256, 600, 1, "bf16", 1.0, 1.0, False,
+     {"exact_split": True}),
     # LM heads of more than 4096 tiles at up to 80 rows: the 1024-thread
     # one-row-group shape (18 rows, sampling with top-p; 16 rows, greedy)
     ("bf16-wide-lm-1024", 3, 5, 128, 192, 70000, 1, "bf16", 0.9, 0.95, False, {}),
