@@ -183,9 +183,15 @@ __device__ __forceinline__ void early_inv_rms(const EpiArgs& e, int M, float* sh
 
 // rms_early: the UP rows below nwaves already hold 1 / rms in sh_inv
 // (early_inv_rms), behind a barrier the caller has passed since.
+// XSK: the packing of the split output when the caller knows it at compile
+// time (0 plain, 3 stacked three-term, 2 stacked two-term), else -1 and the
+// packing comes from e.xs_stack / e.xs_two.
+template <int XSK = -1>
 __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const float* res, int ldr,
                              float* sh_inv, int nwaves, const float (&pv)[8],
                              bool rms_early = false) {
+  const bool xs_stack = XSK < 0 ? e.xs_stack : XSK != 0;
+  const bool xs_two = XSK < 0 ? e.xs_two : XSK == 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15;
   if (e.kind == EPI_UP && e.rms) {
@@ -253,7 +259,7 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
     if (e.kind == EPI_UP) {
       const float y = x.valid ? silu(v * sh_inv[x.r]) : 0.f;
       if (x.live && !e.xs) e.out[x.o] = y;   // the MFMA path reads only the split copy
-      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, e.xs_stack, e.xs_two, y);
+      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, xs_stack, xs_two, y);
     } else if (e.kind == EPI_DOWN) {
       float hn = 0.f;
       if (x.valid) hn = (pre ? p0 : e.out[x.o]) + v;
@@ -265,7 +271,7 @@ __device__ void run_epilogue(const EpiArgs& e, int M, int c0, int nt, const floa
         const float sq = sum16(hn * hn);
         if (x.live && c == 0) e.ss_out[(size_t)x.r * e.ss_ld + x.tile] = sq;
       }
-      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, e.xs_stack, e.xs_two, y);
+      if (to_xs) xs_store(e.xs, x.r, x.n, e.xs_ks, xs_stack, xs_two, y);
     } else {
       if (x.valid && e.out) e.out[x.o] = v;   // no logits buffer: greedy, no debug copy
       const float qv = pre ? p0 : lm_item_q(e, x);
@@ -467,7 +473,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
     }
     __syncthreads();
   }
-  run_epilogue(a.e, M, c0, NT, res, ldr, sh_inv, nwaves, pv, rms_early);
+  run_epilogue<SK>(a.e, M, c0, NT, res, ldr, sh_inv, nwaves, pv, rms_early);
 }
 
 // ---------------------------------------------------------------- LM epilogue from registers
