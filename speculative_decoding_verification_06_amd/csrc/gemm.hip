@@ -8,9 +8,10 @@
 // aicomputerinstitute.com, Why Generation Is Slow: A Roofline View).  Each
 // weight byte is read from HBM once; activations are split once, by the
 // kernel that produces them, into bf16 terms for the MFMA path: three exact
-// terms in the stacked passes of up to 10 rows, two rounded ones (2^-16
-// relative) in the wide passes unless the exact split is asked for, so the
-// logits track a float64 reference.
+// terms in the stacked passes of up to 5 and of 9 or 10 rows, two rounded
+// ones (2^-16 relative) in the stacked passes of 6 to 8 rows and the wide
+// passes unless the exact split is asked for, so the logits track a float64
+// reference.
 //
 // Work decomposition: a work group owns NT MFMA column tiles (16 columns
 // each) over the whole K range.  Its waves are MG row groups x KG k-groups;
