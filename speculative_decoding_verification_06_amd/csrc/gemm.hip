@@ -1406,6 +1406,9 @@ hipError_t launch_wide(const WidePlan& p, const WideArgs& a_in, const EpiArgs& e
                        hipEvent_t e0, hipEvent_t e1) {
   WideArgs a = a_in;
   a.fuse_lm = p.S == 1 && e.kind == EPI_LM;
+  // plan_wide gives two row groups of 2-tile column groups only with two
+  // terms; no other plan reaches that shape's launch
+  if (p.mg == 2 && p.ntc == 2 && p.terms != 2) return hipErrorInvalidValue;
   if (p.terms == 2) launch_wide_terms<2>(p, a, e, st, e0, e1);
   else launch_wide_terms<3>(p, a, e, st, e0, e1);
   hipError_t err = hipGetLastError();
