@@ -54,8 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--exact-split", action="store_true",
                     help="register the weights with SPEC_FLAG_EXACT_SPLIT (three exact bf16 terms "
-                         "per activation in every pass; by default passes of 6 to 8 and of 11 "
-                         "to 224 rows carry two)")
+                         "per activation in every pass; by default passes of 6 to 224 rows "
+                         "carry two)")
     ap.add_argument("--gemm", choices=("auto", "fma"), default="auto",
                     help="fma: bf16 weights kept row-major and every GEMM on the vector-FMA "
                          "kernel (a comparison of the two GEMM paths at the same shape)")
@@ -753,14 +753,14 @@ def main():
     # activation terms; another configuration has no stored reading
     traffic = stored_traffic(wl.name) if args.gemm == "auto" and not args.exact_split else None
 
-    # bf16 terms per fp32 activation on the MFMA path: two for the wide passes
-    # of 11 to 224 rows and the stacked ones of 6 to 8 rows unless the exact
-    # split is asked for, else three; the vector-FMA path and fp32 weights
-    # take the activations as they are.
+    # bf16 terms per fp32 activation on the MFMA path: two for the stacked
+    # passes of 6 to 8 rows and the wide ones of 9 to 224 rows unless the
+    # exact split is asked for, else three; the vector-FMA path and fp32
+    # weights take the activations as they are.
     if args.gemm == "fma" or wl.wdtype != "bf16":
         terms = 0
     else:
-        terms = 2 if (not args.exact_split and (6 <= M <= 8 or 11 <= M <= 224)) else 3
+        terms = 2 if (not args.exact_split and 6 <= M <= 224) else 3
     out = {
         "metric": METRIC, "value": passes_s, "unit": "verify passes/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": ms / K, "higher_is_better": True,

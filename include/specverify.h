@@ -76,7 +76,7 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
                                        vector-FMA GEMM can serve any row count */
 #define SPEC_FLAG_EXACT_SPLIT 2u    /* bf16: keep the exact three-term split
                                        of each fp32 activation in every pass.
-                                       Without it, passes of 11 to 224 rows
+                                       Without it, passes of 9 to 224 rows
                                        (the wide GEMM's) and of 6 to 8 rows
                                        carry each activation as two bf16
                                        terms rounded to nearest (|x - hi -
@@ -87,8 +87,7 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
                                        of five, at a logit error about 1.5 to
                                        10 times the exact split's (measured
                                        under 1e-5 of max |logit|).  Passes of
-                                       up to 5 rows and of 9 or 10 keep
-                                       three terms. */
+                                       up to 5 rows keep three terms. */
 
 /* Description of the target's weights, read once by spec_weights_create.
  * The pointer arrays are host arrays of n_blocks device pointers.  The

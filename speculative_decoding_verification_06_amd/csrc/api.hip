@@ -89,9 +89,8 @@ int gemm_path(const spec_weights* w, int M) {
 // 72-row top-p pass and 14-21% of B = 1 passes of 65 to 97 rows), and the
 // stacked passes of 6 to 8 rows, whose eight rows of two terms fit one
 // fragment where five rows of three do not.  Stacked passes of up to 5 rows
-// keep three exact terms, which cost no extra matrix operation there, and so
-// do those of 9 and 10 rows (two tiles either way).  Every producer of the
-// pass splits alike.
+// keep three exact terms, which cost no extra matrix operation there.  Every
+// producer of the pass splits alike.
 bool two_term(const spec_weights* w, int M, int path) {
   return !(w->flags & SPEC_FLAG_EXACT_SPLIT) && path == PATH_MFMA &&
          (wide_rows(M) || (M >= 6 && M <= kStackRows2));

@@ -8,10 +8,9 @@
 // aicomputerinstitute.com, Why Generation Is Slow: A Roofline View).  Each
 // weight byte is read from HBM once; activations are split once, by the
 // kernel that produces them, into bf16 terms for the MFMA path: three exact
-// terms in the stacked passes of up to 5 and of 9 or 10 rows, two rounded
-// ones (2^-16 relative) in the stacked passes of 6 to 8 rows and the wide
-// passes unless the exact split is asked for, so the logits track a float64
-// reference.
+// terms in the stacked passes of up to 5 rows, two rounded ones (2^-16
+// relative) in the stacked passes of 6 to 8 rows and the wide passes unless
+// the exact split is asked for, so the logits track a float64 reference.
 //
 // Work decomposition: a work group owns NT MFMA column tiles (16 columns
 // each) over the whole K range.  Its waves are MG row groups x KG k-groups;
@@ -774,7 +773,7 @@ __device__ __forceinline__ void wide_lm_epilogue2(const EpiArgs& e, const f32x4 
 }
 
 // ---------------------------------------------------------------- wide MFMA GEMM
-// Many rows (plain packing, 11 to 224 rows): the split activations of a
+// Many rows (plain packing, 9 to 224 rows): the split activations of a
 // k-step, MT row tiles x TERMS terms, are staged once per work group in LDS and
 // shared by the group's 16 column tiles (256 columns), instead of being
 // read from L2 by every 16-column tile.  MG x CG waves: row groups of MTW

@@ -97,11 +97,13 @@ struct GemmPlan {
   size_t lds = 0;                // dynamic LDS bytes
 };
 
-// The MFMA path packs the split activations of up to 10 rows stacked (up to
-// two five-row tiles of three terms, or one eight-row tile of two terms for
-// 6 to 8 rows, one fragment per k-step each); more rows use the plain
-// packing, which needs no more fragments from 11 rows on.
-inline bool xs_stacked(int M) { return M <= 10; }
+// The MFMA path packs the split activations of up to 8 rows stacked (one
+// five-row tile of three terms up to 5 rows, one eight-row tile of two terms
+// for 6 to 8, or two five-row tiles of three with the exact split; one
+// fragment per k-step each); more rows use the plain packing on the wide
+// GEMM (measured: B = 1 passes of 9 and 10 rows 5% faster there on the mid
+// model and 7% on the large one than in two stacked tiles).
+inline bool xs_stacked(int M) { return M <= kStackRows2; }
 
 // Bytes of one split-activation buffer of M rows and ks k-steps (plus the
 // all-zero step): one 1 KiB fragment per row tile and k-step stacked (sized

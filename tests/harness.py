@@ -94,7 +94,7 @@ def greedy_drafts(ell, key, agree=0.75):
 # oracle if the logits it reads are close.
 LOGIT_TOL = 1e-5
 # The same for passes whose GEMMs take the two-term activation split (bf16
-# weights, the stacked passes of 6 to 8 rows and the wide GEMM's 11 to 224
+# weights, the stacked passes of 6 to 8 rows and the wide GEMM's 9 to 224
 # rows, unless SPEC_FLAG_EXACT_SPLIT): each activation
 # carries a rounding error of at most 2^-16 relative (rms 2^-16 / sqrt(3),
 # about 8.8e-6) into its GEMM, where the exact three-term split carries
@@ -105,7 +105,7 @@ LOGIT_TOL = 1e-5
 # not held for such passes (the two sides compute different logits); every
 # difference must still be a flagged decision, and is counted.
 LOGIT_TOL_TWO = 3e-5
-TWO_TERM_ROWS = ((6, 8), (11, 224))
+TWO_TERM_ROWS = ((6, 224),)
 
 
 def two_term_pass(M, wdtype="bf16", exact_split=False, fma=False):

@@ -5,8 +5,8 @@ spec_diag_access_check evaluates the kernels' address formulas at the
 extremes of their index ranges for the launch plans spec_verify would take
 and checks them against the buffers spec_workspace_size lays out and the
 registered weight layouts.  It covers every row count the GEMM paths serve
-(1 .. 448 rows: stacked MFMA up to 10, in eight-row tiles of two terms
-from 6 to 8 rows, wide MFMA 11 .. 224 with two activation terms, or three
+(1 .. 448 rows: stacked MFMA up to 8, in eight-row tiles of two terms
+from 6 to 8 rows, wide MFMA 9 .. 224 with two activation terms, or three
 when the exact split is asked for, chunked plain MFMA beyond; and the
 vector-FMA paths), the five workload shapes, and the
 shapes the GPU parity tests run.  A planted inconsistency (workspace
@@ -76,7 +76,7 @@ def test_parity_test_shapes():
 
 def test_exact_split_row_counts():
     """The row counts where the default takes two terms (6 .. 8 stacked, the
-    wide GEMM's 11 .. 224), with the exact three-term split kept instead,
+    wide GEMM's 9 .. 224), with the exact three-term split kept instead,
     and a short workspace caught either way."""
     for (d, ffn, nb, V) in [(8192, 28672, 1, 128256), (200, 300, 2, 1000), (160, 288, 1, 700)]:
         for M in range(1, 229):
