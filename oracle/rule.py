@@ -116,7 +116,8 @@ class TopP:
 class Decision:
     """One decision of the rule: kind ('accept', 'resample', 'bonus',
     'argmax'), position, margin, slack and band (see the module docstring).
-    `raw` is the ratio test's |r - p'/q'| as the spec rule states it."""
+    `raw` is the ratio test's |r - p'/q'|, whose near-zero draws are counted
+    as knife edges."""
 
     __slots__ = ("kind", "pos", "margin", "slack", "band", "raw")
 

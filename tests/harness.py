@@ -134,7 +134,7 @@ class TokenReport:
         self.unexplained = []     # rows whose first difference no flagged decision explains
         self.flagged = collections.Counter()    # flagged decisions by kind
         self.total = collections.Counter()      # decisions by kind
-        self.knife = 0            # ratio tests with |r - p'/q'| < MARGIN (the spec count)
+        self.knife = 0            # ratio tests with |r - p'/q'| < MARGIN (the counted knife edges)
         self.band_sizes = []      # band sizes of flagged token decisions
 
     @property
